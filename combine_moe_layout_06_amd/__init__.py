@@ -1,0 +1,155 @@
+"""MoE expert-parallel hot path on one AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in include/moe.h (library libmoe_layout.so,
+built by `python -m combine_moe_layout_06_amd.build`). The functions keep
+the C names and argument order and only marshal arguments: every step runs
+in the HIP kernels of the library. A tensor argument must be a contiguous
+device tensor (its data_ptr() is passed); an int is taken as a raw device
+pointer; None is NULL. `stream` defaults to torch's current stream.
+
+There is no CPU fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+MOE_OK = 0
+MOE_ERR_INVALID = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+MOE_SCORE_SOFTMAX = 0
+MOE_SCORE_SIGMOID = 1
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_FP8_E4M3 = 1
+
+MOE_MAX_EXPERTS = 512
+MOE_MAX_TOPK = 32
+MOE_MAX_GROUPS = 64
+MOE_FP8_BLOCK = 128
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layout.so")
+
+EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
+            "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch", "moe_combine")
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_status_name(status), message))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("HIP library %s is missing; run "
+                           "`python -m combine_moe_layout_06_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i32, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_route.argtypes = [i32, i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.moe_route.restype = i32
+    L.moe_layout_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_layout_workspace_bytes.restype = sz
+    L.moe_layout.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                             vp, sz, vp]
+    L.moe_layout.restype = i32
+    L.moe_dispatch.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, vp, vp]
+    L.moe_dispatch.restype = i32
+    L.moe_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.moe_combine.restype = i32
+    _lib = L
+    return L
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().moe_status_string(status).decode()
+    except Exception:  # the library itself failed to load
+        return "status %d" % status
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor, got one on %s" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_route(num_tokens, num_experts, top_k, logits, bias, score_fn, num_groups,
+              topk_groups, topk_idx, topk_weights, stream=None) -> None:
+    _check(lib().moe_route(num_tokens, num_experts, top_k, _ptr(logits), _ptr(bias),
+                           score_fn, num_groups, topk_groups, _ptr(topk_idx),
+                           _ptr(topk_weights), _stream(stream)))
+
+
+def moe_layout_workspace_bytes(num_tokens, num_experts, top_k) -> int:
+    return int(lib().moe_layout_workspace_bytes(num_tokens, num_experts, top_k))
+
+
+def moe_layout(num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
+               expert_counts, expert_offsets, rank_counts, rank_offsets,
+               rank_token_counts, dst_row, src_pair, overflow, workspace,
+               workspace_bytes, stream=None) -> None:
+    _check(lib().moe_layout(num_tokens, num_experts, top_k, num_ranks, capacity,
+                            _ptr(topk_idx), _ptr(expert_counts), _ptr(expert_offsets),
+                            _ptr(rank_counts), _ptr(rank_offsets), _ptr(rank_token_counts),
+                            _ptr(dst_row), _ptr(src_pair), _ptr(overflow), _ptr(workspace),
+                            workspace_bytes, _stream(stream)))
+
+
+def moe_dispatch(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out_dtype, out,
+                 out_scales, stream=None) -> None:
+    _check(lib().moe_dispatch(num_tokens, hidden, top_k, num_rows, _ptr(x_bf16),
+                              _ptr(dst_row), out_dtype, _ptr(out), _ptr(out_scales),
+                              _stream(stream)))
+
+
+def moe_combine(num_tokens, hidden, top_k, num_rows, expert_out_bf16, dst_row,
+                topk_weights, out_bf16, stream=None) -> None:
+    _check(lib().moe_combine(num_tokens, hidden, top_k, num_rows, _ptr(expert_out_bf16),
+                             _ptr(dst_row), _ptr(topk_weights), _ptr(out_bf16),
+                             _stream(stream)))
+
+
+from .buffers import LayerBuffers, run_layer  # noqa: E402,F401

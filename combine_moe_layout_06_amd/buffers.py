@@ -1,0 +1,103 @@
+"""Device buffers of one MoE layer pass and the calls that fill them.
+
+Plumbing only: torch allocates the caller-owned buffers that the C ABI
+writes, sized on the host from (T, H, E, k, R, capacity) so that no count
+has to be read back before dispatch (packed mode: T*k rows; capacity mode:
+E*capacity rows). Every computation is a call into the HIP library.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_FP8_BLOCK, moe_combine,
+               moe_dispatch, moe_layout, moe_layout_workspace_bytes, moe_route)
+
+
+@dataclasses.dataclass
+class LayerBuffers:
+    tokens: int
+    hidden: int
+    experts: int
+    top_k: int
+    ranks: int
+    capacity: int
+    fp8: bool
+    topk_idx: object = None
+    topk_weights: object = None
+    expert_counts: object = None
+    expert_offsets: object = None
+    rank_counts: object = None
+    rank_offsets: object = None
+    rank_token_counts: object = None
+    dst_row: object = None
+    src_pair: object = None
+    overflow: object = None
+    workspace: object = None
+    workspace_bytes: int = 0
+    dispatched: object = None     # [rows, H] bf16 (as int16) or uint8 codes
+    scales: object = None         # [rows, H/128] fp32 (FP8 only)
+    combined: object = None       # [T, H] bf16 (as int16)
+
+    @property
+    def num_rows(self) -> int:
+        if self.capacity > 0:
+            return self.experts * self.capacity
+        return self.tokens * self.top_k
+
+    @classmethod
+    def allocate(cls, tokens, hidden, experts, top_k, ranks, capacity=0, fp8=False,
+                 device="cuda", with_rank_tokens=True) -> "LayerBuffers":
+        import torch
+        i32 = dict(dtype=torch.int32, device=device)
+        b = cls(tokens, hidden, experts, top_k, ranks, capacity, fp8)
+        t, e, k, r = tokens, experts, top_k, ranks
+        b.topk_idx = torch.empty((t, k), **i32)
+        b.topk_weights = torch.empty((t, k), dtype=torch.float32, device=device)
+        b.expert_counts = torch.empty(e, **i32)
+        b.expert_offsets = torch.empty(e + 1, **i32)
+        b.rank_counts = torch.empty(r, **i32)
+        b.rank_offsets = torch.empty(r + 1, **i32)
+        b.rank_token_counts = torch.empty(r, **i32) if with_rank_tokens else None
+        b.dst_row = torch.empty((t, k), **i32)
+        b.src_pair = torch.empty(max(b.num_rows, 1), **i32)
+        b.overflow = torch.empty(1, **i32)
+        b.workspace_bytes = moe_layout_workspace_bytes(t, e, k)
+        b.workspace = torch.empty(max(b.workspace_bytes, 4), dtype=torch.uint8, device=device)
+        rows = max(b.num_rows, 1)
+        if fp8:
+            b.dispatched = torch.empty((rows, hidden), dtype=torch.uint8, device=device)
+            b.scales = torch.empty((rows, hidden // MOE_FP8_BLOCK), dtype=torch.float32,
+                                   device=device)
+        else:
+            b.dispatched = torch.empty((rows, hidden), dtype=torch.int16, device=device)
+        b.combined = torch.empty((max(t, 1), hidden), dtype=torch.int16, device=device)
+        return b
+
+    def route(self, logits, bias, score_fn, num_groups=1, topk_groups=1, stream=None):
+        moe_route(self.tokens, self.experts, self.top_k, logits, bias, score_fn, num_groups,
+                  topk_groups, self.topk_idx, self.topk_weights, stream)
+
+    def layout(self, stream=None):
+        moe_layout(self.tokens, self.experts, self.top_k, self.ranks, self.capacity,
+                   self.topk_idx, self.expert_counts, self.expert_offsets, self.rank_counts,
+                   self.rank_offsets, self.rank_token_counts, self.dst_row, self.src_pair,
+                   self.overflow, self.workspace, self.workspace_bytes, stream)
+
+    def dispatch(self, x, stream=None):
+        moe_dispatch(self.tokens, self.hidden, self.top_k, self.num_rows, x, self.dst_row,
+                     MOE_DTYPE_FP8_E4M3 if self.fp8 else MOE_DTYPE_BF16, self.dispatched,
+                     self.scales if self.fp8 else None, stream)
+
+    def combine(self, expert_out, stream=None):
+        moe_combine(self.tokens, self.hidden, self.top_k, self.num_rows, expert_out,
+                    self.dst_row, self.topk_weights, self.combined, stream)
+
+
+def run_layer(buf: LayerBuffers, logits, bias, x, score_fn, num_groups=1, topk_groups=1,
+              stream: Optional[object] = None) -> None:
+    """Route, lay out and dispatch one layer pass (combine follows the experts)."""
+    buf.route(logits, bias, score_fn, num_groups, topk_groups, stream)
+    buf.layout(stream)
+    buf.dispatch(x, stream)

@@ -1,0 +1,220 @@
+// Dispatch on gfx950: copy each token's hidden state to the rows of its k
+// experts, as bf16 or as FP8 e4m3 with one fp32 scale per 128 columns.
+//
+// Sources: glossary "Expert Parallelism" (polydesk.ai), "Le pattern de
+// communication all-to-all", Phase 1 (each token goes to the GPUs of its
+// experts); DeepEP article (ai-master.dev), "Kernels low-latency dispatch et
+// combine" (dispatch kernels that understand the MoE data and fuse steps),
+// "Support FP8 et MXFP8" (FP8 halves the BF16 volume) and "Configuration
+// type" (FP8 quantisation happens inside the dispatch call); hyper.ai story
+// on Hybrid-EP (native FP8/BF16 dispatch).
+//
+// One 64-lane wave per (token, column part). The token row is read once,
+// held in registers, and written to each destination row with 16-byte
+// (bf16) or 8-byte (FP8) nontemporal stores: every store instruction of a
+// wave covers whole 128-byte lines. FP8 quantises once per token; the
+// block amax is a 16-lane DPP max inside each 64-lane wave.
+
+#include "kernels.h"
+#include "wave.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kUnroll = 4;        // 16-byte chunks per lane held at once (bf16)
+constexpr int kScaleSlots = 4;    // FP8: scales of up to 256 blocks per part
+
+__global__ __launch_bounds__(256) void dispatch_bf16_kernel(
+    int T, int k, int nch, int parts, int cpp, int num_rows,
+    const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
+    u32x4* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= T * parts) return;
+  const int t = gw / parts;
+  const int c0 = (gw - t * parts) * cpp;
+  const int cnt = min(cpp, nch - c0);
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const u32x4* src = x + (size_t)t * nch + c0;
+
+  for (int base = 0; base < cnt; base += MOE_WAVE * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = base + u * MOE_WAVE + lane;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (c < cnt) v[u] = __builtin_nontemporal_load(src + c);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int d = read_lane(my_dst, j);
+      if (d < 0 || d >= num_rows) continue;
+      u32x4* dst = out + (size_t)d * nch + c0;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = base + u * MOE_WAVE + lane;
+        if (c < cnt) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+  }
+}
+
+// Max over the 16 lanes of each DPP row (lanes 16r .. 16r+15).
+__device__ __forceinline__ uint32_t row16_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));  // row_mirror
+  return m;
+}
+
+// fp32 -> OCP e4m3fn code, round to nearest even, saturating at +-448.
+// The sign of zero is kept. `p` is finite or +-inf here.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float p) {
+  const uint32_t b = __float_as_uint(p);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  uint32_t mag;
+  if (a > 0x43E00000u) {                 // above 448: saturate
+    mag = 0x7Eu;
+  } else if (a >= 0x3C800000u) {         // normal e4m3 range, >= 2^-6
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);   // RNE to 3 mantissa bits
+    mag = (r >> 20) - (120u << 3);                        // rebias exponent 127 -> 7
+  } else {                               // subnormal range: multiples of 2^-9
+    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return sign | mag;
+}
+
+// Quantise one bf16 element (held in the low 16 bits of `h`).
+__device__ __forceinline__ uint32_t quant_one(uint32_t h, float inv) {
+  const float xv = __uint_as_float(h << 16);
+  if ((h & 0x7FFFu) == 0u) return (h >> 8) & 0x80u;       // +-0 keeps its sign
+  return e4m3_from_f32(xv * inv);
+}
+
+__device__ __forceinline__ uint32_t quant_pair(uint32_t w, float inv) {
+  return quant_one(w & 0xFFFFu, inv) | (quant_one(w >> 16, inv) << 8);
+}
+
+__global__ __launch_bounds__(256) void dispatch_fp8_kernel(
+    int T, int k, int H, int parts, int bpp, int num_rows,
+    const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
+    uint8_t* __restrict__ out, float* __restrict__ out_scales) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= T * parts) return;
+  const int t = gw / parts;
+  const int nb = H / MOE_FP8_BLOCK;
+  const int nch = H / 8;
+  const int b0 = (gw - t * parts) * bpp;
+  const int nbp = min(bpp, nb - b0);
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const int group = lane >> 4;       // which of the 4 blocks of a 512-column step
+  const int sub = lane & 15;         // 16-byte chunk inside the block
+  const u32x4* src = x + (size_t)t * nch;
+
+  float sreg[kScaleSlots];
+#pragma unroll
+  for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0.0f;
+
+  for (int it = 0; it * 4 < nbp; ++it) {
+    const int bl = it * 4 + group;
+    const bool act = bl < nbp;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (act) v = __builtin_nontemporal_load(src + (b0 + bl) * 16 + sub);
+
+    // block amax on the bf16 magnitudes (their bit patterns order like values)
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = v[q] & 0x7FFF7FFFu;
+      m = max(m, max(w & 0xFFFFu, w >> 16));
+    }
+    m = row16_max(m);
+    const float amax = __uint_as_float(m << 16);
+    const float scale = amax / 448.0f;
+    const float inv = 448.0f / amax;
+
+    const uint32_t lo = quant_pair(v[0], inv) | (quant_pair(v[1], inv) << 16);
+    const uint32_t hi = quant_pair(v[2], inv) | (quant_pair(v[3], inv) << 16);
+
+    // lane (b & 63), slot (b >> 6) keeps the scale of part-local block b
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int b = it * 4 + g;
+      const float sg = read_lane(scale, g * 16);
+      if (b < nbp && lane == (b & 63)) {
+#pragma unroll
+        for (int s = 0; s < kScaleSlots; ++s)
+          if ((b >> 6) == s) sreg[s] = sg;
+      }
+    }
+
+    if (act) {
+      const u32x2 q = {lo, hi};
+      for (int j = 0; j < k; ++j) {
+        const int d = read_lane(my_dst, j);
+        if (d < 0 || d >= num_rows) continue;
+        u32x2* dst = reinterpret_cast<u32x2*>(out + (size_t)d * H + (size_t)(b0 + bl) * MOE_FP8_BLOCK) + sub;
+        __builtin_nontemporal_store(q, dst);
+      }
+    }
+  }
+
+  for (int j = 0; j < k; ++j) {
+    const int d = read_lane(my_dst, j);
+    if (d < 0 || d >= num_rows) continue;
+    float* srow = out_scales + (size_t)d * nb + b0;
+#pragma unroll
+    for (int s = 0; s < kScaleSlots; ++s) {
+      const int b = s * 64 + lane;
+      if (b < nbp) srow[b] = sreg[s];
+    }
+  }
+}
+
+// Split a row of `units` into parts so that the launch has about
+// kTargetWaves waves, each part a multiple of `align` units (but at least
+// `min_units` and at most `max_units` units).
+void split_row(int T, int units, int align, int max_units, int* parts, int* per_part) {
+  int p = T > 0 ? (kTargetWaves + T - 1) / T : 1;
+  p = max(1, min(p, units / align));
+  int per = (units + p - 1) / p;
+  per = (per + align - 1) / align * align;
+  if (per > max_units) per = max_units;
+  *per_part = per;
+  *parts = (units + per - 1) / per;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_bf16(int T, int H, int k, int num_rows, const void* x,
+                                const int32_t* dst_row, void* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int nch = H / 8;
+  int parts, cpp;
+  split_row(T, nch, MOE_WAVE, 1 << 30, &parts, &cpp);
+  const int waves = T * parts;
+  hipLaunchKernelGGL(dispatch_bf16_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(256), 0, stream, T, k, nch, parts, cpp, num_rows,
+                     static_cast<const u32x4*>(x), dst_row, static_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fp8(int T, int H, int k, int num_rows, const void* x,
+                               const int32_t* dst_row, void* out, float* out_scales,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int nb = H / MOE_FP8_BLOCK;
+  int parts, bpp;
+  split_row(T, nb, 4, 64 * kScaleSlots, &parts, &bpp);
+  const int waves = T * parts;
+  hipLaunchKernelGGL(dispatch_fp8_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(256), 0, stream, T, k, H, parts, bpp, num_rows,
+                     static_cast<const u32x4*>(x), dst_row, static_cast<uint8_t*>(out),
+                     out_scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

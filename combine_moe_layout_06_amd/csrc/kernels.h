@@ -1,0 +1,43 @@
+// Internal launch functions of the HIP kernels. Each assumes its arguments
+// were validated by the C-ABI layer (moe_api.hip) and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+hipError_t launch_route(int T, int E, int k, const float* logits, const float* bias,
+                        int sigmoid, int G, int kg, int32_t* idx_out, float* w_out,
+                        hipStream_t stream);
+
+// Layout: pairs are cut into tiles of whole tokens; one block per tile.
+int layout_tile_tokens(int k);
+int layout_num_tiles(int T, int k);
+size_t layout_workspace_bytes(int T, int E, int k);
+
+hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* rank_counts, int32_t* rank_offsets,
+                         int32_t* rank_token_counts, int32_t* dst_row,
+                         int32_t* src_pair, int32_t* overflow, void* workspace,
+                         hipStream_t stream);
+
+hipError_t launch_dispatch_bf16(int T, int H, int k, int num_rows, const void* x,
+                                const int32_t* dst_row, void* out, hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(int T, int H, int k, int num_rows, const void* x,
+                               const int32_t* dst_row, void* out, float* out_scales,
+                               hipStream_t stream);
+
+hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
+                          const int32_t* dst_row, const float* w, void* out,
+                          hipStream_t stream);
+
+// Number of waves a row-parallel kernel aims for: 256 CUs x 32 wave slots.
+constexpr int kTargetWaves = 8192;
+
+}  // namespace moe

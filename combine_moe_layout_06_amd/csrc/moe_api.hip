@@ -1,0 +1,198 @@
+// C ABI of the MoE hot path (declared in include/moe.h).
+//
+// Every entry point validates its scalar and pointer arguments on the host
+// before it enqueues anything, so that a bad call changes no memory and can
+// be tested without a GPU. Launches go to the caller's stream; the library
+// never allocates, frees or synchronises.
+
+#include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return MOE_OK;
+}
+
+int from_hip(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Limits shared by routing and layout.
+int check_topk(const char* fn, int T, int E, int k) {
+  if (T < 0) return fail(MOE_ERR_INVALID, "%s: num_tokens=%d < 0", fn, T);
+  if (E < 1) return fail(MOE_ERR_INVALID, "%s: num_experts=%d < 1", fn, E);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: num_experts=%d > %d", fn, E, MOE_MAX_EXPERTS);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID, "%s: top_k=%d not in [1, %d]", fn, k, E);
+  if (k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: top_k=%d > %d", fn, k, MOE_MAX_TOPK);
+  if ((long long)T * k > INT_MAX) return fail(MOE_ERR_INVALID, "%s: num_tokens*top_k overflows", fn);
+  return MOE_OK;
+}
+
+int check_rows(const char* fn, int T, int H, int k, int num_rows) {
+  if (T < 0) return fail(MOE_ERR_INVALID, "%s: num_tokens=%d < 0", fn, T);
+  if (k < 1 || k > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID, "%s: top_k=%d not in [1, %d]", fn, k, MOE_MAX_TOPK);
+  if (H < 8 || H % 8 != 0)
+    return fail(MOE_ERR_INVALID, "%s: hidden=%d must be a positive multiple of 8", fn, H);
+  if (num_rows < 0) return fail(MOE_ERR_INVALID, "%s: num_rows=%d < 0", fn, num_rows);
+  if ((long long)T * k > INT_MAX) return fail(MOE_ERR_INVALID, "%s: num_tokens*top_k overflows", fn);
+  // waves are indexed with int: T * parts <= T * H / 8
+  if ((long long)T * (H / 8) > INT_MAX) return fail(MOE_ERR_INVALID, "%s: num_tokens*hidden too large", fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+int moe_route(int num_tokens, int num_experts, int top_k, const float* logits,
+              const float* bias, int score_fn, int num_groups, int topk_groups,
+              int32_t* topk_idx, float* topk_weights, void* stream) {
+  const char* fn = "moe_route";
+  int st = check_topk(fn, num_tokens, num_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID, "%s: score_fn=%d", fn, score_fn);
+  if (num_groups < 1 || num_groups > MOE_MAX_GROUPS || num_experts % num_groups != 0)
+    return fail(MOE_ERR_INVALID, "%s: num_groups=%d must divide num_experts=%d and be <= %d", fn,
+                num_groups, num_experts, MOE_MAX_GROUPS);
+  if (score_fn == MOE_SCORE_SOFTMAX && num_groups != 1)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: softmax routing takes no groups", fn);
+  if (topk_groups < 1 || topk_groups > num_groups)
+    return fail(MOE_ERR_INVALID, "%s: topk_groups=%d not in [1, %d]", fn, topk_groups, num_groups);
+  if ((long long)topk_groups * (num_experts / num_groups) < top_k)
+    return fail(MOE_ERR_INVALID, "%s: the kept groups hold fewer than top_k experts", fn);
+  if (num_tokens > 0 && (!logits || !topk_idx || !topk_weights))
+    return fail(MOE_ERR_INVALID, "%s: NULL logits/topk_idx/topk_weights", fn);
+  if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+  return from_hip(moe::launch_route(num_tokens, num_experts, top_k, logits, bias,
+                                    score_fn == MOE_SCORE_SIGMOID, num_groups, topk_groups,
+                                    topk_idx, topk_weights, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+size_t moe_layout_workspace_bytes(int num_tokens, int num_experts, int top_k) {
+  if (num_tokens < 0 || num_experts < 1 || top_k < 1 || top_k > MOE_MAX_TOPK) return 0;
+  return moe::layout_workspace_bytes(num_tokens, num_experts, top_k);
+}
+
+int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int capacity,
+               const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
+               int32_t* rank_counts, int32_t* rank_offsets, int32_t* rank_token_counts,
+               int32_t* dst_row, int32_t* src_pair, int32_t* overflow, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_layout";
+  int st = check_topk(fn, num_tokens, num_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (num_ranks < 1 || num_ranks > num_experts || num_experts % num_ranks != 0)
+    return fail(MOE_ERR_INVALID, "%s: num_ranks=%d must divide num_experts=%d", fn, num_ranks,
+                num_experts);
+  if (capacity < 0) return fail(MOE_ERR_INVALID, "%s: capacity=%d < 0", fn, capacity);
+  if ((long long)num_experts * capacity > INT_MAX)
+    return fail(MOE_ERR_INVALID, "%s: num_experts*capacity overflows", fn);
+  if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets || !overflow)
+    return fail(MOE_ERR_INVALID, "%s: NULL count/offset/overflow output", fn);
+  const long long rows = capacity > 0 ? (long long)num_experts * capacity
+                                      : (long long)num_tokens * top_k;
+  if (num_tokens > 0 && (!topk_idx || !dst_row))
+    return fail(MOE_ERR_INVALID, "%s: NULL topk_idx/dst_row", fn);
+  if (rows > 0 && !src_pair) return fail(MOE_ERR_INVALID, "%s: NULL src_pair", fn);
+  const void* ptrs[] = {topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        rank_token_counts, dst_row, src_pair, overflow};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return fail(MOE_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+  const size_t need = moe::layout_workspace_bytes(num_tokens, num_experts, top_k);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace_bytes);
+  if (!aligned(workspace, 4)) return fail(MOE_ERR_INVALID, "%s: workspace not aligned", fn);
+  return from_hip(moe::launch_layout(num_tokens, num_experts, top_k, num_ranks, capacity,
+                                     topk_idx, expert_counts, expert_offsets, rank_counts,
+                                     rank_offsets, rank_token_counts, dst_row, src_pair,
+                                     overflow, workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows, const void* x_bf16,
+                 const int32_t* dst_row, int out_dtype, void* out, float* out_scales,
+                 void* stream) {
+  const char* fn = "moe_dispatch";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
+  if (st != MOE_OK) return st;
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID, "%s: out_dtype=%d", fn, out_dtype);
+  const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3;
+  if (fp8 && hidden % MOE_FP8_BLOCK != 0)
+    return fail(MOE_ERR_INVALID, "%s: FP8 needs hidden %% %d == 0 (hidden=%d)", fn,
+                MOE_FP8_BLOCK, hidden);
+  if (num_tokens > 0 && (!x_bf16 || !dst_row))
+    return fail(MOE_ERR_INVALID, "%s: NULL x/dst_row", fn);
+  if (num_rows > 0 && !out) return fail(MOE_ERR_INVALID, "%s: NULL out", fn);
+  if (fp8 && num_rows > 0 && !out_scales) return fail(MOE_ERR_INVALID, "%s: NULL out_scales", fn);
+  if (!fp8 && out_scales) return fail(MOE_ERR_INVALID, "%s: out_scales is for FP8 only", fn);
+  if (!aligned(x_bf16, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID, "%s: x and out must be 16-byte aligned", fn);
+  if (!aligned(dst_row, 4) || !aligned(out_scales, 4))
+    return fail(MOE_ERR_INVALID, "%s: dst_row/out_scales must be 4-byte aligned", fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err =
+      fp8 ? moe::launch_dispatch_fp8(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out,
+                                     out_scales, s)
+          : moe::launch_dispatch_bf16(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out, s);
+  return from_hip(err, fn);
+}
+
+int moe_combine(int num_tokens, int hidden, int top_k, int num_rows, const void* expert_out_bf16,
+                const int32_t* dst_row, const float* topk_weights, void* out_bf16,
+                void* stream) {
+  const char* fn = "moe_combine";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
+  if (st != MOE_OK) return st;
+  if (num_tokens > 0 && (!dst_row || !topk_weights || !out_bf16))
+    return fail(MOE_ERR_INVALID, "%s: NULL dst_row/topk_weights/out", fn);
+  if (num_rows > 0 && !expert_out_bf16) return fail(MOE_ERR_INVALID, "%s: NULL expert_out", fn);
+  if (!aligned(expert_out_bf16, 16) || !aligned(out_bf16, 16))
+    return fail(MOE_ERR_INVALID, "%s: expert_out and out must be 16-byte aligned", fn);
+  if (!aligned(dst_row, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_INVALID, "%s: dst_row/topk_weights must be 4-byte aligned", fn);
+  return from_hip(moe::launch_combine(num_tokens, hidden, top_k, num_rows, expert_out_bf16,
+                                      dst_row, topk_weights, out_bf16,
+                                      static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"

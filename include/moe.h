@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MoE expert-parallel hot path on one AMD Instinct
+ * MI355X (gfx950): routing, layout, dispatch and combine.
+ *
+ * Sources. The operations are the ones described by four web pages on MoE
+ * expert parallelism:
+ *   - glossary page "Expert Parallelism (Parallélisme d'experts)"
+ *     (polydesk.ai): section "Le principe de base" (each GPU owns whole
+ *     experts; 8 experts over 4 GPUs gives 2 per GPU) and section "Le pattern
+ *     de communication all-to-all" (Phase 1 dispatch, Phase 2 combine
+ *     weighted by the router scores), sections "Megatron-LM (NVIDIA)" and
+ *     "Défis et optimisations" (capacity factor, token dropping);
+ *   - article "DeepEP de DeepSeek : la lib open source qui optimise la
+ *     communication GPU pour les modèles MoE à l'échelle" (ai-master.dev):
+ *     sections "Kernels low-latency dispatch et combine", "Support FP8 et
+ *     MXFP8", "Group-limited gating algorithm", "Configuration type";
+ *   - the hyper.ai story on NVIDIA Hybrid-EP: top-k routing, the dispatch and
+ *     combine operators, native FP8/BF16, and buffers preallocated at a
+ *     maximum size so that no size synchronisation is needed.
+ * The destination GPUs ("ranks") of those pages are modelled here as
+ * consecutive regions of one buffer in one GPU's HBM: rank r owns experts
+ * [r*E/R, (r+1)*E/R) and its region is the rows of those experts.
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or synchronises, and keeps no state.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     on it and the call returns without waiting.
+ *   - Arguments are validated on the host BEFORE anything is enqueued: on a
+ *     bad argument the call returns MOE_ERR_INVALID (or MOE_ERR_UNSUPPORTED
+ *     / MOE_ERR_WORKSPACE) and touches nothing. A failed launch returns
+ *     MOE_ERR_HIP. moe_last_error() describes the last failure of the
+ *     calling thread.
+ *   - Device-side contents are not validated. Kernels ignore an expert id
+ *     outside [0, E) (treated like the mask value -1) and a row index
+ *     outside [0, num_rows) (the pair is skipped), so that bad routing data
+ *     can produce wrong results but never an out-of-bounds access.
+ *     NaN and Inf inputs give unspecified results.
+ *   - Outputs must not overlap inputs. Calls are re-entrant.
+ *   - bf16 data is passed as raw 16-bit patterns; rows are contiguous with
+ *     `hidden` elements each and must start 16-byte aligned.
+ */
+#ifndef MOE_LAYOUT_MOE_H
+#define MOE_LAYOUT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* bad scalar or pointer argument          */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid, but outside the built kernels    */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or too small          */
+  MOE_ERR_HIP = 4           /* a HIP call or kernel launch failed      */
+} moe_status;
+
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3 = 1 };
+
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_GROUPS 64
+#define MOE_FP8_BLOCK 128
+
+/* Name of a status code ("MOE_OK", ...). Never NULL. */
+const char* moe_status_string(int status);
+
+/* Text of the last failure seen by the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * moe_route -- pick k of E experts per token and their weights.
+ *
+ * Top-k routing: each token activates only k experts (hyper.ai story on
+ * Hybrid-EP). With num_groups > 1 the choice is group-limited (DeepEP
+ * article, section "Group-limited gating algorithm"): the E experts form
+ * num_groups contiguous groups, each group is scored by the sum of its two
+ * largest selection keys, the topk_groups best groups are kept, and the k
+ * experts are chosen among the kept groups only.
+ *
+ *   score_fn  MOE_SCORE_SOFTMAX: s_e = l_e; weights are the softmax of the
+ *             selected logits, w_j = exp(l_j) / sum_i exp(l_i).
+ *             MOE_SCORE_SIGMOID: s_e = 1/(1+exp(-l_e)) (evaluated in fp64,
+ *             rounded to fp32); weights w_j = s_j / sum_i s_i.
+ *   key_e   = s_e + bias_e (fp32 add; bias may be NULL). The bias moves the
+ *             selection only, never the weights.
+ *   Order   : slot j holds the expert with the j-th largest key; equal keys
+ *             go to the lower expert index. Weight sums run in fp64 and each
+ *             weight is rounded once to fp32.
+ *
+ *   logits        [num_tokens, num_experts] fp32, row-major
+ *   bias          [num_experts] fp32 or NULL
+ *   topk_idx      [num_tokens, top_k] int32 output
+ *   topk_weights  [num_tokens, top_k] fp32 output
+ *
+ * Requires 0 <= num_tokens, 1 <= top_k <= min(num_experts, MOE_MAX_TOPK),
+ * num_experts <= MOE_MAX_EXPERTS; softmax needs num_groups == 1; with
+ * groups: num_experts % num_groups == 0, num_groups <= MOE_MAX_GROUPS,
+ * 1 <= topk_groups <= num_groups and top_k <= topk_groups * (E/num_groups).
+ */
+int moe_route(int num_tokens, int num_experts, int top_k,
+              const float* logits, const float* bias,
+              int score_fn, int num_groups, int topk_groups,
+              int32_t* topk_idx, float* topk_weights, void* stream);
+
+/* Bytes of device workspace moe_layout needs for these sizes. */
+size_t moe_layout_workspace_bytes(int num_tokens, int num_experts, int top_k);
+
+/*
+ * moe_layout -- counts, prefix-sum offsets and the stable destination row of
+ * every (token, slot) pair (glossary "Expert Parallelism", "Le principe de
+ * base" for the placement and Phase 1 for the dispatch it prepares).
+ *
+ * Packed mode (capacity == 0): the dispatch buffer has T*k rows, a size the
+ * caller knows without reading anything back (hyper.ai story on Hybrid-EP,
+ * preallocated buffers).
+ *   expert_counts[e]   pairs routed to e (mask value -1 is skipped)
+ *   expert_offsets[e]  sum of counts of experts < e; [E] = live pairs
+ *   dst_row[t,j]       expert_offsets[e] + number of earlier pairs of e in
+ *                      row-major (t, j) order (stable); -1 if masked
+ * Capacity mode (capacity > 0; glossary "Megatron-LM (NVIDIA)", capacity
+ * factor and token dropping): the buffer has E*capacity rows and the pair
+ * with stable position p in expert e goes to row e*capacity + p when
+ * p < capacity, else it is dropped (dst_row = -1).
+ *   expert_counts[e]   raw demand (dropped pairs included)
+ *   expert_offsets[e]  e*capacity
+ *   overflow[0]        number of dropped pairs
+ * Both modes:
+ *   rank_counts[r]       rows written into rank r's region
+ *   rank_offsets[r]      first row of rank r's region; [R] = end
+ *   rank_token_counts[r] distinct tokens with >= 1 unmasked expert on rank r
+ *                        (may be NULL)
+ *   src_pair[row]        t*k + j of the pair stored in `row`, -1 if none
+ *
+ *   topk_idx   [num_tokens, top_k] int32, values in [0, E) or -1
+ *   sizes: expert_counts [E], expert_offsets [E+1], rank_counts [R],
+ *          rank_offsets [R+1], rank_token_counts [R], dst_row [T, k],
+ *          src_pair [T*k] (packed) or [E*capacity], overflow [1]
+ *   workspace  device scratch of at least moe_layout_workspace_bytes()
+ *
+ * Placement uses no atomics on global memory: results are deterministic.
+ * Requires num_experts % num_ranks == 0 and the limits of moe_route.
+ */
+int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
+               int capacity, const int32_t* topk_idx,
+               int32_t* expert_counts, int32_t* expert_offsets,
+               int32_t* rank_counts, int32_t* rank_offsets,
+               int32_t* rank_token_counts, int32_t* dst_row,
+               int32_t* src_pair, int32_t* overflow,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch -- copy each token's hidden state to the rows of its
+ * experts (glossary "Expert Parallelism", Phase 1; DeepEP article,
+ * "Kernels low-latency dispatch et combine").
+ *
+ * MOE_DTYPE_BF16:     out[dst_row[t,j], :] = x[t, :]   (bit copy)
+ * MOE_DTYPE_FP8_E4M3: x is quantised once per token and copied to every
+ *   row of the token (DeepEP article, "Support FP8 et MXFP8": FP8 halves
+ *   the BF16 bytes; "Configuration type": quantisation inside the call).
+ *   For each 128-column block b of token t:
+ *     a = max |x|, scale = fp32(a/448), inv = fp32(448/a),
+ *     q = e4m3fn(fp32(x*inv)) rounded to nearest even, saturating at
+ *     +-448; an input of +-0 gives the code of +-0.
+ *   out holds the 1-byte OCP e4m3fn codes [num_rows, hidden];
+ *   out_scales[row, b] = scale, fp32 [num_rows, hidden/128].
+ *
+ *   x          [num_tokens, hidden] bf16
+ *   dst_row    [num_tokens, top_k] int32 from moe_layout (-1 = no row)
+ *   num_rows   rows of `out` (T*k packed, E*capacity padded)
+ * Rows that receive no pair are left untouched.
+ * Requires hidden % 8 == 0 (16-byte rows); FP8 also hidden % 128 == 0.
+ */
+int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows,
+                 const void* x_bf16, const int32_t* dst_row, int out_dtype,
+                 void* out, float* out_scales, void* stream);
+
+/*
+ * moe_combine -- bring each token's k expert outputs back and sum them
+ * weighted by the router scores (glossary "Expert Parallelism", Phase 2).
+ *
+ *   out[t, :] = bf16( sum_j w[t,j] * y[dst_row[t,j], :] )
+ *
+ * The sum runs over the pairs with a row (dropped pairs add nothing, the
+ * weights are not renormalised), in slot order j = 0..k-1, as a chain of
+ * fp32 fused multiply-adds, rounded once to bf16 (nearest even).
+ *
+ *   expert_out  [num_rows, hidden] bf16
+ *   dst_row     [num_tokens, top_k] int32
+ *   topk_weights [num_tokens, top_k] fp32
+ *   out         [num_tokens, hidden] bf16
+ * Requires hidden % 8 == 0.
+ */
+int moe_combine(int num_tokens, int hidden, int top_k, int num_rows,
+                const void* expert_out_bf16, const int32_t* dst_row,
+                const float* topk_weights, void* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYOUT_MOE_H */

@@ -1,0 +1,177 @@
+"""The C-ABI library loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before any HIP call (so these run
+without a GPU: every call here returns before a kernel could be queued)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_moe_layout_06_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+# Fake, well-aligned device addresses. Every call below must be rejected by
+# host-side validation; should one slip through, it would queue a kernel on
+# these addresses, so the calls only run where no GPU is visible.
+A16 = 0x10000
+A16b = 0x20000
+
+
+def _no_gpu():
+    try:
+        import torch
+        if torch.cuda.device_count() > 0:   # counts devices without initialising HIP
+            pytest.skip("fake device pointers are only passed where no GPU is visible")
+    except ImportError:
+        pass
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(M.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert M.moe_status_string(0) == "MOE_OK"
+    assert M.moe_status_string(4) == "MOE_ERR_HIP"
+    assert M.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def _route(**kw):
+    _no_gpu()
+    a = dict(T=4, E=8, k=2, logits=A16, bias=None, fn=0, G=1, kg=1, idx=A16, w=A16b)
+    a.update(kw)
+    return M.lib().moe_route(a["T"], a["E"], a["k"], a["logits"], a["bias"], a["fn"],
+                             a["G"], a["kg"], a["idx"], a["w"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), M.MOE_ERR_INVALID),
+    (dict(E=0), M.MOE_ERR_INVALID),
+    (dict(E=1024, k=2), M.MOE_ERR_UNSUPPORTED),
+    (dict(k=0), M.MOE_ERR_INVALID),
+    (dict(k=9), M.MOE_ERR_INVALID),
+    (dict(E=64, k=33), M.MOE_ERR_UNSUPPORTED),
+    (dict(fn=2), M.MOE_ERR_INVALID),
+    (dict(fn=0, G=2, kg=1), M.MOE_ERR_UNSUPPORTED),
+    (dict(fn=1, E=256, k=8, G=3, kg=1), M.MOE_ERR_INVALID),
+    (dict(fn=1, E=256, k=8, G=8, kg=0), M.MOE_ERR_INVALID),
+    (dict(fn=1, E=256, k=8, G=8, kg=9), M.MOE_ERR_INVALID),
+    (dict(fn=1, E=256, k=40, G=8, kg=1), M.MOE_ERR_UNSUPPORTED),
+    (dict(fn=1, E=16, k=5, G=4, kg=1), M.MOE_ERR_INVALID),
+    (dict(logits=None), M.MOE_ERR_INVALID),
+    (dict(idx=None), M.MOE_ERR_INVALID),
+    (dict(logits=A16 + 2), M.MOE_ERR_INVALID),
+    (dict(E=128, G=1, fn=1, k=2, logits=A16, bias=A16 + 1), M.MOE_ERR_INVALID),
+])
+def test_route_rejects(kw, status):
+    assert _route(**kw) == status
+    assert M.moe_last_error().startswith("moe_route")
+
+
+def _layout(**kw):
+    _no_gpu()
+    a = dict(T=4, E=8, k=2, R=4, cap=0, idx=A16, ws=A16, wsb=1 << 20, src=A16,
+             ec=A16, eo=A16, rc=A16, ro=A16, rtc=None, dst=A16, ov=A16)
+    a.update(kw)
+    return M.lib().moe_layout(a["T"], a["E"], a["k"], a["R"], a["cap"], a["idx"], a["ec"],
+                              a["eo"], a["rc"], a["ro"], a["rtc"], a["dst"], a["src"],
+                              a["ov"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=3), M.MOE_ERR_INVALID),
+    (dict(R=0), M.MOE_ERR_INVALID),
+    (dict(R=16), M.MOE_ERR_INVALID),
+    (dict(cap=-1), M.MOE_ERR_INVALID),
+    (dict(E=512, cap=1 << 23), M.MOE_ERR_INVALID),
+    (dict(ec=None), M.MOE_ERR_INVALID),
+    (dict(ov=None), M.MOE_ERR_INVALID),
+    (dict(idx=None), M.MOE_ERR_INVALID),
+    (dict(src=None), M.MOE_ERR_INVALID),
+    (dict(dst=A16 + 2), M.MOE_ERR_INVALID),
+    (dict(wsb=0), M.MOE_ERR_WORKSPACE),
+    (dict(ws=None), M.MOE_ERR_WORKSPACE),
+    (dict(T=1 << 28, k=16, E=16), M.MOE_ERR_INVALID),
+])
+def test_layout_rejects(kw, status):
+    assert _layout(**kw) == status
+    assert M.moe_last_error().startswith("moe_layout")
+
+
+def _dispatch(**kw):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, rows=8, x=A16, dst=A16, dt=0, out=A16b, sc=None)
+    a.update(kw)
+    return M.lib().moe_dispatch(a["T"], a["H"], a["k"], a["rows"], a["x"], a["dst"], a["dt"],
+                                a["out"], a["sc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=100), M.MOE_ERR_INVALID),
+    (dict(H=0), M.MOE_ERR_INVALID),
+    (dict(H=264, dt=1, sc=A16), M.MOE_ERR_INVALID),        # FP8 needs H % 128
+    (dict(dt=1, sc=None), M.MOE_ERR_INVALID),
+    (dict(dt=0, sc=A16), M.MOE_ERR_INVALID),
+    (dict(dt=7), M.MOE_ERR_INVALID),
+    (dict(x=A16 + 8), M.MOE_ERR_INVALID),
+    (dict(out=A16b + 4), M.MOE_ERR_INVALID),
+    (dict(rows=-1), M.MOE_ERR_INVALID),
+    (dict(k=0), M.MOE_ERR_INVALID),
+    (dict(k=33), M.MOE_ERR_INVALID),
+    (dict(x=None), M.MOE_ERR_INVALID),
+    (dict(T=1 << 20, H=1 << 16), M.MOE_ERR_INVALID),
+])
+def test_dispatch_rejects(kw, status):
+    assert _dispatch(**kw) == status
+    assert M.moe_last_error().startswith("moe_dispatch")
+
+
+def _combine(**kw):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, rows=8, y=A16, dst=A16, w=A16, out=A16b)
+    a.update(kw)
+    return M.lib().moe_combine(a["T"], a["H"], a["k"], a["rows"], a["y"], a["dst"], a["w"],
+                               a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=12), M.MOE_ERR_INVALID),
+    (dict(y=None), M.MOE_ERR_INVALID),
+    (dict(w=None), M.MOE_ERR_INVALID),
+    (dict(out=A16b + 2), M.MOE_ERR_INVALID),
+    (dict(y=A16 + 4), M.MOE_ERR_INVALID),
+    (dict(T=-5), M.MOE_ERR_INVALID),
+])
+def test_combine_rejects(kw, status):
+    assert _combine(**kw) == status
+    assert M.moe_last_error().startswith("moe_combine")
+
+
+def test_workspace_bytes():
+    assert M.moe_layout_workspace_bytes(0, 8, 2) == 0
+    assert M.moe_layout_workspace_bytes(-1, 8, 2) == 0
+    # one tile per 1024 pairs, 2*E ints per tile
+    assert M.moe_layout_workspace_bytes(4096, 256, 8) == 32 * 2 * 256 * 4
+    assert M.moe_layout_workspace_bytes(4097, 256, 8) == 33 * 2 * 256 * 4
+
+
+def test_binding_raises_with_message():
+    _no_gpu()
+    with pytest.raises(M.MoeError, match="MOE_ERR_INVALID.*num_tokens"):
+        M.moe_route(-1, 8, 2, A16, None, 0, 1, 1, A16, A16b, stream=0)
