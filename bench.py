@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE expert-parallel hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+route (group-limited sigmoid top-k) -> layout (counts, offsets, stable
+rows) -> dispatch (FP8 e4m3 + per-1x128 scales) -> combine (weighted bf16
+sum). The stand-in expert between dispatch and combine is not part of the
+path: its output (dequantised rows) is prepared once before timing.
+
+Default workload: the DeepSeek-V3-shaped layer, T=4096 tokens, hidden 7168,
+256 experts in 8 groups (top-4 groups, top-8 experts), 32 simulated ranks,
+FP8 dispatch, bf16 combine. Inputs are seeded synthetic data already resident
+in HBM when timing starts.
+
+Prints one JSON line. Besides the contract fields it carries:
+  roofline      HBM roofline of the dominant kernel (combine): algorithmic
+                bytes per launch / average launch time from HIP events
+                recorded on the launch stream; `traffic` comes from the
+                committed rocprofv3 counter summary when it was taken on the
+                current kernel source, else null
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  phases_us     average per-phase times (events) of the timed steps
+  cold_us_per_step  the same step with a 1 GiB write between steps, which
+                evicts L2 and the 256 MB Infinity Cache
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_traffic.json")
+COMBINE_SOURCES = [os.path.join(ROOT, "combine_moe_layout_06_amd", "csrc", f)
+                   for f in ("combine.hip", "wave.h")]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="dsv3",
+                   choices=["dsv3", "mixtral", "qwen3_skew", "tiny", "decode"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cold-steps", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def step_bytes(w, rows_live):
+    """Algorithmic bytes of one step, per phase (what the method must move)."""
+    T, H, E, k = w.tokens, w.hidden, w.experts, w.top_k
+    rows = w.num_rows
+    fp8 = w.dispatch_dtype == 1
+    route = T * E * 4 + (E * 4 if w.bias != "none" else 0) + T * k * 8
+    layout = T * k * 4 + T * k * 4 + rows * 4 + (3 * E + 3 * w.ranks + 3) * 4
+    if fp8:
+        dispatch = T * H * 2 + T * k * 4 + rows_live * H + rows_live * (H // 128) * 4
+    else:
+        dispatch = T * H * 2 + T * k * 4 + rows_live * H * 2
+    combine = rows_live * H * 2 + T * k * 8 + T * H * 2
+    return dict(route=route, layout=layout, dispatch=dispatch, combine=combine)
+
+
+def sha_of(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per combine launch from the committed counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != sha_of(COMBINE_SOURCES):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 5}), flush=True)
+
+
+def copy_ceiling_gbps():
+    """Read+write GB/s of a plain 512 MiB device-to-device copy."""
+    import torch
+    n = 1 << 29
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    reps = 20
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    return 2.0 * n * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+
+
+def cpu_baseline(w, seed, budget_s):
+    """The CPU oracle (numpy, one thread) on a bounded sample of the same
+    workload: the first `ts` tokens, the whole path per repeat."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from synth import workloads as W
+
+    ts = min(w.tokens, 512)
+    inp = W.make_inputs(w, seed, tokens=ts)
+    idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+    L = O.layout(idx, w.experts, w.ranks, w.capacity)
+    if w.dispatch_dtype == 1:
+        codes, sc = O.quantize_fp8_blocks(inp.x)
+        y_tok = O.expert_dequant(codes, sc)
+    else:
+        y_tok = inp.x
+    y, _ = O.dispatch_bf16(y_tok, L["dst_row"], L["num_rows"])
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+        L = O.layout(idx, w.experts, w.ranks, w.capacity)
+        if w.dispatch_dtype == 1:
+            O.dispatch_fp8(inp.x, L["dst_row"], L["num_rows"])
+        else:
+            O.dispatch_bf16(inp.x, L["dst_row"], L["num_rows"])
+        O.combine(y, L["dst_row"], wt)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and reps >= 1:
+            break
+    return {"value": ts * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%s shape, first %d of %d tokens, %d repeats of route+layout+"
+                      "dispatch+combine in %.1f s (numpy, single thread)"
+                      % (w.name, ts, w.tokens, reps, el)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs the hot path on one GPU only: the simulated destination "
+              "ranks are regions of one GPU's HBM and no collective is built, so "
+              "--gpus %d is not supported" % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_moe_layout_06_amd as M
+    from synth import workloads as W
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fp8 = w.dispatch_dtype == W.DTYPE_FP8_E4M3
+    steps, warm = args.steps, args.warmup
+
+    # ---- inputs, resident in HBM before timing
+    n_inputs = steps + warm if w.steps > 1 else 1
+    seeds = [w.step_seed0 + i for i in range(n_inputs)] if w.steps > 1 else [args.seed]
+    inputs = []
+    for s in seeds:
+        inp = W.make_inputs(w, s)
+        inputs.append(dict(
+            logits=torch.from_numpy(inp.logits).to(dev),
+            bias=torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None,
+            x=torch.from_numpy(inp.x.view(np.int16)).to(dev)))
+    buf = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
+                                  w.capacity, fp8, device=dev)
+
+    def front(i):
+        d = inputs[i % len(inputs)]
+        buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        buf.layout()
+        buf.dispatch(d["x"])
+
+    # stand-in expert output (harness): dequantised / scaled rows of step 0
+    front(0)
+    torch.cuda.synchronize()
+    rows = buf.num_rows
+    if fp8:
+        codes = buf.dispatched[:rows].view(torch.float8_e4m3fn).float()
+        sc = buf.scales[:rows].repeat_interleave(128, dim=1)
+        y = (codes * sc).to(torch.bfloat16).view(torch.int16).contiguous()
+    elif w.expert_kind == "scaled":
+        off = buf.expert_offsets.cpu().numpy()
+        e_of_row = torch.from_numpy(np.searchsorted(off[1:], np.arange(rows), side="right")).to(dev)
+        c = ((e_of_row + 1).float() / w.experts)[:, None]
+        y = (buf.dispatched[:rows].view(torch.bfloat16).float() * c).to(torch.bfloat16)
+        y = y.view(torch.int16).contiguous()
+    else:
+        y = buf.dispatched[:rows].clone()
+    rows_live = int((buf.dst_row >= 0).sum().item())
+    nbytes = step_bytes(w, rows_live)
+    total_bytes = sum(nbytes.values())
+
+    # ---- warmup
+    for i in range(warm):
+        front(i)
+        buf.combine(y)
+    torch.cuda.synchronize()
+
+    # ---- timed steps, with events between the phases
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        d = inputs[(warm + i) % len(inputs)]
+        e = ev[i]
+        e[0].record()
+        buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        e[1].record()
+        buf.layout()
+        e[2].record()
+        buf.dispatch(d["x"])
+        e[3].record()
+        buf.combine(y)
+        e[4].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["route", "layout", "dispatch", "combine"]
+    phase_ms = {n: 0.0 for n in names}
+    step_ms = []
+    for e in ev:
+        for j, n in enumerate(names):
+            phase_ms[n] += e[j].elapsed_time(e[j + 1]) / steps
+        step_ms.append(e[0].elapsed_time(e[4]))
+    ms_per_step = wall * 1e3 / steps
+    value = w.tokens / (ms_per_step * 1e-3)
+
+    # ---- cold steps: 1 GiB write between steps (untimed)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.cold_steps):
+        flush.zero_()
+        d = inputs[i % len(inputs)]
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        buf.layout()
+        buf.dispatch(d["x"])
+        buf.combine(y)
+        e.record()
+        torch.cuda.synchronize()
+        cold.append(s.elapsed_time(e))
+    del flush
+
+    comb_s = phase_ms["combine"] * 1e-3
+    achieved = nbytes["combine"] / comb_s / 1e9
+    roof = {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(), "algorithmic_bytes_per_launch": nbytes["combine"]}
+
+    out = {
+        "metric": "dispatch+combine tokens/s and HBM GB/s (% of peak), DeepSeek-V3 shape, 1 GPU",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
+                   % (w.name, w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
+                      "group-limited sigmoid G=%d kg=%d" % (w.groups, w.topk_groups)
+                      if w.groups > 1 else ("sigmoid" if w.score_fn else "softmax"),
+                      ", zipf bias" if w.bias == "zipf" else "",
+                      "fp8 e4m3 (1x128 scales)" if fp8 else "bf16",
+                      ", capacity %d" % w.capacity if w.capacity else ""),
+                   "tokens": w.tokens, "hidden": w.hidden, "experts": w.experts,
+                   "top_k": w.top_k, "ranks": w.ranks, "seed": args.seed},
+        "gbps": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total_bytes,
+        "phases_us": {n: round(v * 1e3, 2) for n, v in phase_ms.items()},
+        "phase_bytes": nbytes,
+        "event_us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
+        "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
+        "copy_ceiling_gbps": round(copy_ceiling_gbps(), 1),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
