@@ -21,6 +21,10 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+#ifndef MOE_COMBINE_U8
+#define MOE_COMBINE_U8 2   // 16-byte chunks per lane per step when k = 8
+#endif
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = base + u * MOE_WAVE + lane;
-        if (d[j] >= 0 && c < cnt) v[j][u] = __builtin_nontemporal_load(row + c);
+        if (d[j] >= 0 && c < cnt) v[j][u] = stream_load(row + c);
       }
     }
 #pragma unroll
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
       for (int j = 0; j < K; ++j)
         if (d[j] >= 0) fma_row(acc, wj[j], v[j][u]);
-      if (c < cnt) __builtin_nontemporal_store(pack_row(acc), dst + c);
+      if (c < cnt) stream_store(pack_row(acc), dst + c);
     }
   }
 }
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
       for (int u = 0; u < U; ++u) {
         const int c = base + u * MOE_WAVE + lane;
         v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (c < cnt) v[u] = __builtin_nontemporal_load(row + c);
+        if (c < cnt) v[u] = stream_load(row + c);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) fma_row(acc[u], wj, v[u]);
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = base + u * MOE_WAVE + lane;
-      if (c < cnt) __builtin_nontemporal_store(pack_row(acc[u]), dst + c);
+      if (c < cnt) stream_store(pack_row(acc[u]), dst + c);
     }
   }
 }
@@ -167,7 +171,7 @@ hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
     case 2: launch_fixed<2, 4>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
     case 4: launch_fixed<4, 2>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
     case 6: launch_fixed<6, 1>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
-    case 8: launch_fixed<8, 1>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
+    case 8: launch_fixed<8, MOE_COMBINE_U8>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
     default:
       hipLaunchKernelGGL(combine_kernel_any_k, grid, dim3(256), 0, stream, T, k, nch, parts,
                          cpp, num_rows, static_cast<const u32x4*>(y), dst_row, w,

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(
     for (int u = 0; u < kUnroll; ++u) {
       const int c = base + u * MOE_WAVE + lane;
       v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (c < cnt) v[u] = __builtin_nontemporal_load(src + c);
+      if (c < cnt) v[u] = stream_load(src + c);
     }
     for (int j = 0; j < k; ++j) {
       const int d = read_lane(my_dst, j);
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = base + u * MOE_WAVE + lane;
-        if (c < cnt) __builtin_nontemporal_store(v[u], dst + c);
+        if (c < cnt) stream_store(v[u], dst + c);
       }
     }
   }
@@ -86,16 +86,60 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float p) {
   return sign | mag;
 }
 
-// Quantise one bf16 element (held in the low 16 bits of `h`).
+// Quantise one bf16 element (held in the low 16 bits of `h`) in software.
 __device__ __forceinline__ uint32_t quant_one(uint32_t h, float inv) {
   const float xv = __uint_as_float(h << 16);
   if ((h & 0x7FFFu) == 0u) return (h >> 8) & 0x80u;       // +-0 keeps its sign
   return e4m3_from_f32(xv * inv);
 }
 
-__device__ __forceinline__ uint32_t quant_pair(uint32_t w, float inv) {
+__device__ __forceinline__ uint32_t quant_pair_sw(uint32_t w, float inv) {
   return quant_one(w & 0xFFFFu, inv) | (quant_one(w >> 16, inv) << 8);
 }
+
+// Two bf16 -> two e4m3 codes with the hardware pack-convert (round to
+// nearest even). Products are clamped to +-448 first; for every fp32 value
+// of magnitude <= 464 this gives the same code as e4m3_from_f32 (checked
+// exhaustively on the device). Needs a finite multiplier: then +-0 stays +-0.
+__device__ __forceinline__ uint32_t quant_pair_hw(uint32_t w, float inv) {
+  const float a = __builtin_amdgcn_fmed3f(__uint_as_float(w << 16) * inv, -448.0f, 448.0f);
+  const float b = __builtin_amdgcn_fmed3f(__uint_as_float(w & 0xFFFF0000u) * inv, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// 8 bf16 (16 bytes) -> 8 codes (8 bytes)
+__device__ __forceinline__ u32x2 quant8(const u32x4& v, float inv) {
+  u32x2 q;
+  if (__builtin_isfinite(inv)) {
+    q[0] = quant_pair_hw(v[0], inv) | (quant_pair_hw(v[1], inv) << 16);
+    q[1] = quant_pair_hw(v[2], inv) | (quant_pair_hw(v[3], inv) << 16);
+  } else {   // the block's amax is so small that 448/amax overflows
+    q[0] = quant_pair_sw(v[0], inv) | (quant_pair_sw(v[1], inv) << 16);
+    q[1] = quant_pair_sw(v[2], inv) | (quant_pair_sw(v[3], inv) << 16);
+  }
+  return q;
+}
+
+// Block amax of the 16 lanes of a DPP row, from the bf16 magnitudes (their
+// bit patterns order like the values).
+__device__ __forceinline__ float block_amax(const u32x4& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = v[q] & 0x7FFF7FFFu;
+    m = max(m, max(w & 0xFFFFu, w >> 16));
+  }
+  return __uint_as_float(row16_max(m) << 16);
+}
+
+// One wave per (token, part of kFp8StepBlocks-block steps). A step covers
+// 1024 columns: lane L holds chunk A = columns [8L, 8L+8) and chunk B =
+// columns [512 + 8L, 512 + 8L + 8); the 16 lanes of a DPP row form one
+// 128-column block of A and one of B. After quantisation the lanes of a pair
+// (2i, 2i+1) swap halves, so lane 2i writes codes of A-columns [16i, 16i+16)
+// and lane 2i+1 those of B-columns [16i, 16i+16): one 16-byte store per lane
+// and copy.
+constexpr int kFp8StepBlocks = 8;
 
 __global__ __launch_bounds__(256) void dispatch_fp8_kernel(
     int T, int k, int H, int parts, int bpp, int num_rows,
@@ -110,40 +154,46 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(
   const int b0 = (gw - t * parts) * bpp;
   const int nbp = min(bpp, nb - b0);
   const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const int group = lane >> 4;       // which of the 4 blocks of a 512-column step
+  const int group = lane >> 4;       // block of A (and of B) inside the step
   const int sub = lane & 15;         // 16-byte chunk inside the block
+  const bool odd = lane & 1;
   const u32x4* src = x + (size_t)t * nch;
 
   float sreg[kScaleSlots];
 #pragma unroll
   for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0.0f;
 
-  for (int it = 0; it * 4 < nbp; ++it) {
-    const int bl = it * 4 + group;
-    const bool act = bl < nbp;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (act) v = __builtin_nontemporal_load(src + (b0 + bl) * 16 + sub);
+  for (int st = 0; st * kFp8StepBlocks < nbp; ++st) {
+    const int ba = st * kFp8StepBlocks + group;          // part-local blocks
+    const int bb = ba + kFp8StepBlocks / 2;
+    const bool act_a = ba < nbp, act_b = bb < nbp;
+    u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+    if (act_a) va = stream_load(src + (b0 + ba) * 16 + sub);
+    if (act_b) vb = stream_load(src + (b0 + bb) * 16 + sub);
 
-    // block amax on the bf16 magnitudes (their bit patterns order like values)
-    uint32_t m = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = v[q] & 0x7FFF7FFFu;
-      m = max(m, max(w & 0xFFFFu, w >> 16));
-    }
-    m = row16_max(m);
-    const float amax = __uint_as_float(m << 16);
-    const float scale = amax / 448.0f;
-    const float inv = 448.0f / amax;
+    const float amax_a = block_amax(va), amax_b = block_amax(vb);
+    const float scale_a = amax_a / 448.0f, scale_b = amax_b / 448.0f;
+    // lanes of a block past the part's end quantise with multiplier 1 (their
+    // codes are never stored), which keeps the whole wave on the fast path
+    const u32x2 qa = quant8(va, act_a ? 448.0f / amax_a : 1.0f);
+    const u32x2 qb = quant8(vb, act_b ? 448.0f / amax_b : 1.0f);
 
-    const uint32_t lo = quant_pair(v[0], inv) | (quant_pair(v[1], inv) << 16);
-    const uint32_t hi = quant_pair(v[2], inv) | (quant_pair(v[3], inv) << 16);
+    // swap halves inside lane pairs: even lanes keep A, odd lanes keep B
+    const u32x2 send = odd ? qa : qb;
+    u32x2 recv;
+    recv[0] = dpp_u32<0xB1>(send[0]);
+    recv[1] = dpp_u32<0xB1>(send[1]);
+    const u32x4 q = odd ? u32x4{recv[0], recv[1], qb[0], qb[1]}
+                        : u32x4{qa[0], qa[1], recv[0], recv[1]};
+    const int bq = odd ? bb : ba;                        // block this lane writes
+    const bool act_q = odd ? act_b : act_a;
+    const int col = (b0 + bq) * MOE_FP8_BLOCK + (sub & ~1) * 8;   // 16-byte aligned
 
     // lane (b & 63), slot (b >> 6) keeps the scale of part-local block b
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int b = it * 4 + g;
-      const float sg = read_lane(scale, g * 16);
+    for (int g = 0; g < kFp8StepBlocks; ++g) {
+      const int b = st * kFp8StepBlocks + g;
+      const float sg = read_lane(g < 4 ? scale_a : scale_b, (g & 3) * 16);
       if (b < nbp && lane == (b & 63)) {
 #pragma unroll
         for (int s = 0; s < kScaleSlots; ++s)
@@ -151,14 +201,10 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(
       }
     }
 
-    if (act) {
-      const u32x2 q = {lo, hi};
-      for (int j = 0; j < k; ++j) {
-        const int d = read_lane(my_dst, j);
-        if (d < 0 || d >= num_rows) continue;
-        u32x2* dst = reinterpret_cast<u32x2*>(out + (size_t)d * H + (size_t)(b0 + bl) * MOE_FP8_BLOCK) + sub;
-        __builtin_nontemporal_store(q, dst);
-      }
+    for (int j = 0; j < k; ++j) {
+      const int d = read_lane(my_dst, j);
+      if (d < 0 || d >= num_rows) continue;
+      if (act_q) stream_store(q, reinterpret_cast<u32x4*>(out + (size_t)d * H + col));
     }
   }
 
@@ -208,7 +254,7 @@ hipError_t launch_dispatch_fp8(int T, int H, int k, int num_rows, const void* x,
   if (T == 0) return hipSuccess;
   const int nb = H / MOE_FP8_BLOCK;
   int parts, bpp;
-  split_row(T, nb, 4, 64 * kScaleSlots, &parts, &bpp);
+  split_row(T, nb, kFp8StepBlocks, 64 * kScaleSlots, &parts, &bpp);
   const int waves = T * parts;
   hipLaunchKernelGGL(dispatch_fp8_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
                      dim3(256), 0, stream, T, k, H, parts, bpp, num_rows,

@@ -37,7 +37,11 @@ hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
                           hipStream_t stream);
 
-// Number of waves a row-parallel kernel aims for: 256 CUs x 32 wave slots.
-constexpr int kTargetWaves = 8192;
+// Number of waves a row-parallel kernel aims for: about four times the
+// 256 CUs x 32 wave slots, so that short waves keep every CU busy to the end.
+#ifndef MOE_TARGET_WAVES
+#define MOE_TARGET_WAVES 32768
+#endif
+constexpr int kTargetWaves = MOE_TARGET_WAVES;
 
 }  // namespace moe

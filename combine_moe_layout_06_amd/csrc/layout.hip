@@ -29,53 +29,74 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kTilePairs = 1024;                          // pairs per tile (max)
 constexpr int kChunks = kTilePairs / kWaves / MOE_WAVE;   // 64-pair chunks per wave
+constexpr int kStage = 8192;                              // histogram ints staged per pass
 
 __device__ __forceinline__ int clean_expert(int v, int E) {
   return (v >= 0 && v < E) ? v : -1;
 }
 
+// Rank of an expert: a shift when E/R is a power of two, else a division.
+__device__ __forceinline__ int rank_of(int e, int epr, int epr_shift) {
+  return epr_shift >= 0 ? (e >> epr_shift) : e / epr;
+}
+
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(
-    int T, int E, int k, int R, int epr, int tt, const int32_t* __restrict__ idx,
-    int32_t* __restrict__ ws_hist, int32_t* __restrict__ ws_rhist) {
+    int T, int E, int k, int R, int epr, int epr_shift, int tt,
+    const int32_t* __restrict__ idx, int32_t* __restrict__ ws_hist,
+    int32_t* __restrict__ ws_rhist) {
   __shared__ int s_hist[MOE_MAX_EXPERTS];
   __shared__ int s_rhist[MOE_MAX_EXPERTS];
-  __shared__ int s_idx[kTilePairs];
+  __shared__ int s_rank[kTilePairs];     // rank of each pair, -1 if masked
 
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
   const int tok0 = tile * tt;
-  const int np = min(tt, T - tok0) * k;
+  const int ntok = min(tt, T - tok0);
+  const int np = ntok * k;
   const int32_t* src = idx + (size_t)tok0 * k;
-  const int nbits = ceil_log2(E);
 
+  // all loads of the tile are issued before the first use
+  int v[kTilePairs / kThreads];
+#pragma unroll
+  for (int q = 0; q < kTilePairs / kThreads; ++q) {
+    const int p = q * kThreads + tid;
+    v[q] = p < np ? src[p] : -1;
+  }
   for (int e = tid; e < E; e += kThreads) { s_hist[e] = 0; s_rhist[e] = 0; }
   __syncthreads();
-
-  for (int base = 0; base < np; base += kThreads) {
-    const int p = base + tid;
-    const int v = p < np ? clean_expert(src[p], E) : -1;
-    if (p < np) s_idx[p] = v;
-    const uint64_t peers = peer_mask((uint32_t)v, v >= 0, nbits);
-    if (v >= 0 && count_below(peers) == 0) atomicAdd(&s_hist[v], __popcll(peers));
+#pragma unroll
+  for (int q = 0; q < kTilePairs / kThreads; ++q) {
+    const int p = q * kThreads + tid;
+    const int e = clean_expert(v[q], E);
+    if (p < np) s_rank[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+    if (e >= 0) atomicAdd(&s_hist[e], 1);
   }
   __syncthreads();
 
   if (ws_rhist != nullptr) {
-    // a pair counts for its rank if no earlier slot of the token is on it
-    for (int p = tid; p < np; p += kThreads) {
-      const int v = s_idx[p];
-      if (v < 0) continue;
-      const int r = v / epr;
-      const int j = p % k;
-      bool first = true;
-      for (int q = 0; q < j; ++q) {
-        const int o = s_idx[p - j + q];
-        first = first && !(o >= 0 && o / epr == r);
+    // one thread per token: a rank counts once, at its first slot
+    for (int tl = tid; tl < ntok; tl += kThreads) {
+      const int* r = s_rank + tl * k;
+      if (R <= 64) {
+        uint64_t seen = 0;
+        for (int j = 0; j < k; ++j) {
+          const int x = r[j];
+          if (x >= 0 && !((seen >> x) & 1ull)) {
+            seen |= 1ull << x;
+            atomicAdd(&s_rhist[x], 1);
+          }
+        }
+      } else {
+        for (int j = 0; j < k; ++j) {
+          const int x = r[j];
+          bool first = x >= 0;
+          for (int o = 0; o < j; ++o) first = first && r[o] != x;
+          if (first) atomicAdd(&s_rhist[x], 1);
+        }
       }
-      if (first) atomicAdd(&s_rhist[r], 1);
     }
     __syncthreads();
-    for (int r = tid; r < R; r += kThreads) ws_rhist[(size_t)tile * R + r] = s_rhist[r];
+    for (int q = tid; q < R; q += kThreads) ws_rhist[(size_t)tile * R + q] = s_rhist[q];
   }
   for (int e = tid; e < E; e += kThreads) ws_hist[(size_t)tile * E + e] = s_hist[e];
 }
@@ -115,6 +136,33 @@ __device__ int block_exclusive_scan(int* s, int n, int* s_wave) {
   return total;
 }
 
+// Load n ints of `src` (n <= kStage) into registers, all in flight at once.
+__device__ __forceinline__ void stage_load(int (&h)[kStage / kThreads], const int32_t* src, int n) {
+#pragma unroll
+  for (int q = 0; q < kStage / kThreads; ++q) {
+    const int i = q * kThreads + threadIdx.x;
+    h[q] = i < n ? src[i] : 0;
+  }
+}
+__device__ __forceinline__ void stage_store(const int (&h)[kStage / kThreads], int* s_stage) {
+#pragma unroll
+  for (int q = 0; q < kStage / kThreads; ++q) s_stage[q * kThreads + threadIdx.x] = h[q];
+}
+
+// Sum column c of a row-major [rows, W] matrix whose flat elements
+// [c0, c0 + n) are staged in s_stage; rows below `limit` also go to *pre.
+__device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, int W, int c,
+                                            int limit, int* tot, int* pre) {
+  int t = 0, p = 0;
+  for (int b = (c0 + W - 1 - c) / W; b * W + c < c0 + n; ++b) {
+    const int x = s_stage[b * W + c - c0];
+    t += x;
+    p += b < limit ? x : 0;
+  }
+  *tot += t;
+  *pre += p;
+}
+
 __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     int T, int E, int k, int R, int epr, int cap, int tt, int ntiles, int num_rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_hist,
@@ -126,28 +174,62 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
+  __shared__ int s_rtc[MOE_MAX_EXPERTS];
   __shared__ int s_cnt[kWaves][MOE_MAX_EXPERTS];
   __shared__ int s_base[kWaves][MOE_MAX_EXPERTS];
   __shared__ int s_wave[kWaves];
   __shared__ int s_overflow;
+  __shared__ int s_stage[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x;   // blocks at or past ntiles only fill unused rows
+  const int tok0 = tile * tt;
+  const int np = tile < ntiles ? min(tt, T - tok0) * k : 0;
+  const size_t pair0 = (size_t)tok0 * k;
 
-  // per-expert totals and the base of this tile (sum over earlier tiles)
+  // this tile's pairs and the first histogram chunk are loaded together
+  int v[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    v[c] = p < np ? idx[pair0 + p] : -1;
+  }
+  const int hist_n = ntiles * E;
+  int h[kStage / kThreads];
+  stage_load(h, ws_hist, min(kStage, hist_n));
+
   for (int e = tid; e < E; e += kThreads) {
-    int pre = 0, tot = 0;
-    for (int b = 0; b < ntiles; ++b) {
-      const int h = ws_hist[(size_t)b * E + e];
-      tot += h;
-      pre += b < tile ? h : 0;
-    }
-    s_tot[e] = tot;
-    s_pre[e] = pre;
-    s_off[e] = cap > 0 ? 0 : tot;
+    s_tot[e] = 0;
+    s_pre[e] = 0;
+    s_rtc[e] = 0;
     for (int w = 0; w < kWaves; ++w) s_cnt[w][e] = 0;
   }
   if (tid == 0) s_overflow = 0;
+
+  // per-expert totals and the base of this tile (sum over earlier tiles)
+  for (int c0 = 0; c0 < hist_n; c0 += kStage) {
+    const int n = min(kStage, hist_n - c0);
+    if (c0 > 0) stage_load(h, ws_hist + c0, n);
+    __syncthreads();   // the previous chunk has been consumed
+    stage_store(h, s_stage);
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) column_sums(s_stage, c0, n, E, e, tile, &s_tot[e], &s_pre[e]);
+  }
+  // block 0 also sums the per-tile distinct-token counts of each rank
+  if (tile == 0 && rank_token_counts != nullptr) {
+    const int rn = ntiles * R;
+    for (int c0 = 0; c0 < rn; c0 += kStage) {
+      const int n = min(kStage, rn - c0);
+      stage_load(h, ws_rhist + c0, n);
+      __syncthreads();
+      stage_store(h, s_stage);
+      __syncthreads();
+      int unused = 0;
+      for (int r = tid; r < R; r += kThreads) column_sums(s_stage, c0, n, R, r, 0, &s_rtc[r], &unused);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) s_off[e] = cap > 0 ? 0 : s_tot[e];
   __syncthreads();
   if (cap > 0) {
     for (int e = tid; e <= E; e += kThreads) s_off[e] = e * cap;
@@ -171,29 +253,22 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
         rows += cap > 0 ? min(s_tot[e], cap) : s_tot[e];
       rank_counts[r] = rows;
       rank_offsets[r] = s_off[r * epr];
-      if (rank_token_counts != nullptr) {
-        int c = 0;
-        for (int b = 0; b < ntiles; ++b) c += ws_rhist[(size_t)b * R + r];
-        rank_token_counts[r] = c;
-      }
+      if (rank_token_counts != nullptr) rank_token_counts[r] = s_rtc[r];
     }
     if (tid == 0) rank_offsets[R] = s_off[E];
     __syncthreads();
     if (tid == 0) overflow[0] = s_overflow;
   }
 
-  // stable placement of this tile's pairs
-  const int tok0 = tile * tt;
-  const int np = T > 0 ? min(tt, T - tok0) * k : 0;
-  const size_t pair0 = (size_t)tok0 * k;
+  // stable placement of this tile's pairs: count per wave, chain the waves,
+  // then rank inside each wave by lane order
   const int nbits = ceil_log2(E);
-  int v[kChunks];
+  uint64_t peers[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
-    v[c] = p < np ? clean_expert(idx[pair0 + p], E) : -1;
-    const uint64_t peers = peer_mask((uint32_t)v[c], v[c] >= 0, nbits);
-    if (v[c] >= 0 && count_below(peers) == 0) atomicAdd(&s_cnt[wave][v[c]], __popcll(peers));
+    v[c] = clean_expert(v[c], E);
+    peers[c] = peer_mask((uint32_t)v[c], v[c] >= 0, nbits);
+    if (v[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][v[c]], __popcll(peers[c]));
   }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
@@ -208,12 +283,11 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   for (int c = 0; c < kChunks; ++c) {
     const int p = (wave * kChunks + c) * MOE_WAVE + lane;
     const int e = v[c];
-    const uint64_t peers = peer_mask((uint32_t)e, e >= 0, nbits);
     int dst = -1;
     if (e >= 0) {
-      const int below = count_below(peers);
+      const int below = count_below(peers[c]);
       const int pos = s_base[wave][e] + below;
-      if (below == 0) atomicAdd(&s_base[wave][e], __popcll(peers));
+      if (below == 0) atomicAdd(&s_base[wave][e], __popcll(peers[c]));
       if (cap == 0) dst = s_off[e] + pos;
       else if (pos < cap) dst = e * cap + pos;
     }
@@ -223,16 +297,17 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     }
   }
 
-  // rows that receive no pair are marked -1 (spread over all blocks)
-  for (int row = tile * kThreads + tid; row < num_rows; row += gridDim.x * kThreads) {
-    bool unused;
-    if (cap == 0) {
-      unused = row >= s_off[E];
-    } else {
-      const int e = row / cap;
-      unused = (row - e * cap) >= s_tot[e];
+  // rows that receive no pair are marked -1; all waves of the grid share it
+  const int gwave = tile * kWaves + wave, nwaves = gridDim.x * kWaves;
+  if (cap == 0) {
+    for (int row = s_off[E] + gwave * MOE_WAVE + lane; row < num_rows; row += nwaves * MOE_WAVE)
+      src_pair[row] = -1;
+  } else {
+    for (int e = gwave; e < E; e += nwaves) {
+      const int end = (e + 1) * cap;
+      for (int row = e * cap + min(s_tot[e], cap) + lane; row < end; row += MOE_WAVE)
+        src_pair[row] = -1;
     }
-    if (unused) src_pair[row] = -1;
   }
 }
 
@@ -262,13 +337,18 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   const int num_rows = cap > 0 ? E * cap : T * k;
   int32_t* ws_hist = static_cast<int32_t*>(workspace);
   int32_t* ws_rhist = rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
+  const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
   if (ntiles > 0) {
     hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
-                       T, E, k, R, epr, tt, idx, ws_hist, ws_rhist);
+                       T, E, k, R, epr, epr_shift, tt, idx, ws_hist, ws_rhist);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(layout_place_kernel, dim3(ntiles > 0 ? ntiles : 1), dim3(kThreads), 0,
+  // padded buffers: enough waves that each fills the unused rows of about
+  // one expert
+  const int fill_blocks = cap > 0 ? (E + kWaves - 1) / kWaves : 1;
+  const int blocks = ntiles > fill_blocks ? ntiles : fill_blocks;
+  hipLaunchKernelGGL(layout_place_kernel, dim3(blocks), dim3(kThreads), 0,
                      stream, T, E, k, R, epr, cap, tt, ntiles, num_rows, idx, ws_hist,
                      ws_rhist, expert_counts, expert_offsets, rank_counts, rank_offsets,
                      rank_token_counts, dst_row, src_pair, overflow);

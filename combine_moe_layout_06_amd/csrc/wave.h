@@ -9,6 +9,25 @@
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Streaming accesses: data touched once per call bypass the caches' normal
+// retention (nontemporal hint) unless built with MOE_TEMPORAL_ROWS.
+template <typename V>
+__device__ __forceinline__ V stream_load(const V* p) {
+#ifdef MOE_TEMPORAL_ROWS
+  return *p;
+#else
+  return __builtin_nontemporal_load(p);
+#endif
+}
+template <typename V>
+__device__ __forceinline__ void stream_store(V v, V* p) {
+#ifdef MOE_TEMPORAL_ROWS
+  *p = v;
+#else
+  __builtin_nontemporal_store(v, p);
+#endif
+}
+
 __device__ __forceinline__ int lane_id() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
@@ -48,4 +67,67 @@ __device__ __forceinline__ int ceil_log2(int n) {
   int b = 0;
   while ((1 << b) < n) ++b;
   return b;
+}
+
+// DPP lane moves inside 16-lane rows (gfx9 DPP controls):
+//   0xB1 quad_perm(1,0,3,2)   0x4E quad_perm(2,3,0,1)
+//   0x141 row_half_mirror     0x140 row_mirror
+// Applying an associative, commutative op after each of the four moves in
+// that order leaves the op over the whole row in every lane of the row.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  return __longlong_as_double((long long)dpp_u64<CTRL>((uint64_t)__double_as_longlong(v)));
+}
+
+__device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double read_lane_f64(double v, int src) {
+  return __longlong_as_double((long long)read_lane_u64((uint64_t)__double_as_longlong(v), src));
+}
+
+// Wave-wide reductions: DPP inside each row, then the four row results are
+// read into scalars and combined there. The result is wave-uniform.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;
+  o = dpp_u64<0x141>(v); v = o > v ? o : v;
+  o = dpp_u64<0x140>(v); v = o > v ? o : v;
+  const uint64_t r0 = read_lane_u64(v, 0), r1 = read_lane_u64(v, 16);
+  const uint64_t r2 = read_lane_u64(v, 32), r3 = read_lane_u64(v, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  return (read_lane_f64(v, 0) + read_lane_f64(v, 16)) + (read_lane_f64(v, 32) + read_lane_f64(v, 48));
 }

@@ -77,6 +77,16 @@ ROUTE_CASES = [
     (130, 200, 7, 1, 5, 2, "normal", "normal"),
     (3, 256, 8, 1, 8, 4, "normal", "normal"),
     (0, 256, 8, 1, 8, 4, None, "normal"),
+    # 16-lane teams: 1, 2 and 4 slots per group, k = team size
+    (999, 128, 16, 1, 2, 1, "normal", "normal"),
+    (517, 128, 8, 1, 4, 2, "normal", "normal"),
+    (700, 128, 6, 1, 8, 5, "normal", "normal"),
+    (333, 64, 8, 1, 2, 1, "int", "int"),
+    (600, 128, 16, 0, 1, 1, None, "normal"),
+    (450, 192, 8, 1, 6, 3, "int", "int"),
+    # k above the team size falls back to one wave per token
+    (300, 64, 10, 0, 1, 1, None, "normal"),
+    (301, 40, 9, 1, 1, 1, "normal", "normal"),
 ]
 
 
