@@ -32,6 +32,16 @@ __device__ __forceinline__ uint64_t candidate(float key, int e) {
   return ((uint64_t)ordered_bits(key) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// Wave max of a 32-bit value, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  v = max(v, xor16_u32(v));
+  return max(v, xor32_u32(v));
+}
+
 // Top-2 merge of (largest, second largest) pairs.
 __device__ __forceinline__ void merge_top2(float& m1, float& m2, float o1, float o2) {
   const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
@@ -72,8 +82,10 @@ __global__ __launch_bounds__(256) void route_kernel(
     const int gs = E / G;
     float gscore = 0.0f;                // lane g < G: score of group g
     if (gs == 16 || gs == 32 || gs == 64) {
-      // groups cover whole 16-lane rows of one slot: top-2 per row in
-      // registers, then rows of a group are merged from scalar reads
+      // groups cover whole rows of one slot: top-2 per row with DPP, then
+      // the row and half swaps merge the rows of a group (16: none, 32: one
+      // swap, 64: two). Group scores are then spread so that lane g < G
+      // holds the score of group g.
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         float m1 = ok[i] ? key[i] : -INFINITY, m2 = -INFINITY;
@@ -81,13 +93,17 @@ __global__ __launch_bounds__(256) void route_kernel(
         dpp_top2<0x4E>(m1, m2);
         dpp_top2<0x141>(m1, m2);
         dpp_top2<0x140>(m1, m2);
-        const int rows = gs / 16;
-        for (int g = (64 * i) / gs; g < min(G, (64 * (i + 1)) / gs); ++g) {
-          const int r0 = (g * gs - 64 * i) / 16;
-          float a1 = read_lane(m1, 16 * r0), a2 = read_lane(m2, 16 * r0);
-          for (int r = 1; r < rows; ++r)
-            merge_top2(a1, a2, read_lane(m1, 16 * (r0 + r)), read_lane(m2, 16 * (r0 + r)));
-          if (lane == g) gscore = a1 + a2;
+        if (gs >= 32) merge_top2(m1, m2, xor16_f32(m1), xor16_f32(m2));
+        if (gs == 64) merge_top2(m1, m2, xor32_f32(m1), xor32_f32(m2));
+        const float sc = m1 + m2;          // score of the group holding this lane, slot i
+        // group of (slot i, this lane) is (64 i + lane) / gs; lane g < G takes
+        // the score of group g from lane (g * gs - 64 i), which is in slot i
+        const int per_slot = 64 / gs;      // groups per slot
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q >= per_slot) break;
+          const float v = read_lane(sc, q * gs);
+          if (lane == i * per_slot + q) gscore = v;
         }
       }
     } else {
@@ -101,11 +117,13 @@ __global__ __launch_bounds__(256) void route_kernel(
         gscore = gs == 1 ? m1 : m1 + m2;
       }
     }
-    // rank of each group (ties to the lower group), then the kept set
+    // rank of each group (ties to the lower group), then the kept set:
+    // lane g < G counts the groups that beat it
     int rank = 0;
+    const uint32_t mine = ordered_bits(gscore);
     for (int q = 0; q < G; ++q) {
-      const float o = read_lane(gscore, q);
-      rank += (o > gscore) || (o == gscore && q < lane);
+      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, q);
+      rank += (o > mine) || (o == mine && q < lane);
     }
     const uint64_t kept = wave_ballot(lane < G && rank < kg);
 #pragma unroll
@@ -114,26 +132,43 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
   if (!live) return;  // whole wave; no barrier follows
 
+  // Selection on 32-bit ordered keys (0 = taken or not allowed; every
+  // finite key maps above 0). Each step takes the wave max of the keys; the
+  // lowest lane holding it owns the winner unless another lane holds the
+  // same key, in which case the lowest expert index among them wins.
   int my_e = -1;
   float my_score = 0.0f;
-  uint64_t cand[VPL];
+  uint32_t ok_key[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) cand[i] = ok[i] ? candidate(key[i], lane + 64 * i) : 0ull;
+  for (int i = 0; i < VPL; ++i) ok_key[i] = ok[i] ? ordered_bits(key[i]) : 0u;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-    float best_score = 0.0f;
+    uint32_t best = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) best = max(best, ok_key[i]);
+    const uint32_t top = wave_max_u32(best);
+    // lowest slot of this lane holding the top key (VPL if none)
+    int slot = VPL;
+#pragma unroll
+    for (int i = VPL - 1; i >= 0; --i)
+      if (ok_key[i] == top) slot = i;
+    const uint64_t holders = wave_ballot(slot < VPL);
+    int e_win;
+    if ((holders & (holders - 1)) == 0) {          // one lane holds it
+      const int owner = (int)__builtin_ctzll(holders);
+      e_win = owner + 64 * __builtin_amdgcn_readlane(slot, owner);
+    } else {                                       // equal keys: lowest expert
+      const int e_mine = slot < VPL ? lane + 64 * slot : 0x7FFFFFFF;
+      e_win = (int)(0xFFFFFFFFu - wave_max_u32(0xFFFFFFFFu - (uint32_t)e_mine));
+    }
+    const int owner = e_win & 63, wslot = e_win >> 6;
+    float sel = score[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i)
+      if (i == wslot) sel = score[i];
+    const float s_win = read_lane(sel, owner);
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if (cand[i] > best) { best = cand[i]; best_score = score[i]; }
-    const uint64_t win = wave_max_u64(best);
-    const int e_win = (int)(0xFFFFFFFFu - (uint32_t)win);
-    const int owner = e_win & 63;
-    const float s_win = read_lane(best_score, owner);
-    if (lane == owner) {
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (lane + 64 * i == e_win) cand[i] = 0ull;
-    }
+      if (lane == owner && i == wslot) ok_key[i] = 0u;
     if (lane == j) { my_e = e_win; my_score = s_win; }
   }
 
@@ -227,7 +262,7 @@ __global__ __launch_bounds__(256) void route_team_kernel(
 
   if (SPG > 0) {
     // group g is slots [g*SPG, (g+1)*SPG) of every lane of the team
-    constexpr int NG = SPG > 0 ? VPL / SPG : 1;
+    constexpr int NG = VPL / (SPG > 0 ? SPG : 1);
     float gsc[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {

@@ -93,35 +93,42 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __longlong_as_double((long long)dpp_u64<CTRL>((uint64_t)__double_as_longlong(v)));
 }
 
-__device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int src) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
+// Value of lane (l ^ 16) and of lane (l ^ 32), with gfx950's row and half
+// swaps (checked on the device: permlane16_swap(v, v) returns v of the lane
+// itself and of the neighbouring row, in an order that depends on the row's
+// parity; permlane32_swap likewise for the two halves of the wave).
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane_id() & 16) ? r[0] : r[1];
 }
-__device__ __forceinline__ double read_lane_f64(double v, int src) {
-  return __longlong_as_double((long long)read_lane_u64((uint64_t)__double_as_longlong(v), src));
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane_id() & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float xor16_f32(float v) { return __uint_as_float(xor16_u32(__float_as_uint(v))); }
+__device__ __forceinline__ float xor32_f32(float v) { return __uint_as_float(xor32_u32(__float_as_uint(v))); }
+__device__ __forceinline__ uint64_t xor16_u64(uint64_t v) {
+  return ((uint64_t)xor16_u32((uint32_t)(v >> 32)) << 32) | xor16_u32((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t xor32_u64(uint64_t v) {
+  return ((uint64_t)xor32_u32((uint32_t)(v >> 32)) << 32) | xor32_u32((uint32_t)v);
+}
+__device__ __forceinline__ double xor16_f64(double v) {
+  return __longlong_as_double((long long)xor16_u64((uint64_t)__double_as_longlong(v)));
+}
+__device__ __forceinline__ double xor32_f64(double v) {
+  return __longlong_as_double((long long)xor32_u64((uint64_t)__double_as_longlong(v)));
 }
 
-// Wave-wide reductions: DPP inside each row, then the four row results are
-// read into scalars and combined there. The result is wave-uniform.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint64_t o;
-  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;
-  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;
-  o = dpp_u64<0x141>(v); v = o > v ? o : v;
-  o = dpp_u64<0x140>(v); v = o > v ? o : v;
-  const uint64_t r0 = read_lane_u64(v, 0), r1 = read_lane_u64(v, 16);
-  const uint64_t r2 = read_lane_u64(v, 32), r3 = read_lane_u64(v, 48);
-  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-  return a > b ? a : b;
-}
-
+// Wave-wide reductions, all in vector registers: four DPP steps inside each
+// 16-lane row, then the row and half swaps. Every lane gets the result.
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));
   v = fmaxf(v, dpp_f32<0x141>(v));
   v = fmaxf(v, dpp_f32<0x140>(v));
-  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
+  v = fmaxf(v, xor16_f32(v));
+  return fmaxf(v, xor32_f32(v));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -129,5 +136,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   v += dpp_f64<0x4E>(v);
   v += dpp_f64<0x141>(v);
   v += dpp_f64<0x140>(v);
-  return (read_lane_f64(v, 0) + read_lane_f64(v, 16)) + (read_lane_f64(v, 32) + read_lane_f64(v, 48));
+  v += xor16_f64(v);
+  return v + xor32_f64(v);
 }
