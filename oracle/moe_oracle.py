@@ -39,6 +39,8 @@ Readings where the pages are silent (each is also listed in the design notes):
   R6 FP8: OCP e4m3fn, 1x128 blocks along H, scale = amax/448 in fp32, codes
      by round-to-nearest-even of x*(448/amax) with saturation to +-448.
   R7 capacity: pairs beyond `cap` in an expert's stable order are dropped.
+  R18 MXFP8: 1x32 blocks, E8M0 scale 2^(floor(log2 amax) - 8), e4m3fn codes
+     of x / scale with round-to-nearest-even and saturation.
 """
 
 from __future__ import annotations
@@ -383,6 +385,67 @@ def dispatch_fp8(x_bits: np.ndarray, dst_row: np.ndarray, num_rows: int):
     out_s[d[live]] = scale[tok[live]]
     written[d[live]] = True
     return out, out_s, written
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 dispatch: 1x32 blocks with power-of-two (E8M0) scales
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E8M0_BIAS = 127
+E4M3_EMAX = 8          # exponent of e4m3fn's largest binade (448 = 1.75 * 2^8)
+
+
+def mxfp8_block_exponents(x_bits: np.ndarray) -> np.ndarray:
+    """Shared exponent of each 32-column block (DeepEP article, "Support FP8
+    et MXFP8", names MXFP8; its block and scale layout is read from the OCP
+    microscaling format, reading R18): e = floor(log2(max |x|)) - 8, clamped
+    to the E8M0 range [-127, 127]; an all-zero block takes -127."""
+    t, h = x_bits.shape
+    xf = bf16_to_f32(x_bits).reshape(t, h // MX_BLOCK, MX_BLOCK).astype(F64)
+    a = np.abs(xf).max(axis=2)
+    _, ex = np.frexp(a)                       # a = m * 2^ex, m in [0.5, 1)
+    e = (ex - 1) - E4M3_EMAX
+    e = np.where(a == 0, -E8M0_BIAS, e)
+    return np.clip(e, -E8M0_BIAS, E8M0_BIAS).astype(np.int64)
+
+
+def quantize_mxfp8_blocks(x_bits: np.ndarray):
+    """MXFP8 quantisation of bf16 rows: per 32-column block a power-of-two
+    scale 2^e (stored as the E8M0 byte e + 127) and e4m3fn codes of x / 2^e,
+    rounded to nearest even and saturated at +-448 (the division by a power
+    of two is exact). Returns codes [T, H] uint8, scale bytes [T, H/32]."""
+    t, h = x_bits.shape
+    e = mxfp8_block_exponents(x_bits)
+    xf = bf16_to_f32(x_bits).reshape(t, h // MX_BLOCK, MX_BLOCK).astype(F64)
+    scaled = np.ldexp(xf, -e[:, :, None])
+    codes = e4m3_encode(scaled.astype(F32)).reshape(t, h)
+    return codes, (e + E8M0_BIAS).astype(np.uint8)
+
+
+def dispatch_mxfp8(x_bits: np.ndarray, dst_row: np.ndarray, num_rows: int):
+    """MXFP8 dispatch: quantise each token once, copy codes and scale bytes
+    to every row of the token. Returns (codes, scale bytes, written)."""
+    t, h = x_bits.shape
+    codes, sbytes = quantize_mxfp8_blocks(x_bits)
+    out = np.zeros((num_rows, h), dtype=np.uint8)
+    out_s = np.zeros((num_rows, h // MX_BLOCK), dtype=np.uint8)
+    written = np.zeros(num_rows, dtype=bool)
+    d = dst_row.reshape(-1)
+    tok = np.repeat(np.arange(t), dst_row.shape[1])
+    live = d >= 0
+    out[d[live]] = codes[tok[live]]
+    out_s[d[live]] = sbytes[tok[live]]
+    written[d[live]] = True
+    return out, out_s, written
+
+
+def expert_dequant_mx(codes: np.ndarray, sbytes: np.ndarray) -> np.ndarray:
+    """y = bf16(decode(q) * 2^(s - 127)) for MXFP8 rows (exact product)."""
+    r, h = codes.shape
+    v = e4m3_decode(codes).reshape(r, h // MX_BLOCK, MX_BLOCK)
+    p = np.ldexp(v, sbytes.astype(np.int64)[:, :, None] - E8M0_BIAS)
+    return round_to_bf16(p.reshape(r, h))
 
 
 # ---------------------------------------------------------------------------
