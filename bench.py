@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--workload", default="dsv3",
                    choices=["dsv3", "mixtral", "qwen3_skew", "tiny", "decode"])
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--dispatch", default="auto", choices=["auto", "bf16", "fp8", "mxfp8"],
+                   help="dispatched format (auto: the workload's own)")
     p.add_argument("--cold-steps", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -60,15 +62,19 @@ def parse():
     return p.parse_args()
 
 
-def step_bytes(w, rows_live):
-    """Algorithmic bytes of one step, per phase (what the method must move)."""
+def step_bytes(w, rows_live, dtype=None):
+    """Algorithmic bytes of one step, per phase (what the method must move).
+    dtype: 0 bf16, 1 FP8 (fp32 scale per 128 columns), 2 MXFP8 (one byte per
+    32 columns); defaults to the workload's own."""
     T, H, E, k = w.tokens, w.hidden, w.experts, w.top_k
     rows = w.num_rows
-    fp8 = w.dispatch_dtype == 1
+    dtype = w.dispatch_dtype if dtype is None else dtype
     route = T * E * 4 + (E * 4 if w.bias != "none" else 0) + T * k * 8
     layout = T * k * 4 + T * k * 4 + rows * 4 + (3 * E + 3 * w.ranks + 3) * 4
-    if fp8:
+    if dtype == 1:
         dispatch = T * H * 2 + T * k * 4 + rows_live * H + rows_live * (H // 128) * 4
+    elif dtype == 2:
+        dispatch = T * H * 2 + T * k * 4 + rows_live * H + rows_live * (H // 32)
     else:
         dispatch = T * H * 2 + T * k * 4 + rows_live * H * 2
     combine = rows_live * H * 2 + T * k * 8 + T * H * 2
@@ -129,7 +135,7 @@ def copy_ceiling_gbps():
     return 2.0 * n * reps / (s.elapsed_time(e) * 1e-3) / 1e9
 
 
-def cpu_baseline(w, seed, budget_s):
+def cpu_baseline(w, seed, budget_s, dtype=None):
     """The CPU oracle (numpy, one thread) on a bounded sample of the same
     workload: the first `ts` tokens, the whole path per repeat."""
     import numpy as np
@@ -140,9 +146,13 @@ def cpu_baseline(w, seed, budget_s):
     inp = W.make_inputs(w, seed, tokens=ts)
     idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
     L = O.layout(idx, w.experts, w.ranks, w.capacity)
-    if w.dispatch_dtype == 1:
+    dtype = w.dispatch_dtype if dtype is None else dtype
+    if dtype == 1:
         codes, sc = O.quantize_fp8_blocks(inp.x)
         y_tok = O.expert_dequant(codes, sc)
+    elif dtype == 2:
+        codes, sc = O.quantize_mxfp8_blocks(inp.x)
+        y_tok = O.expert_dequant_mx(codes, sc)
     else:
         y_tok = inp.x
     y, _ = O.dispatch_bf16(y_tok, L["dst_row"], L["num_rows"])
@@ -151,8 +161,10 @@ def cpu_baseline(w, seed, budget_s):
     while True:
         idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
         L = O.layout(idx, w.experts, w.ranks, w.capacity)
-        if w.dispatch_dtype == 1:
+        if dtype == 1:
             O.dispatch_fp8(inp.x, L["dst_row"], L["num_rows"])
+        elif dtype == 2:
+            O.dispatch_mxfp8(inp.x, L["dst_row"], L["num_rows"])
         else:
             O.dispatch_bf16(inp.x, L["dst_row"], L["num_rows"])
         O.combine(y, L["dst_row"], wt)
@@ -188,7 +200,8 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    fp8 = w.dispatch_dtype == W.DTYPE_FP8_E4M3
+    dtype = {"auto": w.dispatch_dtype, "bf16": M.MOE_DTYPE_BF16, "fp8": M.MOE_DTYPE_FP8_E4M3,
+             "mxfp8": M.MOE_DTYPE_MXFP8_E4M3}[args.dispatch]
     steps, warm = args.steps, args.warmup
 
     # ---- inputs, resident in HBM before timing
@@ -202,7 +215,7 @@ def main():
             bias=torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None,
             x=torch.from_numpy(inp.x.view(np.int16)).to(dev)))
     buf = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
-                                  w.capacity, fp8, device=dev)
+                                  w.capacity, device=dev, dtype=dtype)
 
     def front(i):
         d = inputs[i % len(inputs)]
@@ -214,9 +227,13 @@ def main():
     front(0)
     torch.cuda.synchronize()
     rows = buf.num_rows
-    if fp8:
+    if dtype == M.MOE_DTYPE_FP8_E4M3:
         codes = buf.dispatched[:rows].view(torch.float8_e4m3fn).float()
         sc = buf.scales[:rows].repeat_interleave(128, dim=1)
+        y = (codes * sc).to(torch.bfloat16).view(torch.int16).contiguous()
+    elif dtype == M.MOE_DTYPE_MXFP8_E4M3:
+        codes = buf.dispatched[:rows].view(torch.float8_e4m3fn).float()
+        sc = torch.exp2(buf.scales[:rows].float() - 127.0).repeat_interleave(32, dim=1)
         y = (codes * sc).to(torch.bfloat16).view(torch.int16).contiguous()
     elif w.expert_kind == "scaled":
         off = buf.expert_offsets.cpu().numpy()
@@ -227,7 +244,7 @@ def main():
     else:
         y = buf.dispatched[:rows].clone()
     rows_live = int((buf.dst_row >= 0).sum().item())
-    nbytes = step_bytes(w, rows_live)
+    nbytes = step_bytes(w, rows_live, dtype)
     total_bytes = sum(nbytes.values())
 
     # ---- warmup
@@ -309,14 +326,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3+bf16",
+        "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
                    % (w.name, w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                       "group-limited sigmoid G=%d kg=%d" % (w.groups, w.topk_groups)
                       if w.groups > 1 else ("sigmoid" if w.score_fn else "softmax"),
                       ", zipf bias" if w.bias == "zipf" else "",
-                      "fp8 e4m3 (1x128 scales)" if fp8 else "bf16",
+                      {0: "bf16", 1: "fp8 e4m3 (1x128 fp32 scales)",
+                       2: "mxfp8 e4m3 (1x32 e8m0 scales)"}[dtype],
                       ", capacity %d" % w.capacity if w.capacity else ""),
                    "tokens": w.tokens, "hidden": w.hidden, "experts": w.experts,
                    "top_k": w.top_k, "ranks": w.ranks, "seed": args.seed},
@@ -332,7 +350,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds, dtype)
     print(json.dumps(out), flush=True)
 
 

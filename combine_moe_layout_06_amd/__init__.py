@@ -26,11 +26,13 @@ MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_FP8_E4M3 = 1
+MOE_DTYPE_MXFP8_E4M3 = 2
 
 MOE_MAX_EXPERTS = 512
 MOE_MAX_TOPK = 32
 MOE_MAX_GROUPS = 64
 MOE_FP8_BLOCK = 128
+MOE_MX_BLOCK = 32
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layout.so")
 

@@ -11,8 +11,9 @@ from __future__ import annotations
 import dataclasses
 from typing import Optional
 
-from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_FP8_BLOCK, moe_combine,
-               moe_dispatch, moe_layout, moe_layout_workspace_bytes, moe_route)
+from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_FP8_BLOCK,
+               MOE_MX_BLOCK, moe_combine, moe_dispatch, moe_layout,
+               moe_layout_workspace_bytes, moe_route)
 
 
 @dataclasses.dataclass
@@ -23,7 +24,7 @@ class LayerBuffers:
     top_k: int
     ranks: int
     capacity: int
-    fp8: bool
+    dtype: int                    # MOE_DTYPE_* of the dispatched rows
     topk_idx: object = None
     topk_weights: object = None
     expert_counts: object = None
@@ -37,8 +38,12 @@ class LayerBuffers:
     workspace: object = None
     workspace_bytes: int = 0
     dispatched: object = None     # [rows, H] bf16 (as int16) or uint8 codes
-    scales: object = None         # [rows, H/128] fp32 (FP8 only)
+    scales: object = None         # [rows, H/128] fp32 (FP8) or [rows, H/32] uint8 (MXFP8)
     combined: object = None       # [T, H] bf16 (as int16)
+
+    @property
+    def fp8(self) -> bool:
+        return self.dtype != MOE_DTYPE_BF16
 
     @property
     def num_rows(self) -> int:
@@ -48,10 +53,14 @@ class LayerBuffers:
 
     @classmethod
     def allocate(cls, tokens, hidden, experts, top_k, ranks, capacity=0, fp8=False,
-                 device="cuda", with_rank_tokens=True) -> "LayerBuffers":
+                 device="cuda", with_rank_tokens=True, dtype=None) -> "LayerBuffers":
+        """`dtype` (MOE_DTYPE_*) selects the dispatched format; `fp8=True` is
+        shorthand for MOE_DTYPE_FP8_E4M3."""
         import torch
         i32 = dict(dtype=torch.int32, device=device)
-        b = cls(tokens, hidden, experts, top_k, ranks, capacity, fp8)
+        if dtype is None:
+            dtype = MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_BF16
+        b = cls(tokens, hidden, experts, top_k, ranks, capacity, dtype)
         t, e, k, r = tokens, experts, top_k, ranks
         b.topk_idx = torch.empty((t, k), **i32)
         b.topk_weights = torch.empty((t, k), dtype=torch.float32, device=device)
@@ -66,9 +75,13 @@ class LayerBuffers:
         b.workspace_bytes = moe_layout_workspace_bytes(t, e, k)
         b.workspace = torch.empty(max(b.workspace_bytes, 4), dtype=torch.uint8, device=device)
         rows = max(b.num_rows, 1)
-        if fp8:
+        if dtype == MOE_DTYPE_FP8_E4M3:
             b.dispatched = torch.empty((rows, hidden), dtype=torch.uint8, device=device)
             b.scales = torch.empty((rows, hidden // MOE_FP8_BLOCK), dtype=torch.float32,
+                                   device=device)
+        elif dtype == MOE_DTYPE_MXFP8_E4M3:
+            b.dispatched = torch.empty((rows, hidden), dtype=torch.uint8, device=device)
+            b.scales = torch.empty((rows, hidden // MOE_MX_BLOCK), dtype=torch.uint8,
                                    device=device)
         else:
             b.dispatched = torch.empty((rows, hidden), dtype=torch.int16, device=device)
@@ -87,8 +100,7 @@ class LayerBuffers:
 
     def dispatch(self, x, stream=None):
         moe_dispatch(self.tokens, self.hidden, self.top_k, self.num_rows, x, self.dst_row,
-                     MOE_DTYPE_FP8_E4M3 if self.fp8 else MOE_DTYPE_BF16, self.dispatched,
-                     self.scales if self.fp8 else None, stream)
+                     self.dtype, self.dispatched, self.scales, stream)
 
     def combine(self, expert_out, stream=None):
         moe_combine(self.tokens, self.hidden, self.top_k, self.num_rows, expert_out,

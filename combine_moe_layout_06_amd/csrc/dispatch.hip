@@ -220,6 +220,87 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(
   }
 }
 
+
+// MXFP8: one wave per (token, part); a step covers 512 columns = 16 blocks
+// of 32 columns, 4 lanes per block. The shared exponent comes from the
+// block amax (two DPP steps inside each quad); codes use the hardware
+// pack-convert of x * 2^-e clamped to +-448 (the multiplication by a power
+// of two is exact).
+constexpr int kMxStepBlocks = 16;
+
+__global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(
+    int T, int k, int H, int parts, int bpp, int num_rows,
+    const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
+    uint8_t* __restrict__ out, uint8_t* __restrict__ out_scales) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= T * parts) return;
+  const int t = gw / parts;
+  const int nb = H / MOE_MX_BLOCK;
+  const int nch = H / 8;
+  const int b0 = (gw - t * parts) * bpp;
+  const int nbp = min(bpp, nb - b0);
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const int blk = lane >> 2;         // block inside the step
+  const int sub = lane & 3;          // 16-byte chunk inside the block
+  const u32x4* src = x + (size_t)t * nch;
+
+  uint32_t sreg[kScaleSlots];        // E8M0 byte of part-local block (s*64 + lane)
+#pragma unroll
+  for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0u;
+
+  for (int st = 0; st * kMxStepBlocks < nbp; ++st) {
+    const int bl = st * kMxStepBlocks + blk;
+    const bool act = bl < nbp;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (act) v = stream_load(src + (b0 + bl) * 4 + sub);
+
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = v[q] & 0x7FFF7FFFu;
+      m = max(m, max(w & 0xFFFFu, w >> 16));
+    }
+    m = max(m, dpp_u32<0xB1>(m));
+    m = max(m, dpp_u32<0x4E>(m));
+    const float amax = __uint_as_float(m << 16);
+    int e = amax == 0.0f ? -127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+    e = min(max(e, -127), 127);
+    const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
+    u32x2 q;
+    q[0] = quant_pair_hw(v[0], inv) | (quant_pair_hw(v[1], inv) << 16);
+    q[1] = quant_pair_hw(v[2], inv) | (quant_pair_hw(v[3], inv) << 16);
+
+    // lane L keeps the byte of part-local block L + 64*slot: in step st the
+    // lanes of row (st % 4) receive block (st*16 + L % 16) from its first lane
+    const uint32_t sb = (uint32_t)(e + 127);
+    const uint32_t got = (uint32_t)__shfl((int)sb, 4 * (lane & 15));
+#pragma unroll
+    for (int s = 0; s < kScaleSlots; ++s)
+      if (st / 4 == s && (lane >> 4) == (st & 3)) sreg[s] = got;
+
+    if (act) {
+      for (int j = 0; j < k; ++j) {
+        const int d = read_lane(my_dst, j);
+        if (d < 0 || d >= num_rows) continue;
+        u32x2* dst = reinterpret_cast<u32x2*>(out + (size_t)d * H + (size_t)(b0 + bl) * MOE_MX_BLOCK) + sub;
+        stream_store(q, dst);
+      }
+    }
+  }
+
+  for (int j = 0; j < k; ++j) {
+    const int d = read_lane(my_dst, j);
+    if (d < 0 || d >= num_rows) continue;
+    uint8_t* srow = out_scales + (size_t)d * nb + b0;
+#pragma unroll
+    for (int s = 0; s < kScaleSlots; ++s) {
+      const int b = s * 64 + lane;
+      if (b < nbp) srow[b] = (uint8_t)sreg[s];
+    }
+  }
+}
+
 // Split a row of `units` into parts so that the launch has about
 // kTargetWaves waves, each part a multiple of `align` units (but at least
 // `min_units` and at most `max_units` units).
@@ -234,6 +315,21 @@ void split_row(int T, int units, int align, int max_units, int* parts, int* per_
 }
 
 }  // namespace
+
+hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* x,
+                                 const int32_t* dst_row, void* out, uint8_t* out_scales,
+                                 hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int nb = H / MOE_MX_BLOCK;
+  int parts, bpp;
+  split_row(T, nb, kMxStepBlocks, 64 * kScaleSlots, &parts, &bpp);
+  const int waves = T * parts;
+  hipLaunchKernelGGL(dispatch_mxfp8_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(256), 0, stream, T, k, H, parts, bpp, num_rows,
+                     static_cast<const u32x4*>(x), dst_row, static_cast<uint8_t*>(out),
+                     out_scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch_bf16(int T, int H, int k, int num_rows, const void* x,
                                 const int32_t* dst_row, void* out, hipStream_t stream) {

@@ -33,6 +33,10 @@ hipError_t launch_dispatch_fp8(int T, int H, int k, int num_rows, const void* x,
                                const int32_t* dst_row, void* out, float* out_scales,
                                hipStream_t stream);
 
+hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* x,
+                                 const int32_t* dst_row, void* out, uint8_t* out_scales,
+                                 hipStream_t stream);
+
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
                           hipStream_t stream);

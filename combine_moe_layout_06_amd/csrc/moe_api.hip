@@ -148,31 +148,42 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int ca
 }
 
 int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows, const void* x_bf16,
-                 const int32_t* dst_row, int out_dtype, void* out, float* out_scales,
+                 const int32_t* dst_row, int out_dtype, void* out, void* out_scales,
                  void* stream) {
   const char* fn = "moe_dispatch";
   int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
   if (st != MOE_OK) return st;
-  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3)
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3 &&
+      out_dtype != MOE_DTYPE_MXFP8_E4M3)
     return fail(MOE_ERR_INVALID, "%s: out_dtype=%d", fn, out_dtype);
   const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool mx = out_dtype == MOE_DTYPE_MXFP8_E4M3;
   if (fp8 && hidden % MOE_FP8_BLOCK != 0)
     return fail(MOE_ERR_INVALID, "%s: FP8 needs hidden %% %d == 0 (hidden=%d)", fn,
                 MOE_FP8_BLOCK, hidden);
+  if (mx && hidden % MOE_MX_BLOCK != 0)
+    return fail(MOE_ERR_INVALID, "%s: MXFP8 needs hidden %% %d == 0 (hidden=%d)", fn,
+                MOE_MX_BLOCK, hidden);
   if (num_tokens > 0 && (!x_bf16 || !dst_row))
     return fail(MOE_ERR_INVALID, "%s: NULL x/dst_row", fn);
   if (num_rows > 0 && !out) return fail(MOE_ERR_INVALID, "%s: NULL out", fn);
-  if (fp8 && num_rows > 0 && !out_scales) return fail(MOE_ERR_INVALID, "%s: NULL out_scales", fn);
-  if (!fp8 && out_scales) return fail(MOE_ERR_INVALID, "%s: out_scales is for FP8 only", fn);
+  if ((fp8 || mx) && num_rows > 0 && !out_scales)
+    return fail(MOE_ERR_INVALID, "%s: NULL out_scales", fn);
+  if (!fp8 && !mx && out_scales) return fail(MOE_ERR_INVALID, "%s: out_scales is for FP8 only", fn);
   if (!aligned(x_bf16, 16) || !aligned(out, 16))
     return fail(MOE_ERR_INVALID, "%s: x and out must be 16-byte aligned", fn);
-  if (!aligned(dst_row, 4) || !aligned(out_scales, 4))
+  if (!aligned(dst_row, 4) || (fp8 && !aligned(out_scales, 4)))
     return fail(MOE_ERR_INVALID, "%s: dst_row/out_scales must be 4-byte aligned", fn);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err =
-      fp8 ? moe::launch_dispatch_fp8(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out,
-                                     out_scales, s)
-          : moe::launch_dispatch_bf16(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out, s);
+  hipError_t err;
+  if (fp8)
+    err = moe::launch_dispatch_fp8(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out,
+                                   static_cast<float*>(out_scales), s);
+  else if (mx)
+    err = moe::launch_dispatch_mxfp8(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out,
+                                     static_cast<uint8_t*>(out_scales), s);
+  else
+    err = moe::launch_dispatch_bf16(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out, s);
   return from_hip(err, fn);
 }
 

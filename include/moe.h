@@ -59,12 +59,13 @@ typedef enum {
 } moe_status;
 
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
-enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3 = 1 };
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3 = 1, MOE_DTYPE_MXFP8_E4M3 = 2 };
 
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 64
 #define MOE_FP8_BLOCK 128
+#define MOE_MX_BLOCK 32
 
 /* Name of a status code ("MOE_OK", ...). Never NULL. */
 const char* moe_status_string(int status);
@@ -168,16 +169,25 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
  *     +-448; an input of +-0 gives the code of +-0.
  *   out holds the 1-byte OCP e4m3fn codes [num_rows, hidden];
  *   out_scales[row, b] = scale, fp32 [num_rows, hidden/128].
+ * MOE_DTYPE_MXFP8_E4M3: microscaled FP8 (the DeepEP article's "Support FP8
+ *   et MXFP8" names MXFP8; block and scale layout follow the OCP
+ *   microscaling format). Per 32-column block b:
+ *     e = floor(log2(max |x|)) - 8 clamped to [-127, 127] (-127 if all 0),
+ *     q = e4m3fn(x / 2^e) rounded to nearest even, saturating at +-448.
+ *   out holds the codes [num_rows, hidden]; out_scales holds the E8M0
+ *   bytes e + 127, uint8 [num_rows, hidden/32].
  *
  *   x          [num_tokens, hidden] bf16
  *   dst_row    [num_tokens, top_k] int32 from moe_layout (-1 = no row)
  *   num_rows   rows of `out` (T*k packed, E*capacity padded)
+ *   out_scales fp32 (FP8), uint8 (MXFP8) or NULL (bf16)
  * Rows that receive no pair are left untouched.
- * Requires hidden % 8 == 0 (16-byte rows); FP8 also hidden % 128 == 0.
+ * Requires hidden % 8 == 0 (16-byte rows); FP8 also hidden % 128 == 0,
+ * MXFP8 hidden % 32 == 0.
  */
 int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows,
                  const void* x_bf16, const int32_t* dst_row, int out_dtype,
-                 void* out, float* out_scales, void* stream);
+                 void* out, void* out_scales, void* stream);
 
 /*
  * moe_combine -- bring each token's k expert outputs back and sum them

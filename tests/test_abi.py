@@ -129,6 +129,8 @@ def _dispatch(**kw):
     (dict(dt=1, sc=None), M.MOE_ERR_INVALID),
     (dict(dt=0, sc=A16), M.MOE_ERR_INVALID),
     (dict(dt=7), M.MOE_ERR_INVALID),
+    (dict(H=264, dt=2, sc=A16), M.MOE_ERR_INVALID),        # MXFP8 needs H % 32
+    (dict(dt=2, sc=None), M.MOE_ERR_INVALID),
     (dict(x=A16 + 8), M.MOE_ERR_INVALID),
     (dict(out=A16b + 4), M.MOE_ERR_INVALID),
     (dict(rows=-1), M.MOE_ERR_INVALID),

@@ -117,7 +117,7 @@ def test_route_parity(case):
 def gpu_layout(idx, E, R, cap, with_rtc=True):
     t, k = idx.shape
     rows = E * cap if cap else t * k
-    b = LayerBuffers(t, 8, E, k, R, cap, False)
+    b = LayerBuffers(t, 8, E, k, R, cap, M.MOE_DTYPE_BF16)
     b.expert_counts = poison_like(E, torch.int32)
     b.expert_offsets = poison_like(E + 1, torch.int32)
     b.rank_counts = poison_like(R, torch.int32)
@@ -451,3 +451,87 @@ def test_layer_is_deterministic():
     for name in ("topk_idx", "topk_weights", "dst_row", "src_pair", "expert_counts",
                  "rank_token_counts", "dispatched", "scales"):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def gpu_dispatch_mx(x, dst, num_rows):
+    assert x.dtype == np.uint16 and dst.dtype == np.int32
+    t, h = x.shape
+    k = dst.shape[1]
+    out_full = poison_like((num_rows + GUARD, h), torch.uint8)
+    sc_full = poison_like((num_rows + GUARD, h // 32), torch.uint8)
+    M.moe_dispatch(t, h, k, num_rows, dev(x) if t else None, dev(dst) if t else None,
+                   M.MOE_DTYPE_MXFP8_E4M3, out_full, sc_full, None)
+    out, sc = host(out_full), host(sc_full)
+    assert np.all(out[num_rows:] == 0xFF) and np.all(sc[num_rows:] == 0xFF), "stray write"
+    return out[:num_rows], sc[:num_rows]
+
+
+MX_CASES = [
+    # T, H, k, E, cap
+    (257, 7168, 8, 256, 0),
+    (100, 96, 2, 8, 0),              # 3 blocks: partial 16-block step
+    (33, 1056, 5, 12, 3),            # capacity with drops; 33 blocks
+    (40, 33280, 2, 4, 0),            # 1040 blocks: several parts per row
+    (1500, 4096, 2, 8, 0),
+    (0, 256, 2, 8, 0),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "T%d_H%d_k%d_E%d_cap%d" % c)
+def test_dispatch_mxfp8_parity(case):
+    t, h, k, e, cap = case
+    say("mxfp8 dispatch case", case)
+    g = np.random.Generator(np.random.PCG64(t + 3 * h + k))
+    x = W.random_bf16_rows(g, t, h)
+    idx = W.random_topk_idx(g, t, e, k, mask_frac=0.05)
+    L = O.layout(idx, e, 1, cap)
+    rows = L["num_rows"]
+    out, sc = gpu_dispatch_mx(x, L["dst_row"], rows)
+    q, s, written = O.dispatch_mxfp8(x, L["dst_row"], rows)
+    assert np.array_equal(out[written], q[written])
+    assert np.array_equal(sc[written], s[written])
+    assert np.all(out[~written] == 0xFF) and np.all(sc[~written] == 0xFF)
+
+
+def test_mxfp8_every_bf16_pattern():
+    """All finite bf16 patterns, each block led by an extreme element, so
+    every pattern is quantised under several shared exponents."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[np.isfinite(O.bf16_to_f32(bits))]
+    rows = []
+    for big in (0x43E0, 0x43FF, 0x3F80, 0x7F7F, 0x0080, 0x0001, 0x0000):
+        v = np.concatenate([bits, np.zeros((-len(bits)) % 31, np.uint16)]).reshape(-1, 31)
+        rows.append(np.concatenate([np.full((len(v), 1), big, np.uint16), v], axis=1).reshape(-1))
+    x = np.concatenate(rows)
+    x = np.concatenate([x, np.zeros((-len(x)) % 1024, np.uint16)]).reshape(-1, 1024)
+    t = x.shape[0]
+    out, sc = gpu_dispatch_mx(x, np.arange(t, dtype=np.int32).reshape(t, 1), t)
+    q, s = O.quantize_mxfp8_blocks(x)
+    assert np.array_equal(out, q) and np.array_equal(sc, s)
+
+
+def test_mxfp8_layer_end_to_end():
+    """DeepSeek-V3 shape with MXFP8 dispatch: route -> layout -> dispatch on
+    the GPU, stand-in expert dequantises, combine against the oracle."""
+    w = W.WORKLOADS["dsv3"]
+    inp = W.make_inputs(w, 5)
+    t = inp.x.shape[0]
+    b = LayerBuffers.allocate(t, w.hidden, w.experts, w.top_k, w.ranks, 0,
+                              dtype=M.MOE_DTYPE_MXFP8_E4M3)
+    M.run_layer(b, dev(inp.logits), dev(inp.bias), dev(inp.x), w.score_fn, w.groups,
+                w.topk_groups)
+    torch.cuda.synchronize()
+    idx_g, w_g = host(b.topk_idx), host(b.topk_weights)
+    L = O.layout(idx_g, w.experts, w.ranks, 0)
+    rows = L["num_rows"]
+    q, s, written = O.dispatch_mxfp8(inp.x, L["dst_row"], rows)
+    assert np.array_equal(host(b.dispatched)[:rows], q)
+    assert np.array_equal(host(b.scales)[:rows], s)
+    codes, sb = O.quantize_mxfp8_blocks(inp.x)
+    y, _ = O.dispatch_bf16(O.expert_dequant_mx(codes, sb), L["dst_row"], rows)
+    b.combine(dev(y))
+    got = host(b.combined, np.uint16)[:t]
+    want, mag = O.combine(y, L["dst_row"], w_g)
+    say("  mxfp8 combine bit-exact fraction %.6f" % assert_combine_close(got, want, mag, w.top_k))
