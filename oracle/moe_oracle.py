@@ -476,6 +476,50 @@ def combine(y_bits: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray):
 
 
 # ---------------------------------------------------------------------------
+# Backward of dispatch and combine (the pages note that the exchanges run in
+# both the forward and the backward pass: DeepEP article, "Qu'est-ce que
+# l'Expert Parallelism", and its fine-tuning use case)
+# ---------------------------------------------------------------------------
+
+def dispatch_backward(grad_rows_bits: np.ndarray, dst_row: np.ndarray):
+    """Gradient of dispatch with respect to x: each token collects the
+    gradients of its rows, dx[t] = bf16( sum_j g[dst_row[t, j]] ) (the
+    adjoint of copying x[t] to k rows). It is combine with unit weights.
+    Returns (dx bits [T, H], abs_sum [T, H])."""
+    t, k = dst_row.shape
+    return combine(grad_rows_bits, dst_row, np.ones((t, k), dtype=F32))
+
+
+def combine_backward(grad_out_bits: np.ndarray, y_bits: np.ndarray,
+                     dst_row: np.ndarray, topk_w: np.ndarray, num_rows: int):
+    """Gradients of out[t] = sum_j w[t, j] * y[dst_row[t, j]]:
+        dy[dst_row[t, j]] = bf16( w[t, j] * dout[t] )
+        dw[t, j]          = fp32( sum_h dout[t, h] * y[dst_row[t, j], h] )
+    both exact in fp64 before the final rounding. Dropped pairs (row -1)
+    give dw = 0 and write no row.
+    Returns (dy bits [rows, H], written, dw [T, k] fp32, dw_abs [T, k] fp64 =
+    sum_h |dout * y|)."""
+    t, k = dst_row.shape
+    h = grad_out_bits.shape[1]
+    g = bf16_to_f32(grad_out_bits).astype(F64)
+    dy = np.zeros((num_rows, h), dtype=np.uint16)
+    written = np.zeros(num_rows, dtype=bool)
+    dw = np.zeros((t, k), dtype=F64)
+    dw_abs = np.zeros((t, k), dtype=F64)
+    for j in range(k):
+        d = dst_row[:, j]
+        live = d >= 0
+        rows = d[live]
+        yj = bf16_to_f32(y_bits[rows]).astype(F64)
+        prod = g[live] * yj
+        dw[live, j] = prod.sum(axis=1)
+        dw_abs[live, j] = np.abs(prod).sum(axis=1)
+        dy[rows] = round_to_bf16(topk_w[live, j].astype(F64)[:, None] * g[live])
+        written[rows] = True
+    return dy, written, dw.astype(F32), dw_abs
+
+
+# ---------------------------------------------------------------------------
 # Stand-in experts used between dispatch and combine (harness, not the method)
 # ---------------------------------------------------------------------------
 
