@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--cold-steps", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--pass", dest="pass_", default="forward", choices=["forward", "backward"],
+                   help="backward: time combine-backward then dispatch-backward instead")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -79,6 +81,83 @@ def step_bytes(w, rows_live, dtype=None):
         dispatch = T * H * 2 + T * k * 4 + rows_live * H * 2
     combine = rows_live * H * 2 + T * k * 8 + T * H * 2
     return dict(route=route, layout=layout, dispatch=dispatch, combine=combine)
+
+
+def backward_bytes(w, rows_live):
+    """Algorithmic bytes of the backward pair: combine-backward reads dout,
+    the expert rows, dst_row and weights and writes the row gradients and
+    the weight gradients; dispatch-backward reads the row gradients and
+    dst_row and writes dx."""
+    T, H, k = w.tokens, w.hidden, w.top_k
+    combine_bwd = T * H * 2 + rows_live * H * 2 + T * k * 8 + rows_live * H * 2 + T * k * 4
+    dispatch_bwd = rows_live * H * 2 + T * k * 4 + T * H * 2
+    return dict(combine_backward=combine_bwd, dispatch_backward=dispatch_bwd)
+
+
+def run_backward(args, w, M, W, torch, np):
+    """Backward pair on the layout of one forward pass: combine-backward
+    (dout, expert rows -> row gradients, weight gradients), then
+    dispatch-backward (row gradients -> dx)."""
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w, args.seed)
+    buf = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                  device=dev)
+    bias = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+    buf.route(torch.from_numpy(inp.logits).to(dev), bias, w.score_fn, w.groups, w.topk_groups)
+    buf.layout()
+    rows = buf.num_rows
+    g = W.rng(args.seed + 1)
+    y = torch.from_numpy(W.random_bf16_rows(g, rows, w.hidden).view(np.int16)).to(dev)
+    dout = torch.from_numpy(W.random_bf16_rows(g, w.tokens, w.hidden).view(np.int16)).to(dev)
+    dy = torch.empty_like(y)
+    dw = torch.empty((w.tokens, w.top_k), dtype=torch.float32, device=dev)
+    dx = torch.empty((w.tokens, w.hidden), dtype=torch.int16, device=dev)
+    T, H, k = w.tokens, w.hidden, w.top_k
+
+    def step():
+        M.moe_combine_backward(T, H, k, rows, dout, y, buf.dst_row, buf.topk_weights, dy, dw)
+        M.moe_dispatch_backward(T, H, k, rows, dy, buf.dst_row, dx)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        M.moe_combine_backward(T, H, k, rows, dout, y, buf.dst_row, buf.topk_weights, dy, dw)
+        e[1].record()
+        M.moe_dispatch_backward(T, H, k, rows, dy, buf.dst_row, dx)
+        e[2].record()
+    torch.cuda.synchronize()
+    cb = sum(e[0].elapsed_time(e[1]) for e in ev) / len(ev) * 1e-3
+    db = sum(e[1].elapsed_time(e[2]) for e in ev) / len(ev) * 1e-3
+    rows_live = int((buf.dst_row >= 0).sum().item())
+    nb = backward_bytes(w, rows_live)
+    ms = wall * 1e3 / args.steps
+    total = sum(nb.values())
+    achieved = nb["combine_backward"] / cb / 1e9
+    print(json.dumps({
+        "metric": "backward dispatch+combine tokens/s and HBM GB/s, %s shape, 1 GPU" % w.name,
+        "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s backward: T=%d H=%d E=%d k=%d, bf16 gradients"
+                   % (w.name, T, H, w.experts, k), "tokens": T, "hidden": H, "top_k": k},
+        "gbps": round(total / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total, "phase_bytes": nb,
+        "phases_us": {"combine_backward": round(cb * 1e6, 2), "dispatch_backward": round(db * 1e6, 2)},
+        "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nb["combine_backward"]},
+        "cpu_baseline": None}), flush=True)
 
 
 def sha_of(paths):
@@ -200,6 +279,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.pass_ == "backward":
+        run_backward(args, w, M, W, torch, np)
+        return
     dtype = {"auto": w.dispatch_dtype, "bf16": M.MOE_DTYPE_BF16, "fp8": M.MOE_DTYPE_FP8_E4M3,
              "mxfp8": M.MOE_DTYPE_MXFP8_E4M3}[args.dispatch]
     steps, warm = args.steps, args.warmup

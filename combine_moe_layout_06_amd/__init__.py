@@ -37,7 +37,8 @@ MOE_MX_BLOCK = 32
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layout.so")
 
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
-            "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch", "moe_combine")
+            "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch", "moe_combine",
+            "moe_dispatch_backward", "moe_combine_backward")
 
 _lib = None
 
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
     L.moe_dispatch.restype = i32
     L.moe_combine.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.moe_combine.restype = i32
+    L.moe_dispatch_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    L.moe_dispatch_backward.restype = i32
+    L.moe_combine_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_combine_backward.restype = i32
     _lib = L
     return L
 
@@ -152,6 +157,22 @@ def moe_combine(num_tokens, hidden, top_k, num_rows, expert_out_bf16, dst_row,
     _check(lib().moe_combine(num_tokens, hidden, top_k, num_rows, _ptr(expert_out_bf16),
                              _ptr(dst_row), _ptr(topk_weights), _ptr(out_bf16),
                              _stream(stream)))
+
+
+def moe_dispatch_backward(num_tokens, hidden, top_k, num_rows, grad_rows_bf16, dst_row,
+                          grad_x_bf16, stream=None) -> None:
+    _check(lib().moe_dispatch_backward(num_tokens, hidden, top_k, num_rows,
+                                       _ptr(grad_rows_bf16), _ptr(dst_row), _ptr(grad_x_bf16),
+                                       _stream(stream)))
+
+
+def moe_combine_backward(num_tokens, hidden, top_k, num_rows, grad_out_bf16, expert_out_bf16,
+                         dst_row, topk_weights, grad_expert_out_bf16, grad_weights,
+                         stream=None) -> None:
+    _check(lib().moe_combine_backward(num_tokens, hidden, top_k, num_rows, _ptr(grad_out_bf16),
+                                      _ptr(expert_out_bf16), _ptr(dst_row), _ptr(topk_weights),
+                                      _ptr(grad_expert_out_bf16), _ptr(grad_weights),
+                                      _stream(stream)))
 
 
 from .buffers import LayerBuffers, run_layer  # noqa: E402,F401

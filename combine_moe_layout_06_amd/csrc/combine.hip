@@ -8,6 +8,9 @@
 //
 //   out[t, :] = bf16( fma chain over j = 0..k-1 of w[t,j] * y[dst_row[t,j], :] )
 //
+// With no weights (w == nullptr) every weight is 1: that is the gradient of
+// dispatch with respect to x (each token sums the gradients of its rows).
+//
 // One 64-lane wave per (token, column part). For a compile-time k the wave
 // issues the loads of all k rows (16 bytes per lane each) before the first
 // FMA, so k x 1 KiB per wave are in flight; the fp32 accumulators are
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int c0 = (gw - t * parts) * cpp;
   const int cnt = min(cpp, nch - c0);
   const int my_dst = lane < K ? dst_row[(size_t)t * K + lane] : -1;
-  const float my_w = lane < K ? w[(size_t)t * K + lane] : 0.0f;
+  const float my_w = lane < K ? (w != nullptr ? w[(size_t)t * K + lane] : 1.0f) : 0.0f;
 
   int d[K];
   float wj[K];
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
   const int c0 = (gw - t * parts) * cpp;
   const int cnt = min(cpp, nch - c0);
   const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
+  const float my_w = lane < k ? (w != nullptr ? w[(size_t)t * k + lane] : 1.0f) : 0.0f;
   u32x4* dst = out + (size_t)t * nch + c0;
 
   for (int base = 0; base < cnt; base += MOE_WAVE * U) {
@@ -144,6 +147,90 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward of combine: for each live pair (t, j) with row d = dst_row[t, j]
+//   dy[d, :] = bf16( w[t, j] * dout[t, :] )
+//   dw[t, j] = sum_h dout[t, h] * y[d, h]        (fp32)
+// One 256-thread block per token; wave v covers chunk groups v, v + 4, ...
+// of the row (kBwdChunks 16-byte chunks per lane per group). Its dout chunks
+// stay in registers while it walks the k rows; each pair's dot product is
+// reduced in the wave and the four waves' partial sums are added in wave
+// order, so the result is deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kBwdChunks = 4;
+
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = __builtin_fmaf(bf16_lo(a[q]), bf16_lo(b[q]), acc);
+    acc = __builtin_fmaf(bf16_hi(a[q]), bf16_hi(b[q]), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ u32x4 scale_row(const u32x4& g, float w) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r[q] = bf16_rne(w * bf16_lo(g[q])) | (bf16_rne(w * bf16_hi(g[q])) << 16);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    int T, int k, int nch, int num_rows, const u32x4* __restrict__ dout,
+    const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
+    const float* __restrict__ w, u32x4* __restrict__ dy, float* __restrict__ dw) {
+  __shared__ float s_part[kWavesPerBlock][MOE_MAX_TOPK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
+  if (lane < k) s_part[wave][lane] = 0.0f;
+  const u32x4* g_row = dout + (size_t)t * nch;
+  constexpr int kGroup = MOE_WAVE * kBwdChunks;
+
+  for (int c0 = wave * kGroup; c0 < nch; c0 += kWavesPerBlock * kGroup) {
+    u32x4 g[kBwdChunks];
+#pragma unroll
+    for (int u = 0; u < kBwdChunks; ++u) {
+      const int c = c0 + u * MOE_WAVE + lane;
+      g[u] = u32x4{0u, 0u, 0u, 0u};
+      if (c < nch) g[u] = stream_load(g_row + c);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int d = read_lane(my_dst, j);
+      if (d < 0 || d >= num_rows) continue;
+      const float wj = read_lane(my_w, j);
+      const u32x4* y_row = y + (size_t)d * nch;
+      u32x4* dy_row = dy + (size_t)d * nch;
+      u32x4 v[kBwdChunks];
+#pragma unroll
+      for (int u = 0; u < kBwdChunks; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nch) v[u] = stream_load(y_row + c);
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kBwdChunks; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        part = dot8(g[u], v[u], part);
+        if (c < nch) stream_store(scale_row(g[u], wj), dy_row + c);
+      }
+      const float sum = wave_sum_f32(part);
+      if (lane == 0) s_part[wave][j] += sum;
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < k) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kWavesPerBlock; ++v) acc += s_part[v][lane];
+    dw[(size_t)t * k + lane] = (my_dst >= 0 && my_dst < num_rows) ? acc : 0.0f;
+  }
+}
+
 template <int K, int U>
 void launch_fixed(dim3 grid, hipStream_t stream, int T, int nch, int parts, int cpp,
                   int num_rows, const void* y, const int32_t* dst_row, const float* w,
@@ -154,6 +241,16 @@ void launch_fixed(dim3 grid, hipStream_t stream, int T, int nch, int parts, int 
 }
 
 }  // namespace
+
+hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void* dout,
+                                   const void* y, const int32_t* dst_row, const float* w,
+                                   void* dy, float* dw, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_backward_kernel, dim3(T), dim3(256), 0, stream, T, k, H / 8,
+                     num_rows, static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y),
+                     dst_row, w, static_cast<u32x4*>(dy), dw);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,

@@ -37,9 +37,14 @@ hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* 
                                  const int32_t* dst_row, void* out, uint8_t* out_scales,
                                  hipStream_t stream);
 
+// w == nullptr means unit weights (the gradient of dispatch).
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
                           hipStream_t stream);
+
+hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void* dout,
+                                   const void* y, const int32_t* dst_row, const float* w,
+                                   void* dy, float* dw, hipStream_t stream);
 
 // Number of waves a row-parallel kernel aims for: about four times the
 // 256 CUs x 32 wave slots, so that short waves keep every CU busy to the end.

@@ -206,4 +206,45 @@ int moe_combine(int num_tokens, int hidden, int top_k, int num_rows, const void*
                   fn);
 }
 
+int moe_dispatch_backward(int num_tokens, int hidden, int top_k, int num_rows,
+                          const void* grad_rows_bf16, const int32_t* dst_row,
+                          void* grad_x_bf16, void* stream) {
+  const char* fn = "moe_dispatch_backward";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
+  if (st != MOE_OK) return st;
+  if (num_tokens > 0 && (!dst_row || !grad_x_bf16))
+    return fail(MOE_ERR_INVALID, "%s: NULL dst_row/grad_x", fn);
+  if (num_rows > 0 && !grad_rows_bf16) return fail(MOE_ERR_INVALID, "%s: NULL grad_rows", fn);
+  if (!aligned(grad_rows_bf16, 16) || !aligned(grad_x_bf16, 16))
+    return fail(MOE_ERR_INVALID, "%s: grad_rows and grad_x must be 16-byte aligned", fn);
+  if (!aligned(dst_row, 4)) return fail(MOE_ERR_INVALID, "%s: dst_row must be 4-byte aligned", fn);
+  return from_hip(moe::launch_combine(num_tokens, hidden, top_k, num_rows, grad_rows_bf16,
+                                      dst_row, nullptr, grad_x_bf16,
+                                      static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_combine_backward(int num_tokens, int hidden, int top_k, int num_rows,
+                         const void* grad_out_bf16, const void* expert_out_bf16,
+                         const int32_t* dst_row, const float* topk_weights,
+                         void* grad_expert_out_bf16, float* grad_weights, void* stream) {
+  const char* fn = "moe_combine_backward";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
+  if (st != MOE_OK) return st;
+  if (num_tokens > 0 && (!grad_out_bf16 || !dst_row || !topk_weights || !grad_weights))
+    return fail(MOE_ERR_INVALID, "%s: NULL grad_out/dst_row/topk_weights/grad_weights", fn);
+  if (num_rows > 0 && (!expert_out_bf16 || !grad_expert_out_bf16))
+    return fail(MOE_ERR_INVALID, "%s: NULL expert_out/grad_expert_out", fn);
+  if (!aligned(grad_out_bf16, 16) || !aligned(expert_out_bf16, 16) ||
+      !aligned(grad_expert_out_bf16, 16))
+    return fail(MOE_ERR_INVALID, "%s: row buffers must be 16-byte aligned", fn);
+  if (!aligned(dst_row, 4) || !aligned(topk_weights, 4) || !aligned(grad_weights, 4))
+    return fail(MOE_ERR_INVALID, "%s: index/weight buffers must be 4-byte aligned", fn);
+  return from_hip(moe::launch_combine_backward(num_tokens, hidden, top_k, num_rows,
+                                               grad_out_bf16, expert_out_bf16, dst_row,
+                                               topk_weights, grad_expert_out_bf16, grad_weights,
+                                               static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

@@ -131,6 +131,15 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return fmaxf(v, xor32_f32(v));
 }
 
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  v += xor16_f32(v);
+  return v + xor32_f32(v);
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
   v += dpp_f64<0xB1>(v);
   v += dpp_f64<0x4E>(v);

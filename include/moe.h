@@ -209,6 +209,41 @@ int moe_combine(int num_tokens, int hidden, int top_k, int num_rows,
                 const void* expert_out_bf16, const int32_t* dst_row,
                 const float* topk_weights, void* out_bf16, void* stream);
 
+/*
+ * moe_dispatch_backward -- gradient of dispatch with respect to x. The
+ * exchanges run in the backward pass too (DeepEP article, "Qu'est-ce que
+ * l'Expert Parallelism": every forward and backward pass needs the
+ * all-to-all). Each token collects the gradients of its rows:
+ *
+ *   grad_x[t, :] = bf16( sum over j with a row of grad_rows[dst_row[t,j], :] )
+ *
+ * summed in fp32 in slot order (moe_combine with unit weights).
+ *   grad_rows  [num_rows, hidden] bf16;  grad_x [num_tokens, hidden] bf16
+ * Requires hidden % 8 == 0.
+ */
+int moe_dispatch_backward(int num_tokens, int hidden, int top_k, int num_rows,
+                          const void* grad_rows_bf16, const int32_t* dst_row,
+                          void* grad_x_bf16, void* stream);
+
+/*
+ * moe_combine_backward -- gradients of moe_combine (same passage as
+ * moe_dispatch_backward). For every pair (t, j) with a row d = dst_row[t,j]:
+ *
+ *   grad_expert_out[d, :] = bf16( topk_weights[t,j] * grad_out[t, :] )
+ *   grad_weights[t, j]    = sum_h grad_out[t, h] * expert_out[d, h]   (fp32)
+ *
+ * Pairs without a row get grad_weights = 0 and write no row; rows of
+ * grad_expert_out that no pair addresses are left untouched. The dot
+ * products are summed in a fixed order (deterministic).
+ *   grad_out [num_tokens, hidden] bf16; expert_out, grad_expert_out
+ *   [num_rows, hidden] bf16; grad_weights [num_tokens, top_k] fp32
+ * Requires hidden % 8 == 0.
+ */
+int moe_combine_backward(int num_tokens, int hidden, int top_k, int num_rows,
+                         const void* grad_out_bf16, const void* expert_out_bf16,
+                         const int32_t* dst_row, const float* topk_weights,
+                         void* grad_expert_out_bf16, float* grad_weights, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

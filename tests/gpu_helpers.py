@@ -84,3 +84,22 @@ def assert_route_close(idx_g, w_g, idx_o, w_o, key, what=""):
     wg, wo = w_g[same], w_o[same]
     assert np.all(np.abs(wg - wo) <= np.spacing(np.maximum(np.abs(wg), np.abs(wo)))), what
     return len(diff_rows)
+
+
+def assert_bf16_within_ulp(gpu_bits, ref_bits, what=""):
+    """One bf16 ulp: the GPU rounds an fp32 product to bf16, the oracle rounds
+    the exact product once (the two roundings can differ by one step)."""
+    g = O.bf16_to_f32(gpu_bits).astype(np.float64)
+    r = O.bf16_to_f32(ref_bits).astype(np.float64)
+    bad = ~(np.abs(g - r) <= ulp_bf16(np.maximum(np.abs(g), np.abs(r))))
+    assert not bad.any(), "%s: %d values differ by more than one bf16 ulp" % (what, bad.sum())
+    return float((gpu_bits == ref_bits).mean()) if gpu_bits.size else 1.0
+
+
+def dot_tolerance(hidden, ref, dw_abs):
+    """Bound for an fp32 dot product of `hidden` terms summed as the kernel
+    does (per-lane FMA chains of at most 32 terms per group, a 6-level wave
+    tree, one add per group and a 4-wave sum): n * 2^-24 * sum|terms| with
+    n = 48 + groups, plus the final fp32 rounding of the reference."""
+    groups = -(-(hidden // 8) // 1024)
+    return (48 + groups) * 2.0 ** -24 * dw_abs + 2.0 ** -24 * np.abs(ref)

@@ -177,3 +177,40 @@ def test_binding_raises_with_message():
     _no_gpu()
     with pytest.raises(M.MoeError, match="MOE_ERR_INVALID.*num_tokens"):
         M.moe_route(-1, 8, 2, A16, None, 0, 1, 1, A16, A16b, stream=0)
+
+
+def _bwd(**kw):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, rows=8, g=A16, y=A16, dst=A16, w=A16, dy=A16b, dw=A16b)
+    a.update(kw)
+    return M.lib().moe_combine_backward(a["T"], a["H"], a["k"], a["rows"], a["g"], a["y"],
+                                        a["dst"], a["w"], a["dy"], a["dw"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=12), M.MOE_ERR_INVALID),
+    (dict(g=None), M.MOE_ERR_INVALID),
+    (dict(dw=None), M.MOE_ERR_INVALID),
+    (dict(dy=None), M.MOE_ERR_INVALID),
+    (dict(y=A16 + 8), M.MOE_ERR_INVALID),
+    (dict(dw=A16b + 2), M.MOE_ERR_INVALID),
+    (dict(k=0), M.MOE_ERR_INVALID),
+])
+def test_combine_backward_rejects(kw, status):
+    assert _bwd(**kw) == status
+    assert M.moe_last_error().startswith("moe_combine_backward")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=4), M.MOE_ERR_INVALID),
+    (dict(gx=None), M.MOE_ERR_INVALID),
+    (dict(g=A16 + 4), M.MOE_ERR_INVALID),
+    (dict(rows=-2), M.MOE_ERR_INVALID),
+])
+def test_dispatch_backward_rejects(kw, status):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, rows=8, g=A16, dst=A16, gx=A16b)
+    a.update(kw)
+    assert M.lib().moe_dispatch_backward(a["T"], a["H"], a["k"], a["rows"], a["g"], a["dst"],
+                                         a["gx"], None) == status
+    assert M.moe_last_error().startswith("moe_dispatch_backward")

@@ -18,8 +18,8 @@ torch = pytest.importorskip("torch")
 
 import combine_moe_layout_06_amd as M  # noqa: E402
 from combine_moe_layout_06_amd import LayerBuffers  # noqa: E402
-from gpu_helpers import (assert_combine_close, assert_route_close, dev, host,  # noqa: E402
-                         poison_like)
+from gpu_helpers import (assert_bf16_within_ulp, assert_combine_close,  # noqa: E402
+                         assert_route_close, dev, dot_tolerance, host, poison_like)
 from oracle import moe_oracle as O  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
@@ -535,3 +535,68 @@ def test_mxfp8_layer_end_to_end():
     got = host(b.combined, np.uint16)[:t]
     want, mag = O.combine(y, L["dst_row"], w_g)
     say("  mxfp8 combine bit-exact fraction %.6f" % assert_combine_close(got, want, mag, w.top_k))
+
+
+# --------------------------------------------------------------- backward
+
+BWD_CASES = [
+    # T, H, k, rows, drop_frac
+    (4096, 7168, 8, 32768, 0.0),
+    (1000, 520, 3, 3200, 0.1),
+    (777, 4096, 6, 5000, 0.2),
+    (200, 512, 11, 3000, 0.1),
+    (64, 16384, 2, 300, 0.0),          # several chunk groups per wave
+    (37, 8, 1, 40, 0.0),
+    (0, 256, 2, 0, 0.0),
+]
+
+
+def _bwd_inputs(case):
+    t, h, k, rows, drop = case
+    g = np.random.Generator(np.random.PCG64(t + 7 * h + k))
+    dst = g.permutation(max(rows, 1))[: t * k].reshape(t, k).astype(np.int32) if t else \
+        np.zeros((0, k), np.int32)
+    if t:
+        dst[g.random((t, k)) < drop] = -1
+    return g, dst
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "T%d_H%d_k%d_rows%d" % c[:4])
+def test_dispatch_backward_parity(case):
+    t, h, k, rows, drop = case
+    say("dispatch backward case", case)
+    g, dst = _bwd_inputs(case)
+    grows = W.random_bf16_rows(g, rows, h)
+    out_full = poison_like((max(t, 1) + GUARD, h), torch.int16)
+    M.moe_dispatch_backward(t, h, k, rows, dev(grows) if rows else None,
+                            dev(dst) if t else None, out_full)
+    out = host(out_full, np.uint16)
+    assert np.all(out[max(t, 1):] == 0xFFFF)
+    want, mag = O.dispatch_backward(grows, dst)
+    say("  bit-exact fraction %.6f" % assert_combine_close(out[:t], want, mag, k))
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "T%d_H%d_k%d_rows%d" % c[:4])
+def test_combine_backward_parity(case):
+    t, h, k, rows, drop = case
+    say("combine backward case", case)
+    g, dst = _bwd_inputs(case)
+    dout = W.random_bf16_rows(g, t, h)
+    y = W.random_bf16_rows(g, rows, h)
+    w = W.random_weights(g, t, k)
+    dy_full = poison_like((rows + GUARD, h), torch.int16)
+    dw_full = poison_like((max(t, 1), k), torch.float32)
+    M.moe_combine_backward(t, h, k, rows, dev(dout) if t else None, dev(y) if rows else None,
+                           dev(dst) if t else None, dev(w) if t else None, dy_full, dw_full)
+    dy = host(dy_full, np.uint16)
+    dw = host(dw_full)[:t]
+    assert np.all(dy[rows:] == 0xFFFF), "stray write after grad_expert_out"
+    want_dy, written, want_dw, dw_abs = O.combine_backward(dout, y, dst, w, rows)
+    assert np.all(dy[:rows][~written] == 0xFFFF)          # rows of no pair stay untouched
+    frac = assert_bf16_within_ulp(dy[:rows][written], want_dy[written], "grad_expert_out")
+    live = dst >= 0
+    assert np.all(dw[~live] == 0.0)
+    err = np.abs(dw.astype(np.float64) - want_dw.astype(np.float64))
+    assert np.all(err <= dot_tolerance(h, want_dw.astype(np.float64), dw_abs))
+    say("  dy bit-exact fraction %.6f, max dw error / bound %.3g" % (
+        frac, float(np.max(err / np.maximum(dot_tolerance(h, want_dw, dw_abs), 1e-30))) if t else 0))
