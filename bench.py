@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--dispatch", default="auto", choices=["auto", "bf16", "fp8", "mxfp8"],
                    help="dispatched format (auto: the workload's own)")
     p.add_argument("--cold-steps", type=int, default=10)
+    p.add_argument("--graph", action="store_true",
+                   help="capture the timed steps into one HIP graph and replay it")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--pass", dest="pass_", default="forward", choices=["forward", "backward"],
@@ -336,16 +338,33 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed steps: back to back, nothing but the path on the stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        d = inputs[(warm + i) % len(inputs)]
-        buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        buf.layout()
-        buf.dispatch(d["x"])
-        buf.combine(y)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def timed_steps():
+        for i in range(steps):
+            d = inputs[(warm + i) % len(inputs)]
+            buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+            buf.layout()
+            buf.dispatch(d["x"])
+            buf.combine(y)
+
+    if args.graph:
+        # all timed steps (each with its own inputs) in one graph: the
+        # launches are recorded once, replay issues them without the host
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            timed_steps()
+        graph.replay()                      # first replay uploads the graph
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        timed_steps()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     # ---- the same steps again with HIP events between the phases (on the
     # launch stream) for the per-phase times and the roofline
@@ -410,6 +429,7 @@ def main():
         "vs_baseline": None,
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
+        "launch": "hip graph replay" if args.graph else "eager stream",
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
                    % (w.name, w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                       "group-limited sigmoid G=%d kg=%d" % (w.groups, w.topk_groups)
@@ -426,6 +446,7 @@ def main():
         "phases_us": {n: round(v * 1e3, 2) for n, v in phase_ms.items()},
         "phase_bytes": nbytes,
         "event_us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
+        "event_us_per_step_p99": round(float(np.percentile(step_ms, 99)) * 1e3, 2),
         "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
         "copy_ceiling_gbps": round(copy_ceiling_gbps(), 1),
         "roofline": roof,

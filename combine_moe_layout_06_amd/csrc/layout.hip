@@ -9,7 +9,8 @@
 // sections "Megatron-LM (NVIDIA)" and "Défis et optimisations" (capacity
 // and token dropping).
 //
-// Two launches, no global atomics, deterministic:
+// Two launches (one when all pairs fit in one tile), no global atomics,
+// deterministic:
 //   1. count: one block per tile of whole tokens builds the tile's expert
 //      histogram (and per-rank distinct-token counts) in LDS and writes it
 //      to the workspace.
@@ -163,8 +164,12 @@ __device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, i
   *pre += p;
 }
 
+// self_count: all pairs form one tile (T*k <= kTilePairs) and no count pass
+// ran; every block builds the histogram (and block 0 the distinct-token
+// counts) from topk_idx itself, so the layout takes a single launch.
 __global__ __launch_bounds__(kThreads) void layout_place_kernel(
-    int T, int E, int k, int R, int epr, int cap, int tt, int ntiles, int num_rows,
+    int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
+    int self_count, int num_rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_hist,
     const int32_t* __restrict__ ws_rhist, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     const int p = (wave * kChunks + c) * MOE_WAVE + lane;
     v[c] = p < np ? idx[pair0 + p] : -1;
   }
-  const int hist_n = ntiles * E;
+  const int hist_n = self_count ? 0 : ntiles * E;
   int h[kStage / kThreads];
   stage_load(h, ws_hist, min(kStage, hist_n));
 
@@ -206,6 +211,42 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   }
   if (tid == 0) s_overflow = 0;
 
+  if (self_count) {
+    // the only tile: histogram of all pairs, ranks of the pairs in LDS
+    const int np_all = T * k;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kTilePairs / kThreads; ++q) {
+      const int p = q * kThreads + tid;
+      const int e = p < np_all ? clean_expert(idx[p], E) : -1;
+      if (e >= 0) atomicAdd(&s_tot[e], 1);
+      if (p < np_all) s_stage[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+    }
+    __syncthreads();
+    if (tile == 0 && rank_token_counts != nullptr) {
+      for (int tl = tid; tl < T; tl += kThreads) {
+        const int* r = s_stage + tl * k;
+        if (R <= 64) {
+          uint64_t seen = 0;
+          for (int j = 0; j < k; ++j) {
+            const int x = r[j];
+            if (x >= 0 && !((seen >> x) & 1ull)) {
+              seen |= 1ull << x;
+              atomicAdd(&s_rtc[x], 1);
+            }
+          }
+        } else {
+          for (int j = 0; j < k; ++j) {
+            const int x = r[j];
+            bool first = x >= 0;
+            for (int o = 0; o < j; ++o) first = first && r[o] != x;
+            if (first) atomicAdd(&s_rtc[x], 1);
+          }
+        }
+      }
+    }
+  }
+
   // per-expert totals and the base of this tile (sum over earlier tiles)
   for (int c0 = 0; c0 < hist_n; c0 += kStage) {
     const int n = min(kStage, hist_n - c0);
@@ -216,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     for (int e = tid; e < E; e += kThreads) column_sums(s_stage, c0, n, E, e, tile, &s_tot[e], &s_pre[e]);
   }
   // block 0 also sums the per-tile distinct-token counts of each rank
-  if (tile == 0 && rank_token_counts != nullptr) {
+  if (!self_count && tile == 0 && rank_token_counts != nullptr) {
     const int rn = ntiles * R;
     for (int c0 = 0; c0 < rn; c0 += kStage) {
       const int n = min(kStage, rn - c0);
@@ -338,7 +379,8 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   int32_t* ws_hist = static_cast<int32_t*>(workspace);
   int32_t* ws_rhist = rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
-  if (ntiles > 0) {
+  const int self_count = T * k <= kTilePairs ? 1 : 0;
+  if (ntiles > 0 && !self_count) {
     hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
                        T, E, k, R, epr, epr_shift, tt, idx, ws_hist, ws_rhist);
     const hipError_t err = hipGetLastError();
@@ -349,7 +391,8 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   const int fill_blocks = cap > 0 ? (E + kWaves - 1) / kWaves : 1;
   const int blocks = ntiles > fill_blocks ? ntiles : fill_blocks;
   hipLaunchKernelGGL(layout_place_kernel, dim3(blocks), dim3(kThreads), 0,
-                     stream, T, E, k, R, epr, cap, tt, ntiles, num_rows, idx, ws_hist,
+                     stream, T, E, k, R, epr, epr_shift, cap, tt, ntiles, self_count, num_rows,
+                     idx, ws_hist,
                      ws_rhist, expert_counts, expert_offsets, rank_counts, rank_offsets,
                      rank_token_counts, dst_row, src_pair, overflow);
   return hipGetLastError();

@@ -600,3 +600,45 @@ def test_combine_backward_parity(case):
     assert np.all(err <= dot_tolerance(h, want_dw.astype(np.float64), dw_abs))
     say("  dy bit-exact fraction %.6f, max dw error / bound %.3g" % (
         frac, float(np.max(err / np.maximum(dot_tolerance(h, want_dw, dw_abs), 1e-30))) if t else 0))
+
+
+# ------------------------------------------------------------ graph replay
+
+def test_decode_steps_replay_in_a_graph():
+    """Three decode steps (route, layout, FP8 dispatch into capacity buffers,
+    combine) captured in one HIP graph; the graph is replayed three times with
+    eager work and synchronisations between replays, and every replay must
+    equal the eager run bit for bit."""
+    w = W.WORKLOADS["decode"]
+    steps = [W.make_inputs(w, w.step_seed0 + i) for i in range(3)]
+    ins = [(dev(s.logits), dev(s.bias), dev(s.x)) for s in steps]
+    bufs = [LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                  fp8=True) for _ in steps]
+    y = dev(W.random_bf16_rows(np.random.Generator(np.random.PCG64(9)), w.num_rows, w.hidden))
+
+    def run():
+        for (lg, bi, x), b in zip(ins, bufs):
+            M.run_layer(b, lg, bi, x, w.score_fn, w.groups, w.topk_groups)
+            b.combine(y)
+
+    names = ("topk_idx", "topk_weights", "dst_row", "src_pair", "expert_counts", "overflow",
+             "combined")
+    run()
+    torch.cuda.synchronize()
+    eager = [[getattr(b, n).clone() for n in names] for b in bufs]
+    eager_q = [b.dispatched[b.src_pair >= 0].clone() for b in bufs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for b in bufs:                       # eager work between replays
+            for n in names:
+                getattr(b, n).fill_(-7 if getattr(b, n).dtype != torch.float32 else -7.0)
+            b.dispatched.fill_(0x55)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for b, e, q in zip(bufs, eager, eager_q):
+            for n, v in zip(names, e):
+                assert torch.equal(getattr(b, n), v), (rep, n)
+            assert torch.equal(b.dispatched[b.src_pair >= 0], q), rep
