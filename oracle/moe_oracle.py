@@ -41,6 +41,10 @@ Readings where the pages are silent (each is also listed in the design notes):
   R7 capacity: pairs beyond `cap` in an expert's stable order are dropped.
   R18 MXFP8: 1x32 blocks, E8M0 scale 2^(floor(log2 amax) - 8), e4m3fn codes
      of x / scale with round-to-nearest-even and saturation.
+  R20 deduplicated dispatch: one row per (token, rank) with at least one
+     unmasked expert there (capacity ignored), rows of a rank in token order;
+     hierarchical combine: per-(token, rank) partial sums rounded to bf16,
+     then a per-token sum of the partials rounded once more.
 """
 
 from __future__ import annotations
@@ -517,6 +521,139 @@ def combine_backward(grad_out_bits: np.ndarray, y_bits: np.ndarray,
         dy[rows] = round_to_bf16(topk_w[live, j].astype(F64)[:, None] * g[live])
         written[rows] = True
     return dy, written, dw.astype(F32), dw_abs
+
+
+# ---------------------------------------------------------------------------
+# Deduplicated dispatch and hierarchical combine (hyper.ai story on Hybrid-EP:
+# the combine reduces hierarchically, first the results inside one
+# destination, then across destinations). One row per (token, destination
+# rank) crosses to a rank however many of its experts the token chose there;
+# the rank fans the row out to its local experts, reduces their weighted
+# outputs into one partial row per (token, rank), and only the partials
+# travel back, where each token sums its partials (reading R20).
+# ---------------------------------------------------------------------------
+
+def rank_layout(topk_idx: np.ndarray, num_experts: int, num_ranks: int) -> dict:
+    """Rows of the (token, rank) buffer.
+
+    A token t has a row on rank r when at least one of its unmasked experts
+    lives on r (rank r owns experts [r*E/R, (r+1)*E/R); glossary "Expert
+    Parallelism", "Le principe de base"). Capacity plays no part: the row
+    exists by demand. Rank r's rows form the region
+    [rank_token_offsets[r], rank_token_offsets[r+1]) and are ordered by token
+    (reading R2 applied to (token, rank) pairs). The buffer is sized for
+    T * min(k, R) rows, its largest possible size, so that nothing is read
+    back first (hyper.ai story on Hybrid-EP, preallocated buffers).
+
+    Returns
+      rank_token_counts [R], rank_token_offsets [R+1]
+      rank_row [T, k]: the (t, rank of expert j) row of every unmasked slot,
+                       -1 for masked slots
+      send_row [T, k]: that row at the first slot (in slot order) of each
+                       rank, -1 at the token's later slots on the same rank
+                       and at masked slots; dispatching x with send_row as
+                       the destination map sends one copy per (token, rank)
+      row_token [T * min(k, R)]: token of each row, -1 past the last row
+      num_rank_rows: T * min(k, R)"""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    t, k = idx.shape
+    epr = num_experts // num_ranks
+    live = (idx >= 0) & (idx < num_experts)
+    rank = np.where(live, idx // epr, -1)
+
+    # first slot of each (token, rank)
+    first = live.copy()
+    for j in range(k):
+        for o in range(j):
+            first[:, j] &= rank[:, o] != rank[:, j]
+
+    hit = np.zeros((t, num_ranks), dtype=bool)
+    tt, jj = np.nonzero(live)
+    hit[tt, rank[tt, jj]] = True
+    counts = hit.sum(axis=0).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    # position of token t among the tokens of rank r, in token order
+    pos = np.cumsum(hit, axis=0) - 1
+    row_of = offsets[:-1][None, :] + pos
+
+    rank_row = np.full((t, k), -1, dtype=np.int64)
+    rank_row[tt, jj] = row_of[tt, rank[tt, jj]]
+    send_row = np.where(first, rank_row, -1)
+
+    num_rank_rows = t * min(k, num_ranks)
+    row_token = np.full(num_rank_rows, -1, dtype=np.int64)
+    ht, hr = np.nonzero(hit)
+    row_token[row_of[ht, hr]] = ht
+
+    i32 = np.int32
+    return dict(rank_token_counts=counts.astype(i32), rank_token_offsets=offsets.astype(i32),
+                rank_row=rank_row.astype(i32), send_row=send_row.astype(i32),
+                row_token=row_token.astype(i32), num_rank_rows=num_rank_rows)
+
+
+def expand_rows(rank_rows: np.ndarray, rank_row: np.ndarray, src_pair: np.ndarray):
+    """On the receiving rank, each expert row takes the (token, rank) row of
+    its pair: out[q] = rank_rows[rank_row.flat[src_pair[q]]] for every row q
+    that holds a pair. `rank_rows` may be bf16 bits, FP8 codes or a scale
+    array: any array whose first axis is the row. Returns (out, written);
+    rows without a pair are left undefined (zero here)."""
+    n = src_pair.shape[0]
+    out = np.zeros((n,) + rank_rows.shape[1:], dtype=rank_rows.dtype)
+    written = src_pair >= 0
+    flat = rank_row.reshape(-1)
+    out[written] = rank_rows[flat[src_pair[written]]]
+    return out, written
+
+
+def combine_local(y_bits: np.ndarray, dst_row: np.ndarray, rank_row: np.ndarray,
+                  topk_w: np.ndarray, num_rank_rows: int):
+    """First level of the hierarchical combine: each rank reduces, for every
+    token it holds a row of, the weighted outputs of that token's experts on
+    the rank:
+        partial[rank_row[t, j]] = bf16( sum over slots j' of t with
+            rank_row[t, j'] = rank_row[t, j] and a kept expert row of
+            w[t, j'] * y[dst_row[t, j']] )
+    taken in fp64 and rounded once to bf16 (the partial travels as a bf16 row,
+    reading R20). A (token, rank) row whose pairs were all dropped by capacity
+    is still written, as +0.
+    Returns (partial bits [num_rank_rows, H], written, abs_sum [num_rank_rows,
+    H] = sum of |w y| of the row's terms)."""
+    t, k = dst_row.shape
+    h = y_bits.shape[1]
+    acc = np.zeros((num_rank_rows, h), dtype=F64)
+    mag = np.zeros((num_rank_rows, h), dtype=F64)
+    written = np.zeros(num_rank_rows, dtype=bool)
+    for j in range(k):
+        s = rank_row[:, j]
+        has = s >= 0
+        written[s[has]] = True
+        keep = has & (dst_row[:, j] >= 0)
+        if not keep.any():
+            continue
+        term = topk_w[keep, j].astype(F64)[:, None] * \
+            bf16_to_f32(y_bits[dst_row[keep, j]]).astype(F64)
+        # each (token, rank) row appears at most once per slot column
+        np.add.at(acc, s[keep], term)
+        np.add.at(mag, s[keep], np.abs(term))
+    return round_to_bf16(acc), written, mag
+
+
+def combine_partials(partial_bits: np.ndarray, send_row: np.ndarray):
+    """Second level: out[t] = bf16( sum over t's (token, rank) rows of the
+    partial rows ), fp64 sum, one rounding. Each row is named once, at the
+    rank's first slot (send_row). Returns (out bits [T, H], abs_sum)."""
+    t, k = send_row.shape
+    return combine(partial_bits, send_row, np.ones((t, k), dtype=F32))
+
+
+def combine_hierarchical(y_bits: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray,
+                         rank_lay: dict):
+    """Both levels: the per-rank partials, then their sum per token.
+    Returns (out bits [T, H], partial bits, partial abs_sum)."""
+    partial, _, pmag = combine_local(y_bits, dst_row, rank_lay["rank_row"], topk_w,
+                                     rank_lay["num_rank_rows"])
+    out, _ = combine_partials(partial, rank_lay["send_row"])
+    return out, partial, pmag
 
 
 # ---------------------------------------------------------------------------
