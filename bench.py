@@ -59,8 +59,10 @@ def parse():
                    help="capture the timed steps into one HIP graph and replay it")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--pass", dest="pass_", default="forward", choices=["forward", "backward"],
-                   help="backward: time combine-backward then dispatch-backward instead")
+    p.add_argument("--pass", dest="pass_", default="forward",
+                   choices=["forward", "backward", "hierarchical"],
+                   help="backward: time combine-backward then dispatch-backward instead; "
+                        "hierarchical: one row per (token, rank) out, per-rank partial sums back")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -160,6 +162,159 @@ def run_backward(args, w, M, W, torch, np):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": nb["combine_backward"]},
         "cpu_baseline": None}), flush=True)
+
+
+def scale_bytes(H, dtype):
+    return {0: 0, 1: (H // 128) * 4, 2: H // 32}[dtype]
+
+
+def hierarchical_bytes(w, rows_live, n_sent, dtype):
+    """Algorithmic bytes of the hierarchical pass, per phase. n_sent is the
+    number of (token, rank) rows; a fanned-out row is read once per rank row
+    it comes from and written once per expert row."""
+    T, H, E, k, R = w.tokens, w.hidden, w.experts, w.top_k, w.ranks
+    row = (H if dtype else 2 * H) + scale_bytes(H, dtype)
+    nrr = T * min(k, R)
+    b = step_bytes(w, rows_live, dtype)
+    return dict(
+        route=b["route"], layout=b["layout"],
+        rank_layout=T * k * 4 + 2 * T * k * 4 + nrr * 4 + (2 * R + 1) * 4,
+        dispatch=T * H * 2 + T * k * 4 + n_sent * row,
+        expand=w.num_rows * 4 + rows_live * 4 + n_sent * row + rows_live * row,
+        combine_local=rows_live * H * 2 + T * k * 12 + n_sent * H * 2,
+        combine_partials=n_sent * H * 2 + T * k * 4 + T * H * 2)
+
+
+def run_hierarchical(args, w, M, W, torch, np):
+    """Deduplicated dispatch and hierarchical combine: route, expert layout,
+    (token, rank) layout, one copy per (token, rank), fan-out to the expert
+    rows, then per-(token, rank) partial sums and the per-token sum."""
+    dev = torch.device("cuda:0")
+    dtype = {"auto": w.dispatch_dtype, "bf16": 0, "fp8": 1, "mxfp8": 2}[args.dispatch]
+    T, H, k = w.tokens, w.hidden, w.top_k
+    n_inputs = args.steps + args.warmup if w.steps > 1 else 1
+    seeds = [w.step_seed0 + i for i in range(n_inputs)] if w.steps > 1 else [args.seed]
+    inputs = []
+    for s in seeds:
+        inp = W.make_inputs(w, s)
+        inputs.append(dict(
+            logits=torch.from_numpy(inp.logits).to(dev),
+            bias=torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None,
+            x=torch.from_numpy(inp.x.view(np.int16)).to(dev)))
+    lb = M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev, dtype=dtype)
+    rb = M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev)
+
+    phases = ["route", "layout", "rank_layout", "dispatch", "expand", "combine_local",
+              "combine_partials"]
+
+    def calls(i):
+        d = inputs[i % len(inputs)]
+        return [lambda: lb.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups),
+                lb.layout, lambda: rb.rank_layout(lb.topk_idx), lambda: rb.dispatch(d["x"]),
+                lambda: rb.expand(lb), lambda: rb.combine_local(lb, y),
+                lambda: rb.combine_partials(lb.combined)]
+
+    # stand-in expert output: the fanned-out rows of step 0, dequantised
+    y = None
+    for c in calls(0)[:5]:
+        c()
+    torch.cuda.synchronize()
+    rows = lb.num_rows
+    if dtype == 1:
+        codes = lb.dispatched[:rows].view(torch.float8_e4m3fn).float()
+        y = (codes * lb.scales[:rows].repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    elif dtype == 2:
+        codes = lb.dispatched[:rows].view(torch.float8_e4m3fn).float()
+        sc = torch.exp2(lb.scales[:rows].float() - 127.0).repeat_interleave(32, dim=1)
+        y = (codes * sc).to(torch.bfloat16)
+    else:
+        y = lb.dispatched[:rows].view(torch.bfloat16).clone()
+    y = y.view(torch.int16).contiguous()
+    rows_live = int((lb.dst_row >= 0).sum().item())
+    n_sent = int(rb.rank_token_offsets[-1].item())
+
+    for i in range(args.warmup):
+        for c in calls(i):
+            c()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for c in calls(args.warmup + i):
+            c()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        for j, c in enumerate(calls(args.warmup + i)):
+            c()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    ph = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / len(ev) * 1e3
+          for j, n in enumerate(phases)}
+    nb = hierarchical_bytes(w, rows_live, n_sent, dtype)
+    ms = wall * 1e3 / args.steps
+    total = sum(nb.values())
+    dom = max(("dispatch", "expand", "combine_local", "combine_partials"), key=lambda n: ph[n])
+    achieved = nb[dom] / (ph[dom] * 1e-6) / 1e9
+    row = (H if dtype else 2 * H) + scale_bytes(H, dtype)
+    out = {
+        "metric": "hierarchical dispatch+combine tokens/s, %s shape, 1 GPU" % w.name,
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
+        "data": "synthetic",
+        "config": {"workload": "%s hierarchical: T=%d H=%d E=%d k=%d R=%d, one row per "
+                   "(token, rank), bf16 partials" % (w.name, T, H, w.experts, k, w.ranks),
+                   "tokens": T, "hidden": H, "experts": w.experts, "top_k": k,
+                   "ranks": w.ranks, "seed": args.seed},
+        "gbps": round(total / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total, "phase_bytes": nb,
+        "phases_us": {n: round(v, 2) for n, v in ph.items()},
+        "rows": {"pairs": rows_live, "sent": n_sent},
+        "exchanged_bytes": {"flat": rows_live * row + rows_live * H * 2,
+                            "hierarchical": n_sent * row + n_sent * H * 2},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nb[dom]},
+        "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_hierarchical(w, args.seed, args.cpu_seconds, dtype)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_hierarchical(w, seed, budget_s, dtype):
+    """The CPU oracle of the hierarchical pass on the first 512 tokens."""
+    from oracle import moe_oracle as O
+    from synth import workloads as W
+
+    ts = min(w.tokens, 512)
+    inp = W.make_inputs(w, seed, tokens=ts)
+    disp = {0: O.dispatch_bf16, 1: O.dispatch_fp8, 2: O.dispatch_mxfp8}[dtype]
+    idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+    L = O.layout(idx, w.experts, w.ranks, w.capacity)
+    y, _ = O.dispatch_bf16(inp.x, L["dst_row"], L["num_rows"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+        L = O.layout(idx, w.experts, w.ranks, w.capacity)
+        rl = O.rank_layout(idx, w.experts, w.ranks)
+        sent = disp(inp.x, rl["send_row"], rl["num_rank_rows"])
+        for part in sent[:-1]:
+            O.expand_rows(part, rl["rank_row"], L["src_pair"])
+        O.combine_hierarchical(y, L["dst_row"], wt, rl)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": ts * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%s shape, first %d of %d tokens, %d repeats of the hierarchical pass "
+                      "in %.1f s (numpy, single thread)" % (w.name, ts, w.tokens, reps, el)}
 
 
 def sha_of(paths):
@@ -283,6 +438,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.pass_ == "backward":
         run_backward(args, w, M, W, torch, np)
+        return
+    if args.pass_ == "hierarchical":
+        run_hierarchical(args, w, M, W, torch, np)
         return
     dtype = {"auto": w.dispatch_dtype, "bf16": M.MOE_DTYPE_BF16, "fp8": M.MOE_DTYPE_FP8_E4M3,
              "mxfp8": M.MOE_DTYPE_MXFP8_E4M3}[args.dispatch]

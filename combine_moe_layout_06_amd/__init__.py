@@ -38,7 +38,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layo
 
 EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
             "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch", "moe_combine",
-            "moe_dispatch_backward", "moe_combine_backward")
+            "moe_dispatch_backward", "moe_combine_backward",
+            "moe_rank_layout_workspace_bytes", "moe_rank_layout", "moe_expand",
+            "moe_combine_local", "moe_combine_partials")
 
 _lib = None
 
@@ -78,6 +80,16 @@ def lib() -> ctypes.CDLL:
     L.moe_dispatch_backward.restype = i32
     L.moe_combine_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine_backward.restype = i32
+    L.moe_rank_layout_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_rank_layout_workspace_bytes.restype = sz
+    L.moe_rank_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_rank_layout.restype = i32
+    L.moe_expand.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp]
+    L.moe_expand.restype = i32
+    L.moe_combine_local.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.moe_combine_local.restype = i32
+    L.moe_combine_partials.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    L.moe_combine_partials.restype = i32
     _lib = L
     return L
 
@@ -175,4 +187,38 @@ def moe_combine_backward(num_tokens, hidden, top_k, num_rows, grad_out_bf16, exp
                                       _stream(stream)))
 
 
-from .buffers import LayerBuffers, run_layer  # noqa: E402,F401
+def moe_rank_layout_workspace_bytes(num_tokens, top_k, num_ranks) -> int:
+    return int(lib().moe_rank_layout_workspace_bytes(num_tokens, top_k, num_ranks))
+
+
+def moe_rank_layout(num_tokens, num_experts, top_k, num_ranks, topk_idx, rank_token_counts,
+                    rank_token_offsets, rank_row, send_row, row_token, workspace,
+                    workspace_bytes, stream=None) -> None:
+    _check(lib().moe_rank_layout(num_tokens, num_experts, top_k, num_ranks, _ptr(topk_idx),
+                                 _ptr(rank_token_counts), _ptr(rank_token_offsets),
+                                 _ptr(rank_row), _ptr(send_row), _ptr(row_token),
+                                 _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def moe_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, rank_rows, rank_scales,
+               rank_row, num_rows, src_pair, out, out_scales, stream=None) -> None:
+    _check(lib().moe_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, _ptr(rank_rows),
+                            _ptr(rank_scales), _ptr(rank_row), num_rows, _ptr(src_pair),
+                            _ptr(out), _ptr(out_scales), _stream(stream)))
+
+
+def moe_combine_local(num_tokens, hidden, top_k, num_rows, expert_out_bf16, dst_row, rank_row,
+                      topk_weights, num_rank_rows, partial_bf16, stream=None) -> None:
+    _check(lib().moe_combine_local(num_tokens, hidden, top_k, num_rows, _ptr(expert_out_bf16),
+                                   _ptr(dst_row), _ptr(rank_row), _ptr(topk_weights),
+                                   num_rank_rows, _ptr(partial_bf16), _stream(stream)))
+
+
+def moe_combine_partials(num_tokens, hidden, top_k, num_rank_rows, partial_bf16, send_row,
+                         out_bf16, stream=None) -> None:
+    _check(lib().moe_combine_partials(num_tokens, hidden, top_k, num_rank_rows,
+                                      _ptr(partial_bf16), _ptr(send_row), _ptr(out_bf16),
+                                      _stream(stream)))
+
+
+from .buffers import LayerBuffers, RankBuffers, run_layer  # noqa: E402,F401

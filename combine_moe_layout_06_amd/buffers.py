@@ -12,8 +12,9 @@ import dataclasses
 from typing import Optional
 
 from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_FP8_BLOCK,
-               MOE_MX_BLOCK, moe_combine, moe_dispatch, moe_layout,
-               moe_layout_workspace_bytes, moe_route)
+               MOE_MX_BLOCK, moe_combine, moe_combine_local, moe_combine_partials,
+               moe_dispatch, moe_expand, moe_layout, moe_layout_workspace_bytes,
+               moe_rank_layout, moe_rank_layout_workspace_bytes, moe_route)
 
 
 @dataclasses.dataclass
@@ -105,6 +106,88 @@ class LayerBuffers:
     def combine(self, expert_out, stream=None):
         moe_combine(self.tokens, self.hidden, self.top_k, self.num_rows, expert_out,
                     self.dst_row, self.topk_weights, self.combined, stream)
+
+
+@dataclasses.dataclass
+class RankBuffers:
+    """Buffers of the deduplicated dispatch and the hierarchical combine:
+    one row per (token, rank), sized for its maximum T * min(k, R) rows so
+    that no count is read back. Used with the expert layout of a
+    LayerBuffers of the same shape (its dst_row, src_pair and weights)."""
+    tokens: int
+    hidden: int
+    experts: int
+    top_k: int
+    ranks: int
+    dtype: int
+    rank_token_counts: object = None
+    rank_token_offsets: object = None
+    rank_row: object = None
+    send_row: object = None
+    row_token: object = None
+    workspace: object = None
+    workspace_bytes: int = 0
+    sent: object = None          # [rank rows, H] bf16 (as int16) or uint8 codes
+    sent_scales: object = None   # FP8 fp32 / MXFP8 uint8 scales of the sent rows
+    partial: object = None       # [rank rows, H] bf16 partial sums (as int16)
+
+    @property
+    def num_rank_rows(self) -> int:
+        return self.tokens * min(self.top_k, self.ranks)
+
+    @classmethod
+    def allocate(cls, tokens, hidden, experts, top_k, ranks, dtype=MOE_DTYPE_BF16,
+                 device="cuda") -> "RankBuffers":
+        import torch
+        i32 = dict(dtype=torch.int32, device=device)
+        b = cls(tokens, hidden, experts, top_k, ranks, dtype)
+        t, k, r = tokens, top_k, ranks
+        n = max(b.num_rank_rows, 1)
+        b.rank_token_counts = torch.empty(r, **i32)
+        b.rank_token_offsets = torch.empty(r + 1, **i32)
+        b.rank_row = torch.empty((t, k), **i32)
+        b.send_row = torch.empty((t, k), **i32)
+        b.row_token = torch.empty(n, **i32)
+        b.workspace_bytes = moe_rank_layout_workspace_bytes(t, k, r)
+        b.workspace = torch.empty(max(b.workspace_bytes, 4), dtype=torch.uint8, device=device)
+        if dtype == MOE_DTYPE_FP8_E4M3:
+            b.sent = torch.empty((n, hidden), dtype=torch.uint8, device=device)
+            b.sent_scales = torch.empty((n, hidden // MOE_FP8_BLOCK), dtype=torch.float32,
+                                        device=device)
+        elif dtype == MOE_DTYPE_MXFP8_E4M3:
+            b.sent = torch.empty((n, hidden), dtype=torch.uint8, device=device)
+            b.sent_scales = torch.empty((n, hidden // MOE_MX_BLOCK), dtype=torch.uint8,
+                                        device=device)
+        else:
+            b.sent = torch.empty((n, hidden), dtype=torch.int16, device=device)
+        b.partial = torch.empty((n, hidden), dtype=torch.int16, device=device)
+        return b
+
+    def rank_layout(self, topk_idx, stream=None):
+        moe_rank_layout(self.tokens, self.experts, self.top_k, self.ranks, topk_idx,
+                        self.rank_token_counts, self.rank_token_offsets, self.rank_row,
+                        self.send_row, self.row_token, self.workspace, self.workspace_bytes,
+                        stream)
+
+    def dispatch(self, x, stream=None):
+        """One copy of each token per rank it has experts on."""
+        moe_dispatch(self.tokens, self.hidden, self.top_k, self.num_rank_rows, x,
+                     self.send_row, self.dtype, self.sent, self.sent_scales, stream)
+
+    def expand(self, layer: LayerBuffers, stream=None):
+        """Fan the sent rows out to the expert rows of `layer`."""
+        moe_expand(self.tokens, self.hidden, self.top_k, self.dtype, self.num_rank_rows,
+                   self.sent, self.sent_scales, self.rank_row, layer.num_rows, layer.src_pair,
+                   layer.dispatched, layer.scales, stream)
+
+    def combine_local(self, layer: LayerBuffers, expert_out, stream=None):
+        moe_combine_local(self.tokens, self.hidden, self.top_k, layer.num_rows, expert_out,
+                          layer.dst_row, self.rank_row, layer.topk_weights, self.num_rank_rows,
+                          self.partial, stream)
+
+    def combine_partials(self, out, stream=None):
+        moe_combine_partials(self.tokens, self.hidden, self.top_k, self.num_rank_rows,
+                             self.partial, self.send_row, out, stream)
 
 
 def run_layer(buf: LayerBuffers, logits, bias, x, score_fn, num_groups=1, topk_groups=1,

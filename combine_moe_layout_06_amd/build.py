@@ -29,7 +29,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_layout.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["moe_api.hip", "route.hip", "layout.hip", "dispatch.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "layout.hip", "dispatch.hip", "combine.hip",
+           "hierarchical.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

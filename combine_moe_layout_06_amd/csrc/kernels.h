@@ -26,6 +26,13 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
                          int32_t* src_pair, int32_t* overflow, void* workspace,
                          hipStream_t stream);
 
+// (token, rank) rows of the deduplicated dispatch.
+size_t rank_layout_workspace_bytes(int T, int k, int R);
+hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
+                              int32_t* counts, int32_t* offsets, int32_t* rank_row,
+                              int32_t* send_row, int32_t* row_token, void* workspace,
+                              hipStream_t stream);
+
 hipError_t launch_dispatch_bf16(int T, int H, int k, int num_rows, const void* x,
                                 const int32_t* dst_row, void* out, hipStream_t stream);
 
@@ -41,6 +48,16 @@ hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* 
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
                           hipStream_t stream);
+
+// Fan-out of the (token, rank) rows to the expert rows, and the per-rank
+// partial combine.
+hipError_t launch_expand(int T, int H, int k, int dtype, int num_rank_rows, const void* src,
+                         const void* src_scales, const int32_t* rank_row, int num_rows,
+                         const int32_t* src_pair, void* out, void* out_scales,
+                         hipStream_t stream);
+hipError_t launch_combine_local(int T, int H, int k, int num_rows, int num_rank_rows,
+                                const void* y, const int32_t* dst_row, const int32_t* rank_row,
+                                const float* w, void* partial, hipStream_t stream);
 
 hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void* dout,
                                    const void* y, const int32_t* dst_row, const float* w,

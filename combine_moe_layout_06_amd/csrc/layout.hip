@@ -352,6 +352,194 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// (token, rank) rows for the deduplicated dispatch and the hierarchical
+// combine (hyper.ai story on Hybrid-EP: the combine reduces inside one
+// destination first, then across destinations). The pair (t, j) at the
+// token's first slot on rank r stands for the (t, r) row. These pairs are
+// placed the way the expert layout places its pairs, with the rank as the
+// key: counted per tile, based on the tiles before, ranked by lane order
+// inside each wave and chained across waves, so that the rows of a rank
+// come in token order. Every other slot of the token on r shares the row.
+// ---------------------------------------------------------------------------
+
+// First slot of the token whose rank equals that of slot j (j itself when
+// it is the first), or -1 for a masked slot. `r` holds the ranks of the
+// token's k slots.
+__device__ __forceinline__ int first_slot_of_rank(const int* r, int j) {
+  const int x = r[j];
+  if (x < 0) return -1;
+  for (int o = 0; o < j; ++o)
+    if (r[o] == x) return o;
+  return j;
+}
+
+__global__ __launch_bounds__(kThreads) void rank_count_kernel(
+    int T, int E, int k, int R, int epr, int epr_shift, int tt,
+    const int32_t* __restrict__ idx, int32_t* __restrict__ ws_rhist) {
+  __shared__ int s_rhist[MOE_MAX_EXPERTS];
+  __shared__ int s_rank[kTilePairs];
+
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int tok0 = tile * tt;
+  const int np = min(tt, T - tok0) * k;
+  const int32_t* src = idx + (size_t)tok0 * k;
+
+  int v[kTilePairs / kThreads];
+#pragma unroll
+  for (int q = 0; q < kTilePairs / kThreads; ++q) {
+    const int p = q * kThreads + tid;
+    v[q] = p < np ? src[p] : -1;
+  }
+  for (int r = tid; r < R; r += kThreads) s_rhist[r] = 0;
+#pragma unroll
+  for (int q = 0; q < kTilePairs / kThreads; ++q) {
+    const int p = q * kThreads + tid;
+    const int e = clean_expert(v[q], E);
+    if (p < np) s_rank[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kTilePairs / kThreads; ++q) {
+    const int p = q * kThreads + tid;
+    if (p < np) {
+      const int tl = p / k, j = p - tl * k;
+      if (first_slot_of_rank(s_rank + tl * k, j) == j) atomicAdd(&s_rhist[s_rank[p]], 1);
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kThreads) ws_rhist[(size_t)tile * R + r] = s_rhist[r];
+}
+
+// ntiles == 1 (all pairs in one tile, one block): the block counts its own
+// pairs and no count pass runs. Otherwise one block per tile.
+__global__ __launch_bounds__(kThreads) void rank_place_kernel(
+    int T, int E, int k, int R, int epr, int epr_shift, int tt, int ntiles, int max_rows,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_rhist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ rank_row, int32_t* __restrict__ send_row,
+    int32_t* __restrict__ row_token) {
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_pre[MOE_MAX_EXPERTS];
+  __shared__ int s_cnt[kWaves][MOE_MAX_EXPERTS];
+  __shared__ int s_base[kWaves][MOE_MAX_EXPERTS];
+  __shared__ int s_wave[kWaves];
+  __shared__ int s_rank[kTilePairs];
+  __shared__ int s_row[kTilePairs];
+  __shared__ int s_stage[kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x;
+  const int tok0 = tile * tt;
+  const int np = tile < ntiles ? min(tt, T - tok0) * k : 0;
+  const size_t pair0 = (size_t)tok0 * k;
+  const bool self_count = ntiles <= 1;
+
+  int v[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    v[c] = p < np ? idx[pair0 + p] : -1;
+  }
+  const int hist_n = self_count ? 0 : ntiles * R;
+  int h[kStage / kThreads];
+  stage_load(h, ws_rhist, min(kStage, hist_n));
+
+  for (int r = tid; r < R; r += kThreads) {
+    s_tot[r] = 0;
+    s_pre[r] = 0;
+    for (int w = 0; w < kWaves; ++w) s_cnt[w][r] = 0;
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    const int e = clean_expert(v[c], E);
+    if (p < np) s_rank[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+  }
+  __syncthreads();
+
+  // key: the rank at the token's first slot on it, else -1
+  int key[kChunks], first[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    key[c] = -1;
+    first[c] = -1;
+    if (p < np) {
+      const int tl = p / k, j = p - tl * k;
+      first[c] = first_slot_of_rank(s_rank + tl * k, j);
+      if (first[c] == j) key[c] = s_rank[p];
+    }
+    if (self_count && key[c] >= 0) atomicAdd(&s_tot[key[c]], 1);
+  }
+
+  for (int c0 = 0; c0 < hist_n; c0 += kStage) {
+    const int n = min(kStage, hist_n - c0);
+    if (c0 > 0) stage_load(h, ws_rhist + c0, n);
+    __syncthreads();
+    stage_store(h, s_stage);
+    __syncthreads();
+    for (int r = tid; r < R; r += kThreads) column_sums(s_stage, c0, n, R, r, tile, &s_tot[r], &s_pre[r]);
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kThreads) s_off[r] = s_tot[r];
+  __syncthreads();
+  const int total = block_exclusive_scan(s_off, R, s_wave);
+  if (tid == 0) s_off[R] = total;
+  __syncthreads();
+  if (tile == 0) {
+    for (int r = tid; r < R; r += kThreads) {
+      counts[r] = s_tot[r];
+      offsets[r] = s_off[r];
+    }
+    if (tid == 0) offsets[R] = s_off[R];
+  }
+
+  const int nbits = ceil_log2(R);
+  uint64_t peers[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    peers[c] = peer_mask((uint32_t)key[c], key[c] >= 0, nbits);
+    if (key[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][key[c]], __popcll(peers[c]));
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kThreads) {
+    int run = s_pre[r];
+    for (int w = 0; w < kWaves; ++w) {
+      s_base[w][r] = run;
+      run += s_cnt[w][r];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    const int r = key[c];
+    int row = -1;
+    if (r >= 0) {
+      const int below = count_below(peers[c]);
+      row = s_off[r] + s_base[wave][r] + below;
+      if (below == 0) atomicAdd(&s_base[wave][r], __popcll(peers[c]));
+      s_row[p] = row;
+      if (row < max_rows) row_token[row] = tok0 + p / k;
+    }
+    if (p < np) send_row[pair0 + p] = row;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    if (p < np) rank_row[pair0 + p] = first[c] >= 0 ? s_row[(p / k) * k + first[c]] : -1;
+  }
+
+  // rows past the last (token, rank) row are marked -1
+  const int gwave = tile * kWaves + wave, nwaves = gridDim.x * kWaves;
+  for (int row = s_off[R] + gwave * MOE_WAVE + lane; row < max_rows; row += nwaves * MOE_WAVE)
+    row_token[row] = -1;
+}
+
 }  // namespace
 
 int layout_tile_tokens(int k) { return kTilePairs / k; }
@@ -395,6 +583,35 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
                      idx, ws_hist,
                      ws_rhist, expert_counts, expert_offsets, rank_counts, rank_offsets,
                      rank_token_counts, dst_row, src_pair, overflow);
+  return hipGetLastError();
+}
+
+
+
+size_t rank_layout_workspace_bytes(int T, int k, int R) {
+  return (size_t)layout_num_tiles(T, k) * (size_t)R * sizeof(int32_t);
+}
+
+hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
+                              int32_t* counts, int32_t* offsets, int32_t* rank_row,
+                              int32_t* send_row, int32_t* row_token, void* workspace,
+                              hipStream_t stream) {
+  const int tt = layout_tile_tokens(k);
+  const int ntiles = layout_num_tiles(T, k);
+  const int epr = E / R;
+  const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
+  const int max_rows = T * (k < R ? k : R);
+  int32_t* ws = static_cast<int32_t*>(workspace);
+  if (ntiles > 1) {
+    hipLaunchKernelGGL(rank_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
+                       T, E, k, R, epr, epr_shift, tt, idx, ws);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int blocks = ntiles > 1 ? ntiles : 1;
+  hipLaunchKernelGGL(rank_place_kernel, dim3(blocks), dim3(kThreads), 0, stream, T, E, k, R,
+                     epr, epr_shift, tt, ntiles, max_rows, idx, ws, counts, offsets, rank_row,
+                     send_row, row_token);
   return hipGetLastError();
 }
 

@@ -247,4 +247,120 @@ int moe_combine_backward(int num_tokens, int hidden, int top_k, int num_rows,
                   fn);
 }
 
+size_t moe_rank_layout_workspace_bytes(int num_tokens, int top_k, int num_ranks) {
+  if (num_tokens < 0 || top_k < 1 || top_k > MOE_MAX_TOPK || num_ranks < 1) return 0;
+  return moe::rank_layout_workspace_bytes(num_tokens, top_k, num_ranks);
+}
+
+int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
+                    const int32_t* topk_idx, int32_t* rank_token_counts,
+                    int32_t* rank_token_offsets, int32_t* rank_row, int32_t* send_row,
+                    int32_t* row_token, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "moe_rank_layout";
+  int st = check_topk(fn, num_tokens, num_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (num_ranks < 1 || num_ranks > num_experts || num_experts % num_ranks != 0)
+    return fail(MOE_ERR_INVALID, "%s: num_ranks=%d must divide num_experts=%d", fn, num_ranks,
+                num_experts);
+  if (!rank_token_counts || !rank_token_offsets)
+    return fail(MOE_ERR_INVALID, "%s: NULL rank_token_counts/rank_token_offsets", fn);
+  if (num_tokens > 0 && (!topk_idx || !rank_row || !send_row || !row_token))
+    return fail(MOE_ERR_INVALID, "%s: NULL topk_idx/rank_row/send_row/row_token", fn);
+  const void* ptrs[] = {topk_idx, rank_token_counts, rank_token_offsets, rank_row, send_row,
+                        row_token};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return fail(MOE_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+  const size_t need = moe::rank_layout_workspace_bytes(num_tokens, top_k, num_ranks);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace_bytes);
+  if (!aligned(workspace, 4)) return fail(MOE_ERR_INVALID, "%s: workspace not aligned", fn);
+  return from_hip(moe::launch_rank_layout(num_tokens, num_experts, top_k, num_ranks, topk_idx,
+                                          rank_token_counts, rank_token_offsets, rank_row,
+                                          send_row, row_token, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_rows,
+               const void* rank_rows, const void* rank_scales, const int32_t* rank_row,
+               int num_rows, const int32_t* src_pair, void* out, void* out_scales,
+               void* stream) {
+  const char* fn = "moe_expand";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
+  if (st != MOE_OK) return st;
+  if (num_rank_rows < 0) return fail(MOE_ERR_INVALID, "%s: num_rank_rows=%d < 0", fn, num_rank_rows);
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3 && dtype != MOE_DTYPE_MXFP8_E4M3)
+    return fail(MOE_ERR_INVALID, "%s: dtype=%d", fn, dtype);
+  const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3;
+  const bool mx = dtype == MOE_DTYPE_MXFP8_E4M3;
+  if (fp8 && hidden % MOE_FP8_BLOCK != 0)
+    return fail(MOE_ERR_INVALID, "%s: FP8 needs hidden %% %d == 0 (hidden=%d)", fn,
+                MOE_FP8_BLOCK, hidden);
+  if (mx && hidden % MOE_MX_BLOCK != 0)
+    return fail(MOE_ERR_INVALID, "%s: MXFP8 needs hidden %% %d == 0 (hidden=%d)", fn,
+                MOE_MX_BLOCK, hidden);
+  if (num_rows > 0 && (!src_pair || !out))
+    return fail(MOE_ERR_INVALID, "%s: NULL src_pair/out", fn);
+  if (num_rows > 0 && num_tokens > 0 && !rank_row)
+    return fail(MOE_ERR_INVALID, "%s: NULL rank_row", fn);
+  if (num_rank_rows > 0 && num_rows > 0 && !rank_rows)
+    return fail(MOE_ERR_INVALID, "%s: NULL rank_rows", fn);
+  if ((fp8 || mx) && num_rows > 0 && (!out_scales || (num_rank_rows > 0 && !rank_scales)))
+    return fail(MOE_ERR_INVALID, "%s: NULL scales", fn);
+  if (!fp8 && !mx && (rank_scales || out_scales))
+    return fail(MOE_ERR_INVALID, "%s: scales are for FP8 and MXFP8 only", fn);
+  if (!aligned(rank_rows, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID, "%s: rank_rows and out must be 16-byte aligned", fn);
+  const bool words = fp8 || (mx && (hidden / MOE_MX_BLOCK) % 4 == 0);
+  if (!aligned(rank_row, 4) || !aligned(src_pair, 4) ||
+      (words && (!aligned(rank_scales, 4) || !aligned(out_scales, 4))))
+    return fail(MOE_ERR_INVALID, "%s: index and scale buffers must be 4-byte aligned", fn);
+  return from_hip(moe::launch_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, rank_rows,
+                                     rank_scales, rank_row, num_rows, src_pair, out, out_scales,
+                                     static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_combine_local(int num_tokens, int hidden, int top_k, int num_rows,
+                      const void* expert_out_bf16, const int32_t* dst_row,
+                      const int32_t* rank_row, const float* topk_weights, int num_rank_rows,
+                      void* partial_bf16, void* stream) {
+  const char* fn = "moe_combine_local";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
+  if (st != MOE_OK) return st;
+  if (num_rank_rows < 0) return fail(MOE_ERR_INVALID, "%s: num_rank_rows=%d < 0", fn, num_rank_rows);
+  if (num_tokens > 0 && (!dst_row || !rank_row || !topk_weights))
+    return fail(MOE_ERR_INVALID, "%s: NULL dst_row/rank_row/topk_weights", fn);
+  if (num_rows > 0 && !expert_out_bf16) return fail(MOE_ERR_INVALID, "%s: NULL expert_out", fn);
+  if (num_rank_rows > 0 && !partial_bf16) return fail(MOE_ERR_INVALID, "%s: NULL partial", fn);
+  if (!aligned(expert_out_bf16, 16) || !aligned(partial_bf16, 16))
+    return fail(MOE_ERR_INVALID, "%s: expert_out and partial must be 16-byte aligned", fn);
+  if (!aligned(dst_row, 4) || !aligned(rank_row, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_INVALID, "%s: index/weight buffers must be 4-byte aligned", fn);
+  return from_hip(moe::launch_combine_local(num_tokens, hidden, top_k, num_rows, num_rank_rows,
+                                            expert_out_bf16, dst_row, rank_row, topk_weights,
+                                            partial_bf16, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_combine_partials(int num_tokens, int hidden, int top_k, int num_rank_rows,
+                         const void* partial_bf16, const int32_t* send_row, void* out_bf16,
+                         void* stream) {
+  const char* fn = "moe_combine_partials";
+  int st = check_rows(fn, num_tokens, hidden, top_k, num_rank_rows);
+  if (st != MOE_OK) return st;
+  if (num_tokens > 0 && (!send_row || !out_bf16))
+    return fail(MOE_ERR_INVALID, "%s: NULL send_row/out", fn);
+  if (num_rank_rows > 0 && !partial_bf16) return fail(MOE_ERR_INVALID, "%s: NULL partial", fn);
+  if (!aligned(partial_bf16, 16) || !aligned(out_bf16, 16))
+    return fail(MOE_ERR_INVALID, "%s: partial and out must be 16-byte aligned", fn);
+  if (!aligned(send_row, 4)) return fail(MOE_ERR_INVALID, "%s: send_row must be 4-byte aligned", fn);
+  return from_hip(moe::launch_combine(num_tokens, hidden, top_k, num_rank_rows, partial_bf16,
+                                      send_row, nullptr, out_bf16,
+                                      static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

@@ -244,6 +244,119 @@ int moe_combine_backward(int num_tokens, int hidden, int top_k, int num_rows,
                          const int32_t* dst_row, const float* topk_weights,
                          void* grad_expert_out_bf16, float* grad_weights, void* stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Deduplicated dispatch and hierarchical combine. The hyper.ai story on
+ * NVIDIA Hybrid-EP describes a combine that reduces hierarchically: first
+ * the results inside one destination, then across destinations. Here a
+ * destination is a rank (rank r owns experts [r*E/R, (r+1)*E/R); glossary
+ * "Expert Parallelism", "Le principe de base"). A token sends ONE row to
+ * each rank that holds at least one of its experts, however many of its
+ * experts live there; the rank fans the row out to its expert rows; after
+ * the experts it reduces the token's weighted outputs into one partial row;
+ * only the partial rows travel back, and each token sums its partials.
+ *
+ *   moe_rank_layout     (token, rank) rows: counts, offsets, maps
+ *   moe_dispatch        with dst_row = send_row and num_rows = T*min(k,R):
+ *                       one copy (bf16, FP8 or MXFP8) per (token, rank)
+ *   moe_expand          (token, rank) rows -> expert rows (rows of moe_layout)
+ *   ...experts...
+ *   moe_combine_local   expert rows -> one bf16 partial row per (token, rank)
+ *   moe_combine_partials  partial rows -> out[t]
+ *
+ * The result differs from moe_combine by the extra bf16 rounding of each
+ * partial (the partial travels as a bf16 row).
+ * ---------------------------------------------------------------------------
+ */
+
+/* Workspace bytes moe_rank_layout needs for these sizes (0 on bad sizes). */
+size_t moe_rank_layout_workspace_bytes(int num_tokens, int top_k, int num_ranks);
+
+/*
+ * moe_rank_layout -- rows of the (token, rank) buffer, one per token and
+ * rank holding at least one of the token's unmasked experts (capacity plays
+ * no part: the row exists by demand). Rank r's rows are
+ * [rank_token_offsets[r], rank_token_offsets[r+1]), in token order. The
+ * buffer is sized for its maximum, num_rank_rows = T * min(k, R), so that no
+ * count is read back before the dispatch (hyper.ai story on Hybrid-EP,
+ * preallocated buffers).
+ *
+ *   topk_idx           [T, k] int32; ids outside [0, E) are masked slots
+ *   rank_token_counts  [R]    int32 out: rows of rank r (its distinct tokens)
+ *   rank_token_offsets [R+1]  int32 out: exclusive prefix sum, [R] = total
+ *   rank_row           [T, k] int32 out: the (t, rank of slot j) row, for
+ *                      every unmasked slot; -1 for masked slots
+ *   send_row           [T, k] int32 out: rank_row at the token's first slot
+ *                      (in slot order) on each rank, -1 elsewhere: the
+ *                      destination map of the deduplicated moe_dispatch and
+ *                      the source map of moe_combine_partials
+ *   row_token          [T*min(k,R)] int32 out: token of each row, -1 past
+ *                      the last row
+ * Requires R to divide E. Deterministic; two launches (one when all T*k
+ * pairs fit in one tile of 1024 pairs).
+ */
+int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
+                    const int32_t* topk_idx, int32_t* rank_token_counts,
+                    int32_t* rank_token_offsets, int32_t* rank_row, int32_t* send_row,
+                    int32_t* row_token, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * moe_expand -- on the receiving rank, copy each (token, rank) row to the
+ * expert rows of that token on the rank:
+ *
+ *   out[q] = rank_rows[rank_row[src_pair[q]]]     for rows q with a pair
+ *
+ * (payload and, for FP8 / MXFP8, the scales; a byte copy). After the
+ * deduplicated dispatch this gives exactly the rows moe_dispatch writes with
+ * dst_row. Rows whose src_pair is -1 are left untouched.
+ *   dtype         MOE_DTYPE_* of the rows
+ *   rank_rows     [num_rank_rows, hidden] bf16 or e4m3 codes
+ *   rank_scales   FP8: fp32 [num_rank_rows, hidden/128]; MXFP8: uint8
+ *                 [num_rank_rows, hidden/32]; bf16: NULL
+ *   rank_row      [T, k] from moe_rank_layout
+ *   src_pair      [num_rows] from moe_layout (row -> t*k + j, -1 = none)
+ *   out, out_scales  [num_rows, ...] in the same formats
+ */
+int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_rows,
+               const void* rank_rows, const void* rank_scales, const int32_t* rank_row,
+               int num_rows, const int32_t* src_pair, void* out, void* out_scales,
+               void* stream);
+
+/*
+ * moe_combine_local -- first level of the hierarchical combine: for each
+ * (token, rank) row s,
+ *
+ *   partial[s, :] = bf16( sum over the token's slots j with rank_row[t,j] = s
+ *                         and a kept expert row of w[t,j] * y[dst_row[t,j], :] )
+ *
+ * in fp32 fused multiply-adds, slot order inside the row, one rounding to
+ * bf16 (nearest even). A row whose pairs were all dropped by capacity is
+ * written as +0. Rows of `partial` that no token owns are left untouched.
+ *   expert_out [num_rows, hidden] bf16;  dst_row [T, k] from moe_layout
+ *   rank_row   [T, k] from moe_rank_layout;  topk_weights [T, k] fp32
+ *   partial    [num_rank_rows, hidden] bf16
+ * Requires hidden % 8 == 0.
+ */
+int moe_combine_local(int num_tokens, int hidden, int top_k, int num_rows,
+                      const void* expert_out_bf16, const int32_t* dst_row,
+                      const int32_t* rank_row, const float* topk_weights, int num_rank_rows,
+                      void* partial_bf16, void* stream);
+
+/*
+ * moe_combine_partials -- second level: each token sums its partial rows,
+ *
+ *   out[t, :] = bf16( sum over j with send_row[t,j] >= 0 of partial[send_row[t,j], :] )
+ *
+ * fp32 sum in slot order, one rounding to bf16. A token with no row gets +0.
+ *   partial [num_rank_rows, hidden] bf16;  send_row [T, k] from moe_rank_layout
+ *   out     [num_tokens, hidden] bf16
+ * Requires hidden % 8 == 0.
+ */
+int moe_combine_partials(int num_tokens, int hidden, int top_k, int num_rank_rows,
+                         const void* partial_bf16, const int32_t* send_row, void* out_bf16,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

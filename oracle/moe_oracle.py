@@ -632,9 +632,11 @@ def combine_local(y_bits: np.ndarray, dst_row: np.ndarray, rank_row: np.ndarray,
             continue
         term = topk_w[keep, j].astype(F64)[:, None] * \
             bf16_to_f32(y_bits[dst_row[keep, j]]).astype(F64)
-        # each (token, rank) row appears at most once per slot column
-        np.add.at(acc, s[keep], term)
-        np.add.at(mag, s[keep], np.abs(term))
+        # a (token, rank) row appears at most once in one slot column (the
+        # rows of different tokens differ), so the indexed sums add each
+        # term once
+        acc[s[keep]] += term
+        mag[s[keep]] += np.abs(term)
     return round_to_bf16(acc), written, mag
 
 

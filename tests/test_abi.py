@@ -214,3 +214,95 @@ def test_dispatch_backward_rejects(kw, status):
     assert M.lib().moe_dispatch_backward(a["T"], a["H"], a["k"], a["rows"], a["g"], a["dst"],
                                          a["gx"], None) == status
     assert M.moe_last_error().startswith("moe_dispatch_backward")
+
+
+def _rank_layout(**kw):
+    _no_gpu()
+    a = dict(T=64, E=16, k=4, R=4, idx=A16, cnt=A16, off=A16, rr=A16, sr=A16, rt=A16,
+             ws=A16b, wsb=1 << 20)
+    a.update(kw)
+    return M.lib().moe_rank_layout(a["T"], a["E"], a["k"], a["R"], a["idx"], a["cnt"], a["off"],
+                                   a["rr"], a["sr"], a["rt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=3), M.MOE_ERR_INVALID),
+    (dict(R=32), M.MOE_ERR_INVALID),
+    (dict(R=0), M.MOE_ERR_INVALID),
+    (dict(k=17), M.MOE_ERR_INVALID),
+    (dict(E=1024), M.MOE_ERR_UNSUPPORTED),
+    (dict(cnt=None), M.MOE_ERR_INVALID),
+    (dict(sr=None), M.MOE_ERR_INVALID),
+    (dict(rt=A16 + 2), M.MOE_ERR_INVALID),
+    (dict(T=5000, wsb=4), M.MOE_ERR_WORKSPACE),
+    (dict(T=5000, ws=None), M.MOE_ERR_WORKSPACE),
+])
+def test_rank_layout_rejects(kw, status):
+    assert _rank_layout(**kw) == status
+    assert M.moe_last_error().startswith("moe_rank_layout")
+
+
+def test_rank_layout_workspace_bytes():
+    assert M.moe_rank_layout_workspace_bytes(0, 8, 32) == 0
+    assert M.moe_rank_layout_workspace_bytes(-1, 8, 32) == 0
+    assert M.moe_rank_layout_workspace_bytes(4096, 8, 32) == 32 * 32 * 4   # R ints per tile
+    assert M.moe_rank_layout_workspace_bytes(4097, 8, 32) == 33 * 32 * 4
+
+
+def _expand(**kw):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, dt=0, nrr=8, src=A16, ssc=None, rr=A16, rows=8, sp=A16,
+             out=A16b, osc=None)
+    a.update(kw)
+    return M.lib().moe_expand(a["T"], a["H"], a["k"], a["dt"], a["nrr"], a["src"], a["ssc"],
+                              a["rr"], a["rows"], a["sp"], a["out"], a["osc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), M.MOE_ERR_INVALID),
+    (dict(nrr=-1), M.MOE_ERR_INVALID),
+    (dict(H=12), M.MOE_ERR_INVALID),
+    (dict(dt=1, H=264, ssc=A16, osc=A16b), M.MOE_ERR_INVALID),   # FP8 needs H % 128
+    (dict(dt=1, ssc=None, osc=A16b), M.MOE_ERR_INVALID),
+    (dict(dt=2, ssc=A16, osc=None), M.MOE_ERR_INVALID),
+    (dict(dt=0, ssc=A16), M.MOE_ERR_INVALID),
+    (dict(dt=1, ssc=A16 + 2, osc=A16b), M.MOE_ERR_INVALID),
+    (dict(sp=None), M.MOE_ERR_INVALID),
+    (dict(src=None), M.MOE_ERR_INVALID),
+    (dict(out=A16b + 8), M.MOE_ERR_INVALID),
+])
+def test_expand_rejects(kw, status):
+    assert _expand(**kw) == status
+    assert M.moe_last_error().startswith("moe_expand")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=12), M.MOE_ERR_INVALID),
+    (dict(rr=None), M.MOE_ERR_INVALID),
+    (dict(w=None), M.MOE_ERR_INVALID),
+    (dict(part=None), M.MOE_ERR_INVALID),
+    (dict(nrr=-3), M.MOE_ERR_INVALID),
+    (dict(part=A16b + 4), M.MOE_ERR_INVALID),
+])
+def test_combine_local_rejects(kw, status):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, rows=8, y=A16, dst=A16, rr=A16, w=A16, nrr=8, part=A16b)
+    a.update(kw)
+    assert M.lib().moe_combine_local(a["T"], a["H"], a["k"], a["rows"], a["y"], a["dst"],
+                                     a["rr"], a["w"], a["nrr"], a["part"], None) == status
+    assert M.moe_last_error().startswith("moe_combine_local")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=4), M.MOE_ERR_INVALID),
+    (dict(sr=None), M.MOE_ERR_INVALID),
+    (dict(part=None), M.MOE_ERR_INVALID),
+    (dict(out=A16b + 2), M.MOE_ERR_INVALID),
+])
+def test_combine_partials_rejects(kw, status):
+    _no_gpu()
+    a = dict(T=4, H=256, k=2, nrr=8, part=A16, sr=A16, out=A16b)
+    a.update(kw)
+    assert M.lib().moe_combine_partials(a["T"], a["H"], a["k"], a["nrr"], a["part"], a["sr"],
+                                        a["out"], None) == status
+    assert M.moe_last_error().startswith("moe_combine_partials")
