@@ -1,6 +1,7 @@
 // Top-k and group-limited top-k routing on gfx950.
 //
-// One 64-lane wave per token; lane l holds experts l, l+64, l+128, ...
+// One 64-lane wave per token (lane l holds experts [l*VPL, l*VPL + VPL)),
+// or, for up to 128 experts, teams of 8 or 16 lanes per token.
 // Sources: hyper.ai story on NVIDIA Hybrid-EP (each token activates only k
 // experts); DeepEP article (ai-master.dev), section "Group-limited gating
 // algorithm" (the choice is restricted to a few expert groups); glossary
@@ -54,10 +55,33 @@ __device__ __forceinline__ void dpp_top2(float& m1, float& m2) {
   merge_top2(m1, m2, dpp_f32<CTRL>(m1), dpp_f32<CTRL>(m2));
 }
 
+// Loads the VPL consecutive values [e0, e0 + VPL) of `row` (zero past n),
+// with one or two 16-byte loads when `vec` says the row allows them.
+template <int VPL>
+__device__ __forceinline__ void load_slots(float (&v)[VPL], const float* __restrict__ row, int e0,
+                                           int n, bool vec) {
+  if (VPL >= 4 && vec && e0 + VPL <= n) {
+#pragma unroll
+    for (int h = 0; h < VPL; h += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(row + e0 + h);
+      v[h] = q.x;
+      v[h + 1] = q.y;
+      v[h + 2] = q.z;
+      v[h + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] = e0 + i < n ? row[e0 + i] : 0.0f;
+  }
+}
+
+// One wave per token; lane l holds the VPL consecutive experts
+// [l*VPL, l*VPL + VPL), so a group of gs experts spans gs/VPL neighbouring
+// lanes and, among equal keys, a lower lane always holds the lower expert.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(
     int T, int E, int k, const float* __restrict__ logits,
-    const float* __restrict__ bias, int sigmoid, int G, int kg,
+    const float* __restrict__ bias, int sigmoid, int G, int kg, int vec,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   __shared__ float s_key[kRouteWaves][MOE_MAX_EXPERTS];
 
@@ -65,111 +89,123 @@ __global__ __launch_bounds__(256) void route_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kRouteWaves + wave;
   const bool live = t < T;
+  const int e0 = lane * VPL;
 
+  float lg[VPL], bs[VPL];
+  load_slots<VPL>(lg, logits + (size_t)(live ? t : 0) * E, e0, live ? E : 0, vec);
+  if (bias != nullptr) load_slots<VPL>(bs, bias, e0, E, vec);
   float key[VPL], score[VPL];
   bool ok[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const int e = lane + 64 * i;
-    ok[i] = live && e < E;
-    const float l = ok[i] ? logits[(size_t)t * E + e] : 0.0f;
-    const float s = sigmoid ? (float)(1.0 / (1.0 + exp(-(double)l))) : l;
+    ok[i] = live && e0 + i < E;
+    const float s = sigmoid ? (float)(1.0 / (1.0 + exp(-(double)lg[i]))) : lg[i];
     score[i] = s;
-    key[i] = (bias != nullptr && ok[i]) ? s + bias[e] : s;
+    key[i] = (bias != nullptr && ok[i]) ? s + bs[i] : s;
   }
 
-  if (G > 1) {  // G is uniform over the block: the barriers below are safe
+  if (G > 1) {  // G is uniform over the block: the barrier below is safe
     const int gs = E / G;
-    float gscore = 0.0f;                // lane g < G: score of group g
-    if (gs == 16 || gs == 32 || gs == 64) {
-      // groups cover whole rows of one slot: top-2 per row with DPP, then
-      // the row and half swaps merge the rows of a group (16: none, 32: one
-      // swap, 64: two). Group scores are then spread so that lane g < G
-      // holds the score of group g.
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        float m1 = ok[i] ? key[i] : -INFINITY, m2 = -INFINITY;
-        dpp_top2<0xB1>(m1, m2);
-        dpp_top2<0x4E>(m1, m2);
-        dpp_top2<0x141>(m1, m2);
-        dpp_top2<0x140>(m1, m2);
-        if (gs >= 32) merge_top2(m1, m2, xor16_f32(m1), xor16_f32(m2));
-        if (gs == 64) merge_top2(m1, m2, xor32_f32(m1), xor32_f32(m2));
-        const float sc = m1 + m2;          // score of the group holding this lane, slot i
-        // group of (slot i, this lane) is (64 i + lane) / gs; lane g < G takes
-        // the score of group g from lane (g * gs - 64 i), which is in slot i
-        const int per_slot = 64 / gs;      // groups per slot
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q >= per_slot) break;
-          const float v = read_lane(sc, q * gs);
-          if (lane == i * per_slot + q) gscore = v;
-        }
-      }
-    } else {
+    const int lpg = gs / VPL;   // lanes per group
+    if (gs % VPL == 0 && (lpg & (lpg - 1)) == 0) {
+      // top-2 of the lane's slots, then of the group's lanes with DPP and
+      // the row and half swaps; every lane ends with its group's score
+      float m1 = -INFINITY, m2 = -INFINITY;
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
-        if (ok[i]) s_key[wave][lane + 64 * i] = key[i];
+        if (ok[i]) merge_top2(m1, m2, key[i], -INFINITY);
+      if (lpg >= 2) dpp_top2<0xB1>(m1, m2);
+      if (lpg >= 4) dpp_top2<0x4E>(m1, m2);
+      if (lpg >= 8) dpp_top2<0x141>(m1, m2);
+      if (lpg >= 16) dpp_top2<0x140>(m1, m2);
+      if (lpg >= 32) merge_top2(m1, m2, xor16_f32(m1), xor16_f32(m2));
+      if (lpg >= 64) merge_top2(m1, m2, xor32_f32(m1), xor32_f32(m2));
+      const float gscore = gs == 1 ? m1 : m1 + m2;
+      // rank of the lane's group (ties to the lower group); group q's score
+      // is in lane q*lpg
+      const int my_group = lane / lpg;
+      const uint32_t mine = ordered_bits(gscore);
+      int rank = 0;
+      for (int q = 0; q < G; ++q) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, q * lpg);
+        rank += (o > mine) || (o == mine && q < my_group);
+      }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) ok[i] = ok[i] && rank < kg;
+    } else {
+      // any group size: lane g < G scans its group in LDS
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (ok[i]) s_key[wave][e0 + i] = key[i];
       __syncthreads();
+      float gscore = 0.0f;
       if (live && lane < G) {
         float m1 = -INFINITY, m2 = -INFINITY;
         for (int q = 0; q < gs; ++q) merge_top2(m1, m2, s_key[wave][lane * gs + q], -INFINITY);
         gscore = gs == 1 ? m1 : m1 + m2;
       }
-    }
-    // rank of each group (ties to the lower group), then the kept set:
-    // lane g < G counts the groups that beat it
-    int rank = 0;
-    const uint32_t mine = ordered_bits(gscore);
-    for (int q = 0; q < G; ++q) {
-      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, q);
-      rank += (o > mine) || (o == mine && q < lane);
-    }
-    const uint64_t kept = wave_ballot(lane < G && rank < kg);
+      int rank = 0;
+      const uint32_t mine = ordered_bits(gscore);
+      for (int q = 0; q < G; ++q) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, q);
+        rank += (o > mine) || (o == mine && q < lane);
+      }
+      const uint64_t kept = wave_ballot(lane < G && rank < kg);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (ok[i]) ok[i] = (kept >> ((lane + 64 * i) / gs)) & 1ull;
+      for (int i = 0; i < VPL; ++i)
+        if (ok[i]) ok[i] = (kept >> ((e0 + i) / gs)) & 1ull;
+    }
   }
   if (!live) return;  // whole wave; no barrier follows
 
-  // Selection on 32-bit ordered keys (0 = taken or not allowed; every
-  // finite key maps above 0). Each step takes the wave max of the keys; the
-  // lowest lane holding it owns the winner unless another lane holds the
-  // same key, in which case the lowest expert index among them wins.
-  int my_e = -1;
-  float my_score = 0.0f;
-  uint32_t ok_key[VPL];
+  // The lane's candidates sorted by key, descending; equal keys keep slot
+  // order (adjacent swaps on strictly greater keys only). 0 = no candidate:
+  // every finite key maps above it.
+  uint32_t sk[VPL];
+  int sj[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) ok_key[i] = ok[i] ? ordered_bits(key[i]) : 0u;
-  for (int j = 0; j < k; ++j) {
-    uint32_t best = 0;
+  for (int i = 0; i < VPL; ++i) {
+    sk[i] = ok[i] ? ordered_bits(key[i]) : 0u;
+    sj[i] = i;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) best = max(best, ok_key[i]);
-    const uint32_t top = wave_max_u32(best);
-    // lowest slot of this lane holding the top key (VPL if none)
-    int slot = VPL;
-#pragma unroll
-    for (int i = VPL - 1; i >= 0; --i)
-      if (ok_key[i] == top) slot = i;
-    const uint64_t holders = wave_ballot(slot < VPL);
-    int e_win;
-    if ((holders & (holders - 1)) == 0) {          // one lane holds it
-      const int owner = (int)__builtin_ctzll(holders);
-      e_win = owner + 64 * __builtin_amdgcn_readlane(slot, owner);
-    } else {                                       // equal keys: lowest expert
-      const int e_mine = slot < VPL ? lane + 64 * slot : 0x7FFFFFFF;
-      e_win = (int)(0xFFFFFFFFu - wave_max_u32(0xFFFFFFFFu - (uint32_t)e_mine));
+    for (int p = i; p >= 1; --p) {
+      const bool up = sk[p] > sk[p - 1];
+      const uint32_t a = sk[p - 1], b = sk[p];
+      const int ja = sj[p - 1], jb = sj[p];
+      sk[p - 1] = up ? b : a;
+      sk[p] = up ? a : b;
+      sj[p - 1] = up ? jb : ja;
+      sj[p] = up ? ja : jb;
     }
-    const int owner = e_win & 63, wslot = e_win >> 6;
-    float sel = score[0];
+  }
+  // k rounds: the wave max of the lanes' heads wins; among lanes holding
+  // it the lowest lane, which holds the lowest expert; that lane pops.
+  int my_e = -1;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t top = wave_max_u32(sk[0]);
+    const uint64_t holders = wave_ballot(sk[0] == top);
+    const int owner = (int)__builtin_ctzll(holders);
+    const int e_win = owner * VPL + __builtin_amdgcn_readlane(sj[0], owner);
+    if (lane == owner) {
 #pragma unroll
-    for (int i = 1; i < VPL; ++i)
-      if (i == wslot) sel = score[i];
-    const float s_win = read_lane(sel, owner);
+      for (int p = 0; p + 1 < VPL; ++p) {
+        sk[p] = sk[p + 1];
+        sj[p] = sj[p + 1];
+      }
+      sk[VPL - 1] = 0u;
+    }
+    if (lane == j) my_e = e_win;
+  }
+  // score of the chosen expert, from the lane that holds it
+  float my_score = 0.0f;
+  {
+    const int e = my_e < 0 ? 0 : my_e;
+    const int src = e / VPL, slot = e - src * VPL;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (lane == owner && i == wslot) ok_key[i] = 0u;
-    if (lane == j) { my_e = e_win; my_score = s_win; }
+    for (int i = 0; i < VPL; ++i) {
+      const float v = __shfl(score[i], src);
+      if (i == slot) my_score = v;
+    }
   }
 
   double u;
@@ -364,14 +400,18 @@ hipError_t launch_route(int T, int E, int k, const float* logits, const float* b
     if (done) return hipGetLastError();
   }
   const dim3 grid((T + kRouteWaves - 1) / kRouteWaves), block(256);
-  if (E <= 64)
-    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out);
-  else if (E <= 128)
-    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out);
-  else if (E <= 256)
-    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out);
+  const int vpl = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8;
+  // 16-byte loads of a lane's slots: rows of whole 16-byte units, aligned
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const int vec = vpl >= 4 && E % vpl == 0 && a16(logits) && (bias == nullptr || a16(bias));
+  if (vpl == 1)
+    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
+  else if (vpl == 2)
+    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
+  else if (vpl == 4)
+    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
   else
-    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out);
+    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
   return hipGetLastError();
 }
 

@@ -97,6 +97,9 @@ __device__ __forceinline__ double dpp_f64(double v) {
 // swaps (checked on the device: permlane16_swap(v, v) returns v of the lane
 // itself and of the neighbouring row, in an order that depends on the row's
 // parity; permlane32_swap likewise for the two halves of the wave).
+// Keep the explicit select of the partner's element: a commutative op
+// applied directly to the two results (e.g. r[0] + r[1]) was compiled into
+// r[0] + r[0] by this toolchain when both operands are the same value.
 __device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return (lane_id() & 16) ? r[0] : r[1];
