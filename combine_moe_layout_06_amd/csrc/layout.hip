@@ -155,7 +155,12 @@ __device__ __forceinline__ void stage_store(const int (&h)[kStage / kThreads], i
 __device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, int W, int c,
                                             int limit, int* tot, int* pre) {
   int t = 0, p = 0;
-  for (int b = (c0 + W - 1 - c) / W; b * W + c < c0 + n; ++b) {
+  // rows b with c0 <= b*W + c < c0 + n; eight LDS reads in flight at a time
+  const int b0 = (c0 + W - 1 - c) / W;
+  const int nb = c0 + n - c > 0 ? (c0 + n - c + W - 1) / W - b0 : 0;
+#pragma unroll 8
+  for (int i = 0; i < nb; ++i) {
+    const int b = b0 + i;
     const int x = s_stage[b * W + c - c0];
     t += x;
     p += b < limit ? x : 0;
@@ -202,6 +207,12 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   const int hist_n = self_count ? 0 : ntiles * E;
   int h[kStage / kThreads];
   stage_load(h, ws_hist, min(kStage, hist_n));
+  // block 0 also sums the per-tile distinct-token counts: its first chunk
+  // is loaded now, with everything else
+  const bool sum_rtc = !self_count && tile == 0 && rank_token_counts != nullptr;
+  const int rn = sum_rtc ? ntiles * R : 0;
+  int hr[kStage / kThreads];
+  stage_load(hr, ws_rhist, min(kStage, rn));
 
   for (int e = tid; e < E; e += kThreads) {
     s_tot[e] = 0;
@@ -257,13 +268,12 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     for (int e = tid; e < E; e += kThreads) column_sums(s_stage, c0, n, E, e, tile, &s_tot[e], &s_pre[e]);
   }
   // block 0 also sums the per-tile distinct-token counts of each rank
-  if (!self_count && tile == 0 && rank_token_counts != nullptr) {
-    const int rn = ntiles * R;
+  if (sum_rtc) {
     for (int c0 = 0; c0 < rn; c0 += kStage) {
       const int n = min(kStage, rn - c0);
-      stage_load(h, ws_rhist + c0, n);
+      if (c0 > 0) stage_load(hr, ws_rhist + c0, n);
       __syncthreads();
-      stage_store(h, s_stage);
+      stage_store(hr, s_stage);
       __syncthreads();
       int unused = 0;
       for (int r = tid; r < R; r += kThreads) column_sums(s_stage, c0, n, R, r, 0, &s_rtc[r], &unused);
