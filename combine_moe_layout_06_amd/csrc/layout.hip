@@ -31,6 +31,7 @@ constexpr int kWaves = kThreads / MOE_WAVE;
 constexpr int kTilePairs = 1024;                          // pairs per tile (max)
 constexpr int kChunks = kTilePairs / kWaves / MOE_WAVE;   // 64-pair chunks per wave
 constexpr int kStage = 8192;                              // histogram ints staged per pass
+constexpr int kRankMaskWords = 256;                       // per-rank token bitmasks (one tile)
 
 __device__ __forceinline__ int clean_expert(int v, int E) {
   return (v >= 0 && v < E) ? v : -1;
@@ -170,8 +171,11 @@ __device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, i
 }
 
 // self_count: all pairs form one tile (T*k <= kTilePairs) and no count pass
-// ran; every block builds the histogram (and block 0 the distinct-token
-// counts) from topk_idx itself, so the layout takes a single launch.
+// ran. Every block loads all pairs and builds the histogram itself (block 0
+// also the distinct-token counts), so the layout takes a single launch; the
+// pairs are then loaded chunk-major (chunk c of wave w = pairs
+// [(4c + w)*64, +64)), and block b places chunk b only, after the pairs of
+// the chunks before it, so up to four blocks share the placement.
 __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
     int self_count, int num_rows,
@@ -190,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   __shared__ int s_wave[kWaves];
   __shared__ int s_overflow;
   __shared__ int s_stage[kStage];
+  __shared__ uint32_t s_rmask[kRankMaskWords];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;   // blocks at or past ntiles only fill unused rows
@@ -197,12 +202,18 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   const int np = tile < ntiles ? min(tt, T - tok0) * k : 0;
   const size_t pair0 = (size_t)tok0 * k;
 
-  // this tile's pairs and the first histogram chunk are loaded together
+  // this tile's pairs and the first histogram chunk are loaded together; in
+  // self_count mode every block loads all pairs (it needs their histogram)
+  const int np_load = self_count ? T * k : np;
+  const size_t base = self_count ? 0 : pair0;   // pair index of local pair 0
+  const auto pair_of = [&](int c) {
+    return self_count ? (c * kWaves + wave) * MOE_WAVE + lane : (wave * kChunks + c) * MOE_WAVE + lane;
+  };
   int v[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
-    v[c] = p < np ? idx[pair0 + p] : -1;
+    const int p = pair_of(c);
+    v[c] = p < np_load ? idx[base + p] : -1;
   }
   const int hist_n = self_count ? 0 : ntiles * E;
   int h[kStage / kThreads];
@@ -221,20 +232,40 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     for (int w = 0; w < kWaves; ++w) s_cnt[w][e] = 0;
   }
   if (tid == 0) s_overflow = 0;
+  // distinct tokens per rank as per-rank token bitmasks (one tile, small T*R)
+  const int mask_words = (T + 31) / 32;
+  const bool rank_masks = self_count && tile == 0 && rank_token_counts != nullptr &&
+                          R * mask_words <= kRankMaskWords;
+  if (rank_masks)
+    for (int i = tid; i < R * mask_words; i += kThreads) s_rmask[i] = 0u;
 
   if (self_count) {
-    // the only tile: histogram of all pairs, ranks of the pairs in LDS
-    const int np_all = T * k;
+    // the only tile: histogram of all pairs (already in v), and of the
+    // pairs before this block's chunk
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kTilePairs / kThreads; ++q) {
-      const int p = q * kThreads + tid;
-      const int e = p < np_all ? clean_expert(idx[p], E) : -1;
-      if (e >= 0) atomicAdd(&s_tot[e], 1);
-      if (p < np_all) s_stage[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+    for (int c = 0; c < kChunks; ++c) {
+      const int p = pair_of(c);
+      const int e = clean_expert(v[c], E);
+      if (e >= 0) {
+        atomicAdd(&s_tot[e], 1);
+        if (c < tile) atomicAdd(&s_pre[e], 1);
+        if (rank_masks) {
+          const int t = p / k;
+          atomicOr(&s_rmask[rank_of(e, epr, epr_shift) * mask_words + (t >> 5)], 1u << (t & 31));
+        }
+      }
+      if (p < np_load) s_stage[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+      if (c != tile) v[c] = -1;   // this block places chunk `tile` only
     }
     __syncthreads();
-    if (tile == 0 && rank_token_counts != nullptr) {
+    if (rank_masks) {
+      for (int r = tid; r < R; r += kThreads) {
+        int n = 0;
+        for (int i = 0; i < mask_words; ++i) n += __popc(s_rmask[r * mask_words + i]);
+        s_rtc[r] = n;
+      }
+    } else if (tile == 0 && rank_token_counts != nullptr) {
       for (int tl = tid; tl < T; tl += kThreads) {
         const int* r = s_stage + tl * k;
         if (R <= 64) {
@@ -330,9 +361,10 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     }
   }
   __syncthreads();
+  const int np_place = self_count ? (tile < kChunks ? np_load : 0) : np;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int p = (wave * kChunks + c) * MOE_WAVE + lane;
+    const int p = pair_of(c);
     const int e = v[c];
     int dst = -1;
     if (e >= 0) {
@@ -342,9 +374,9 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
       if (cap == 0) dst = s_off[e] + pos;
       else if (pos < cap) dst = e * cap + pos;
     }
-    if (p < np) {
-      dst_row[pair0 + p] = dst;
-      if (dst >= 0 && dst < num_rows) src_pair[dst] = (int32_t)(pair0 + p);
+    if (p < np_place && (!self_count || c == tile)) {
+      dst_row[base + p] = dst;
+      if (dst >= 0 && dst < num_rows) src_pair[dst] = (int32_t)(base + p);
     }
   }
 
@@ -587,7 +619,9 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   // padded buffers: enough waves that each fills the unused rows of about
   // one expert
   const int fill_blocks = cap > 0 ? (E + kWaves - 1) / kWaves : 1;
-  const int blocks = ntiles > fill_blocks ? ntiles : fill_blocks;
+  // one tile: one block per 256-pair chunk places it
+  const int place_blocks = self_count ? (T * k + kThreads - 1) / kThreads : ntiles;
+  const int blocks = place_blocks > fill_blocks ? place_blocks : fill_blocks;
   hipLaunchKernelGGL(layout_place_kernel, dim3(blocks), dim3(kThreads), 0,
                      stream, T, E, k, R, epr, epr_shift, cap, tt, ntiles, self_count, num_rows,
                      idx, ws_hist,
