@@ -306,3 +306,13 @@ def test_combine_partials_rejects(kw, status):
     assert M.lib().moe_combine_partials(a["T"], a["H"], a["k"], a["nrr"], a["part"], a["sr"],
                                         a["out"], None) == status
     assert M.moe_last_error().startswith("moe_combine_partials")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU only and says so (exit status 2)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr

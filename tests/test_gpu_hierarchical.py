@@ -347,3 +347,34 @@ def test_hierarchical_layer_end_to_end(name, seed):
     frac = assert_two_level_close(host(out, np.uint16), out_o, part_o, pmag, rl["send_row"], k,
                                   name)
     say("  two-level combine ok; bit-exact fraction %.6f" % frac)
+
+
+def test_hierarchical_pass_is_deterministic():
+    """Two runs of the whole pass on the same inputs give identical bits."""
+    w = W.WORKLOADS["dsv3"]
+    inp = W.make_inputs(w, 5, tokens=1500)
+    t, h, k = 1500, w.hidden, w.top_k
+    runs = []
+    for _ in range(2):
+        lb = LayerBuffers.allocate(t, h, w.experts, k, w.ranks, 0, dtype=M.MOE_DTYPE_FP8_E4M3)
+        rb = RankBuffers.allocate(t, h, w.experts, k, w.ranks, dtype=M.MOE_DTYPE_FP8_E4M3)
+        lb.route(dev(inp.logits), dev(inp.bias), w.score_fn, w.groups, w.topk_groups)
+        lb.layout()
+        rb.rank_layout(lb.topk_idx)
+        rb.dispatch(dev(inp.x))
+        rb.expand(lb)
+        y = lb.dispatched.view(torch.float8_e4m3fn).float().to(torch.bfloat16).view(torch.int16)
+        rb.combine_local(lb, y.contiguous())
+        out = torch.empty((t, h), dtype=torch.int16, device="cuda")
+        rb.combine_partials(out)
+        torch.cuda.synchronize()
+        runs.append([rb.rank_row.clone(), rb.send_row.clone(), rb.row_token.clone(),
+                     rb.sent.clone(), rb.sent_scales.clone(), lb.dispatched.clone(),
+                     rb.partial.clone(), out])
+    names = ["rank_row", "send_row", "row_token", "sent", "sent_scales", "expanded",
+             "partial", "out"]
+    for name, a, b in zip(names, runs[0], runs[1]):
+        if name in ("partial", "sent", "sent_scales"):   # compare the written rows only
+            rows = int(rb.rank_token_offsets[-1].item())
+            a, b = a[:rows], b[:rows]
+        assert torch.equal(a, b), name
