@@ -1,0 +1,84 @@
+"""GPU parity over the whole decode sequence: 1000 steps of 128 tokens
+(seeds 1000..1999), H=7168, E=256, k=8, group-limited routing, FP8 dispatch
+into capacity-128 buffers.
+
+Every step: expert choices (up to logged near-ties) and weights against the
+oracle, the whole layout bit for bit, and overflow 0 (capacity 128 = T, and a
+token sends at most one copy to an expert). Every 20th step also: the FP8
+rows and scales bit for bit and the combine within the combine bound.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+import combine_moe_layout_06_amd as M  # noqa: E402
+from combine_moe_layout_06_amd import LayerBuffers  # noqa: E402
+from gpu_helpers import assert_combine_close, assert_route_close, dev, host  # noqa: E402
+from oracle import moe_oracle as O  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_keys(logits, bias):
+    return O._selection_key(O._sigmoid_f32(logits), bias)
+
+
+def test_decode_sequence_every_step():
+    if not torch.cuda.is_available():
+        pytest.fail("the GPU tests need a visible MI355X")
+    w = W.WORKLOADS["decode"]
+    T, H, E, k, R, cap = w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity
+    assert w.steps == 1000
+    b = LayerBuffers.allocate(T, H, E, k, R, cap, dtype=M.MOE_DTYPE_FP8_E4M3)
+    near_ties = 0
+    for step in range(w.steps):
+        seed = w.step_seed0 + step
+        inp = W.make_inputs(w, seed)
+        b.route(dev(inp.logits), dev(inp.bias), w.score_fn, w.groups, w.topk_groups)
+        b.layout()
+        b.dispatch(dev(inp.x))
+        idx_g, w_g = host(b.topk_idx), host(b.topk_weights)
+        idx_o, w_o = O.route(inp.logits, k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+        near_ties += assert_route_close(idx_g, w_g, idx_o, w_o, oracle_keys(inp.logits, inp.bias),
+                                        "step %d" % step)
+        L = O.layout(idx_g, E, R, cap)
+        assert int(host(b.overflow)[0]) == 0 == int(L["overflow"][0]), step
+        for name in ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets",
+                     "rank_token_counts", "dst_row", "src_pair"):
+            got = host(getattr(b, name))
+            assert np.array_equal(got.reshape(L[name].shape), L[name]), (step, name)
+        if step % 20 == 0:
+            # the padded buffer has E*cap rows: check the written ones
+            # against their token's codes (one quantisation per token)
+            q, s = O.quantize_fp8_blocks(inp.x)
+            dst = L["dst_row"].reshape(-1)
+            live = dst >= 0
+            tok = np.repeat(np.arange(T), k)[live]
+            rows = dst[live]
+            rows_dev = torch.from_numpy(rows).long().cuda()
+            got_q = host(b.dispatched[rows_dev])        # only the written rows come back
+            got_s = host(b.scales[rows_dev])
+            assert np.array_equal(got_q, q[tok]), step
+            assert np.array_equal(got_s.view(np.uint32), s[tok].view(np.uint32)), step
+            # stand-in expert: dequantised rows; the oracle sums a compact
+            # per-pair copy of them (the same terms in the same slots)
+            y_tok = O.expert_dequant(q, s)
+            y_dev = torch.zeros((L["num_rows"], H), dtype=torch.int16, device="cuda")
+            y_dev[rows_dev] = dev(y_tok[tok])
+            b.combine(y_dev)
+            compact = np.where(L["dst_row"] >= 0, np.arange(T * k).reshape(T, k), -1)
+            y_pairs = y_tok[np.repeat(np.arange(T), k)]
+            want, mag = O.combine(y_pairs, compact.astype(np.int32), w_g)
+            assert_combine_close(host(b.combined, np.uint16), want, mag, k, "step %d" % step)
+        if step % 200 == 0:
+            say("decode step %d ok" % step)
+    say("1000 decode steps ok; near-tie tokens %d" % near_ties)
