@@ -19,6 +19,9 @@
 //      into offsets, and gives each pair its stable row. Inside a wave, the
 //      pairs of one expert are found with one ballot per expert-id bit and
 //      ranked by their lane order; waves of a tile are chained through LDS.
+// Every place block reads the whole [tiles, E] histogram (8192 ints per
+// staging pass), so the pass grows with tiles^2 * E over the grid: one
+// staging pass up to 8192 / E tiles (32 for E = 256, 1024 for E = 8).
 
 #include "kernels.h"
 #include "wave.h"
