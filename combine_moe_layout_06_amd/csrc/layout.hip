@@ -292,6 +292,20 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     }
   }
 
+  if (!self_count) __syncthreads();   // the LDS counters are zeroed
+
+  // pairs of one expert inside each wave (one ballot per expert-id bit) and
+  // the per-wave counts: they need no histogram, so they run while its loads
+  // are in flight
+  const int nbits = ceil_log2(E);
+  uint64_t peers[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    v[c] = clean_expert(v[c], E);
+    peers[c] = peer_mask((uint32_t)v[c], v[c] >= 0, nbits);
+    if (v[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][v[c]], __popcll(peers[c]));
+  }
+
   // per-expert totals and the base of this tile (sum over earlier tiles)
   for (int c0 = 0; c0 < hist_n; c0 += kStage) {
     const int n = min(kStage, hist_n - c0);
@@ -325,7 +339,11 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     __syncthreads();
   }
 
-  if (tile == 0) {
+  // the global counts: block 0 holds the distinct-token counts, the last
+  // block (which has no other extra work) writes the rest
+  if (tile == 0 && rank_token_counts != nullptr)
+    for (int r = tid; r < R; r += kThreads) rank_token_counts[r] = s_rtc[r];
+  if (tile == (int)gridDim.x - 1) {
     for (int e = tid; e < E; e += kThreads) {
       expert_counts[e] = s_tot[e];
       expert_offsets[e] = s_off[e];
@@ -338,24 +356,14 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
         rows += cap > 0 ? min(s_tot[e], cap) : s_tot[e];
       rank_counts[r] = rows;
       rank_offsets[r] = s_off[r * epr];
-      if (rank_token_counts != nullptr) rank_token_counts[r] = s_rtc[r];
     }
     if (tid == 0) rank_offsets[R] = s_off[E];
     __syncthreads();
     if (tid == 0) overflow[0] = s_overflow;
   }
 
-  // stable placement of this tile's pairs: count per wave, chain the waves,
-  // then rank inside each wave by lane order
-  const int nbits = ceil_log2(E);
-  uint64_t peers[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    v[c] = clean_expert(v[c], E);
-    peers[c] = peer_mask((uint32_t)v[c], v[c] >= 0, nbits);
-    if (v[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][v[c]], __popcll(peers[c]));
-  }
-  __syncthreads();
+  // stable placement of this tile's pairs: chain the waves' counts, then
+  // rank inside each wave by lane order
   for (int e = tid; e < E; e += kThreads) {
     int run = s_pre[e];
     for (int w = 0; w < kWaves; ++w) {
