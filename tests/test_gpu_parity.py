@@ -87,6 +87,19 @@ ROUTE_CASES = [
     # k above the team size falls back to one wave per token
     (300, 64, 10, 0, 1, 1, None, "normal"),
     (301, 40, 9, 1, 1, 1, "normal", "normal"),
+    # one wave per token, consecutive slots per lane: groups of 1, 8, 16 and
+    # 32 lanes, the LDS path, softmax with exact ties across and within
+    # lanes, rows that do not fill the last lane (scalar loads), G = 64
+    (257, 512, 32, 1, 64, 8, "normal", "normal"),
+    (150, 256, 8, 1, 64, 16, "normal", "normal"),
+    (210, 512, 16, 1, 8, 3, "normal", "normal"),
+    (200, 256, 6, 1, 4, 2, "int", "int"),
+    (180, 256, 4, 1, 2, 1, "normal", "normal"),
+    (190, 130, 5, 1, 13, 3, "normal", "normal"),
+    (300, 256, 8, 0, 1, 1, None, "normal"),
+    (250, 256, 8, 0, 1, 1, None, "int"),
+    (220, 512, 32, 0, 1, 1, "int", "int"),
+    (129, 131, 7, 1, 1, 1, "normal", "normal"),
 ]
 
 
