@@ -527,6 +527,15 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     }
     if (self_count && key[c] >= 0) atomicAdd(&s_tot[key[c]], 1);
   }
+  // per-wave ranking of the keys needs no histogram: it runs while the
+  // histogram loads are in flight
+  const int nbits = ceil_log2(R);
+  uint64_t peers[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    peers[c] = peer_mask((uint32_t)key[c], key[c] >= 0, nbits);
+    if (key[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][key[c]], __popcll(peers[c]));
+  }
 
   for (int c0 = 0; c0 < hist_n; c0 += kStage) {
     const int n = min(kStage, hist_n - c0);
@@ -550,14 +559,6 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     if (tid == 0) offsets[R] = s_off[R];
   }
 
-  const int nbits = ceil_log2(R);
-  uint64_t peers[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    peers[c] = peer_mask((uint32_t)key[c], key[c] >= 0, nbits);
-    if (key[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][key[c]], __popcll(peers[c]));
-  }
-  __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
     int run = s_pre[r];
     for (int w = 0; w < kWaves; ++w) {
