@@ -75,5 +75,20 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+ABI_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "moe_abi_check.cpp")
+ABI_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "moe_abi_check")
+
+
+def build_abi_check() -> str:
+    """Compile the stand-alone host program that checks the C ABI through
+    include/moe.h alone; it finds the library through its run path."""
+    _run([hipcc(), "--offload-arch=gfx950", "-O2", "-std=c++17", "-Wall",
+          "-Wno-unused-command-line-argument", "-I" + os.path.join(ROOT, "include"),
+          ABI_CHECK_SRC, "-L" + PKG, "-lmoe_layout",
+          "-Wl,-rpath,$ORIGIN/../../combine_moe_layout_06_amd", "-o", ABI_CHECK_BIN])
+    return ABI_CHECK_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_abi_check())
