@@ -4,7 +4,9 @@
 One step = one pass of the whole path over one batch of synthetic input:
 route (group-limited sigmoid top-k) -> layout (counts, offsets, stable
 rows) -> dispatch (FP8 e4m3 + per-1x128 scales) -> combine (weighted bf16
-sum). The stand-in expert between dispatch and combine is not part of the
+sum). Layout and dispatch go through moe_layout_dispatch, which is one
+launch for decode-sized inputs in capacity mode and the two launches
+otherwise. The stand-in expert between dispatch and combine is not part of the
 path: its output (dequantised rows) is prepared once before timing.
 
 Default workload: the DeepSeek-V3-shaped layer, T=4096 tokens, hidden 7168,
@@ -459,11 +461,13 @@ def main():
     buf = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                                   w.capacity, device=dev, dtype=dtype)
 
+    # layout + dispatch: one launch for decode-sized inputs in capacity mode
+    fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
+
     def front(i):
         d = inputs[i % len(inputs)]
         buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        buf.layout()
-        buf.dispatch(d["x"])
+        buf.layout_dispatch(d["x"])
 
     # stand-in expert output (harness): dequantised / scaled rows of step 0
     front(0)
@@ -500,8 +504,7 @@ def main():
         for i in range(steps):
             d = inputs[(warm + i) % len(inputs)]
             buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-            buf.layout()
-            buf.dispatch(d["x"])
+            buf.layout_dispatch(d["x"])
             buf.combine(y)
 
     if args.graph:
@@ -525,29 +528,34 @@ def main():
         wall = time.perf_counter() - t0
 
     # ---- the same steps again with HIP events between the phases (on the
-    # launch stream) for the per-phase times and the roofline
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    # launch stream) for the per-phase times and the roofline; layout and
+    # dispatch are one phase when they are one launch
+    if fused:
+        names = ["route", "layout_dispatch", "combine"]
+        calls = [lambda d: buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups),
+                 lambda d: buf.layout_dispatch(d["x"]), lambda d: buf.combine(y)]
+    else:
+        names = ["route", "layout", "dispatch", "combine"]
+        calls = [lambda d: buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups),
+                 lambda d: buf.layout(), lambda d: buf.dispatch(d["x"]),
+                 lambda d: buf.combine(y)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(steps)]
     for i in range(steps):
         d = inputs[(warm + i) % len(inputs)]
         e = ev[i]
         e[0].record()
-        buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        e[1].record()
-        buf.layout()
-        e[2].record()
-        buf.dispatch(d["x"])
-        e[3].record()
-        buf.combine(y)
-        e[4].record()
+        for j, call in enumerate(calls):
+            call(d)
+            e[j + 1].record()
     torch.cuda.synchronize()
 
-    names = ["route", "layout", "dispatch", "combine"]
     phase_ms = {n: 0.0 for n in names}
     step_ms = []
     for e in ev:
         for j, n in enumerate(names):
             phase_ms[n] += e[j].elapsed_time(e[j + 1]) / steps
-        step_ms.append(e[0].elapsed_time(e[4]))
+        step_ms.append(e[0].elapsed_time(e[-1]))
     ms_per_step = wall * 1e3 / steps
     value = w.tokens / (ms_per_step * 1e-3)
 
@@ -560,8 +568,7 @@ def main():
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        buf.layout()
-        buf.dispatch(d["x"])
+        buf.layout_dispatch(d["x"])
         buf.combine(y)
         e.record()
         torch.cuda.synchronize()

@@ -40,7 +40,8 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
             "moe_layout_workspace_bytes", "moe_layout", "moe_dispatch", "moe_combine",
             "moe_dispatch_backward", "moe_combine_backward",
             "moe_rank_layout_workspace_bytes", "moe_rank_layout", "moe_expand",
-            "moe_combine_local", "moe_combine_partials")
+            "moe_combine_local", "moe_combine_partials", "moe_layout_dispatch",
+            "moe_layout_dispatch_is_fused")
 
 _lib = None
 
@@ -90,6 +91,11 @@ def lib() -> ctypes.CDLL:
     L.moe_combine_local.restype = i32
     L.moe_combine_partials.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
     L.moe_combine_partials.restype = i32
+    L.moe_layout_dispatch.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, sz, i32, vp, i32, vp, vp, vp]
+    L.moe_layout_dispatch.restype = i32
+    L.moe_layout_dispatch_is_fused.argtypes = [i32, i32, i32]
+    L.moe_layout_dispatch_is_fused.restype = i32
     _lib = L
     return L
 
@@ -155,6 +161,24 @@ def moe_layout(num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
                             _ptr(rank_counts), _ptr(rank_offsets), _ptr(rank_token_counts),
                             _ptr(dst_row), _ptr(src_pair), _ptr(overflow), _ptr(workspace),
                             workspace_bytes, _stream(stream)))
+
+
+def moe_layout_dispatch_is_fused(num_tokens, top_k, capacity) -> bool:
+    return bool(lib().moe_layout_dispatch_is_fused(num_tokens, top_k, capacity))
+
+
+def moe_layout_dispatch(num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
+                        expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        rank_token_counts, dst_row, src_pair, overflow, workspace,
+                        workspace_bytes, hidden, x_bf16, out_dtype, out, out_scales,
+                        stream=None) -> None:
+    _check(lib().moe_layout_dispatch(num_tokens, num_experts, top_k, num_ranks, capacity,
+                                     _ptr(topk_idx), _ptr(expert_counts), _ptr(expert_offsets),
+                                     _ptr(rank_counts), _ptr(rank_offsets),
+                                     _ptr(rank_token_counts), _ptr(dst_row), _ptr(src_pair),
+                                     _ptr(overflow), _ptr(workspace), workspace_bytes, hidden,
+                                     _ptr(x_bf16), out_dtype, _ptr(out), _ptr(out_scales),
+                                     _stream(stream)))
 
 
 def moe_dispatch(num_tokens, hidden, top_k, num_rows, x_bf16, dst_row, out_dtype, out,

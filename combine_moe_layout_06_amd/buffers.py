@@ -13,7 +13,8 @@ from typing import Optional
 
 from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_FP8_BLOCK,
                MOE_MX_BLOCK, moe_combine, moe_combine_local, moe_combine_partials,
-               moe_dispatch, moe_expand, moe_layout, moe_layout_workspace_bytes,
+               moe_dispatch, moe_expand, moe_layout, moe_layout_dispatch,
+               moe_layout_workspace_bytes,
                moe_rank_layout, moe_rank_layout_workspace_bytes, moe_route)
 
 
@@ -102,6 +103,16 @@ class LayerBuffers:
     def dispatch(self, x, stream=None):
         moe_dispatch(self.tokens, self.hidden, self.top_k, self.num_rows, x, self.dst_row,
                      self.dtype, self.dispatched, self.scales, stream)
+
+    def layout_dispatch(self, x, stream=None):
+        """layout() then dispatch(x); one launch for decode-sized inputs in
+        capacity mode."""
+        moe_layout_dispatch(self.tokens, self.experts, self.top_k, self.ranks, self.capacity,
+                            self.topk_idx, self.expert_counts, self.expert_offsets,
+                            self.rank_counts, self.rank_offsets, self.rank_token_counts,
+                            self.dst_row, self.src_pair, self.overflow, self.workspace,
+                            self.workspace_bytes, self.hidden, x, self.dtype, self.dispatched,
+                            self.scales, stream)
 
     def combine(self, expert_out, stream=None):
         moe_combine(self.tokens, self.hidden, self.top_k, self.num_rows, expert_out,

@@ -1,317 +1,38 @@
-// Dispatch on gfx950: copy each token's hidden state to the rows of its k
-// experts, as bf16 or as FP8 e4m3 with one fp32 scale per 128 columns.
+// Dispatch kernels on gfx950: one 64-lane wave per (token, column part),
+// the destination rows from moe_layout (the device code is in
+// dispatch_body.h).
 //
 // Sources: glossary "Expert Parallelism" (polydesk.ai), "Le pattern de
-// communication all-to-all", Phase 1 (each token goes to the GPUs of its
-// experts); DeepEP article (ai-master.dev), "Kernels low-latency dispatch et
-// combine" (dispatch kernels that understand the MoE data and fuse steps),
-// "Support FP8 et MXFP8" (FP8 halves the BF16 volume) and "Configuration
-// type" (FP8 quantisation happens inside the dispatch call); hyper.ai story
-// on Hybrid-EP (native FP8/BF16 dispatch).
-//
-// One 64-lane wave per (token, column part). The token row is read once,
-// held in registers, and written to each destination row with 16-byte
-// (bf16) or 8-byte (FP8) nontemporal stores: every store instruction of a
-// wave covers whole 128-byte lines. FP8 quantises once per token; the
-// block amax is a 16-lane DPP max inside each 64-lane wave.
+// communication all-to-all", Phase 1; DeepEP article (ai-master.dev),
+// "Kernels low-latency dispatch et combine", "Support FP8 et MXFP8" and
+// "Configuration type"; hyper.ai story on Hybrid-EP (native FP8/BF16).
 
-#include "kernels.h"
-#include "wave.h"
+#include "dispatch_body.h"
 
 namespace moe {
 namespace {
-
-constexpr int kWavesPerBlock = 4;
-constexpr int kUnroll = 4;        // 16-byte chunks per lane held at once (bf16)
-constexpr int kScaleSlots = 4;    // FP8: scales of up to 256 blocks per part
 
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(
     int T, int k, int nch, int parts, int cpp, int num_rows,
     const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
     u32x4* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (gw >= T * parts) return;
-  const int t = gw / parts;
-  const int c0 = (gw - t * parts) * cpp;
-  const int cnt = min(cpp, nch - c0);
-  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const u32x4* src = x + (size_t)t * nch + c0;
-
-  for (int base = 0; base < cnt; base += MOE_WAVE * kUnroll) {
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = base + u * MOE_WAVE + lane;
-      v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (c < cnt) v[u] = stream_load(src + c);
-    }
-    for (int j = 0; j < k; ++j) {
-      const int d = read_lane(my_dst, j);
-      if (d < 0 || d >= num_rows) continue;
-      u32x4* dst = out + (size_t)d * nch + c0;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = base + u * MOE_WAVE + lane;
-        if (c < cnt) stream_store(v[u], dst + c);
-      }
-    }
-  }
+  dispatch_bf16_body(blockIdx.x, T, k, nch, parts, cpp, num_rows, x, DstRows{dst_row}, out);
 }
-
-// Max over the 16 lanes of each DPP row (lanes 16r .. 16r+15).
-__device__ __forceinline__ uint32_t row16_max(uint32_t m) {
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));  // row_mirror
-  return m;
-}
-
-// fp32 -> OCP e4m3fn code, round to nearest even, saturating at +-448.
-// The sign of zero is kept. `p` is finite or +-inf here.
-__device__ __forceinline__ uint32_t e4m3_from_f32(float p) {
-  const uint32_t b = __float_as_uint(p);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t a = b & 0x7FFFFFFFu;
-  uint32_t mag;
-  if (a > 0x43E00000u) {                 // above 448: saturate
-    mag = 0x7Eu;
-  } else if (a >= 0x3C800000u) {         // normal e4m3 range, >= 2^-6
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);   // RNE to 3 mantissa bits
-    mag = (r >> 20) - (120u << 3);                        // rebias exponent 127 -> 7
-  } else {                               // subnormal range: multiples of 2^-9
-    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return sign | mag;
-}
-
-// Quantise one bf16 element (held in the low 16 bits of `h`) in software.
-__device__ __forceinline__ uint32_t quant_one(uint32_t h, float inv) {
-  const float xv = __uint_as_float(h << 16);
-  if ((h & 0x7FFFu) == 0u) return (h >> 8) & 0x80u;       // +-0 keeps its sign
-  return e4m3_from_f32(xv * inv);
-}
-
-__device__ __forceinline__ uint32_t quant_pair_sw(uint32_t w, float inv) {
-  return quant_one(w & 0xFFFFu, inv) | (quant_one(w >> 16, inv) << 8);
-}
-
-// Two bf16 -> two e4m3 codes with the hardware pack-convert (round to
-// nearest even). Products are clamped to +-448 first; for every fp32 value
-// of magnitude <= 464 this gives the same code as e4m3_from_f32 (checked
-// exhaustively on the device). Needs a finite multiplier: then +-0 stays +-0.
-__device__ __forceinline__ uint32_t quant_pair_hw(uint32_t w, float inv) {
-  const float a = __builtin_amdgcn_fmed3f(__uint_as_float(w << 16) * inv, -448.0f, 448.0f);
-  const float b = __builtin_amdgcn_fmed3f(__uint_as_float(w & 0xFFFF0000u) * inv, -448.0f, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
-}
-
-// 8 bf16 (16 bytes) -> 8 codes (8 bytes)
-__device__ __forceinline__ u32x2 quant8(const u32x4& v, float inv) {
-  u32x2 q;
-  if (__builtin_isfinite(inv)) {
-    q[0] = quant_pair_hw(v[0], inv) | (quant_pair_hw(v[1], inv) << 16);
-    q[1] = quant_pair_hw(v[2], inv) | (quant_pair_hw(v[3], inv) << 16);
-  } else {   // the block's amax is so small that 448/amax overflows
-    q[0] = quant_pair_sw(v[0], inv) | (quant_pair_sw(v[1], inv) << 16);
-    q[1] = quant_pair_sw(v[2], inv) | (quant_pair_sw(v[3], inv) << 16);
-  }
-  return q;
-}
-
-// Block amax of the 16 lanes of a DPP row, from the bf16 magnitudes (their
-// bit patterns order like the values).
-__device__ __forceinline__ float block_amax(const u32x4& v) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t w = v[q] & 0x7FFF7FFFu;
-    m = max(m, max(w & 0xFFFFu, w >> 16));
-  }
-  return __uint_as_float(row16_max(m) << 16);
-}
-
-// One wave per (token, part of kFp8StepBlocks-block steps). A step covers
-// 1024 columns: lane L holds chunk A = columns [8L, 8L+8) and chunk B =
-// columns [512 + 8L, 512 + 8L + 8); the 16 lanes of a DPP row form one
-// 128-column block of A and one of B. After quantisation the lanes of a pair
-// (2i, 2i+1) swap halves, so lane 2i writes codes of A-columns [16i, 16i+16)
-// and lane 2i+1 those of B-columns [16i, 16i+16): one 16-byte store per lane
-// and copy.
-constexpr int kFp8StepBlocks = 8;
 
 __global__ __launch_bounds__(256) void dispatch_fp8_kernel(
     int T, int k, int H, int parts, int bpp, int num_rows,
     const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
     uint8_t* __restrict__ out, float* __restrict__ out_scales) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (gw >= T * parts) return;
-  const int t = gw / parts;
-  const int nb = H / MOE_FP8_BLOCK;
-  const int nch = H / 8;
-  const int b0 = (gw - t * parts) * bpp;
-  const int nbp = min(bpp, nb - b0);
-  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const int group = lane >> 4;       // block of A (and of B) inside the step
-  const int sub = lane & 15;         // 16-byte chunk inside the block
-  const bool odd = lane & 1;
-  const u32x4* src = x + (size_t)t * nch;
-
-  float sreg[kScaleSlots];
-#pragma unroll
-  for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0.0f;
-
-  for (int st = 0; st * kFp8StepBlocks < nbp; ++st) {
-    const int ba = st * kFp8StepBlocks + group;          // part-local blocks
-    const int bb = ba + kFp8StepBlocks / 2;
-    const bool act_a = ba < nbp, act_b = bb < nbp;
-    u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-    if (act_a) va = stream_load(src + (b0 + ba) * 16 + sub);
-    if (act_b) vb = stream_load(src + (b0 + bb) * 16 + sub);
-
-    const float amax_a = block_amax(va), amax_b = block_amax(vb);
-    const float scale_a = amax_a / 448.0f, scale_b = amax_b / 448.0f;
-    // lanes of a block past the part's end quantise with multiplier 1 (their
-    // codes are never stored), which keeps the whole wave on the fast path
-    const u32x2 qa = quant8(va, act_a ? 448.0f / amax_a : 1.0f);
-    const u32x2 qb = quant8(vb, act_b ? 448.0f / amax_b : 1.0f);
-
-    // swap halves inside lane pairs: even lanes keep A, odd lanes keep B
-    const u32x2 send = odd ? qa : qb;
-    u32x2 recv;
-    recv[0] = dpp_u32<0xB1>(send[0]);
-    recv[1] = dpp_u32<0xB1>(send[1]);
-    const u32x4 q = odd ? u32x4{recv[0], recv[1], qb[0], qb[1]}
-                        : u32x4{qa[0], qa[1], recv[0], recv[1]};
-    const int bq = odd ? bb : ba;                        // block this lane writes
-    const bool act_q = odd ? act_b : act_a;
-    const int col = (b0 + bq) * MOE_FP8_BLOCK + (sub & ~1) * 8;   // 16-byte aligned
-
-    // lane (b & 63), slot (b >> 6) keeps the scale of part-local block b
-#pragma unroll
-    for (int g = 0; g < kFp8StepBlocks; ++g) {
-      const int b = st * kFp8StepBlocks + g;
-      const float sg = read_lane(g < 4 ? scale_a : scale_b, (g & 3) * 16);
-      if (b < nbp && lane == (b & 63)) {
-#pragma unroll
-        for (int s = 0; s < kScaleSlots; ++s)
-          if ((b >> 6) == s) sreg[s] = sg;
-      }
-    }
-
-    for (int j = 0; j < k; ++j) {
-      const int d = read_lane(my_dst, j);
-      if (d < 0 || d >= num_rows) continue;
-      if (act_q) stream_store(q, reinterpret_cast<u32x4*>(out + (size_t)d * H + col));
-    }
-  }
-
-  for (int j = 0; j < k; ++j) {
-    const int d = read_lane(my_dst, j);
-    if (d < 0 || d >= num_rows) continue;
-    float* srow = out_scales + (size_t)d * nb + b0;
-#pragma unroll
-    for (int s = 0; s < kScaleSlots; ++s) {
-      const int b = s * 64 + lane;
-      if (b < nbp) srow[b] = sreg[s];
-    }
-  }
+  dispatch_fp8_body(blockIdx.x, T, k, H, parts, bpp, num_rows, x, DstRows{dst_row}, out,
+                    out_scales);
 }
-
-
-// MXFP8: one wave per (token, part); a step covers 512 columns = 16 blocks
-// of 32 columns, 4 lanes per block. The shared exponent comes from the
-// block amax (two DPP steps inside each quad); codes use the hardware
-// pack-convert of x * 2^-e clamped to +-448 (the multiplication by a power
-// of two is exact).
-constexpr int kMxStepBlocks = 16;
 
 __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(
     int T, int k, int H, int parts, int bpp, int num_rows,
     const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
     uint8_t* __restrict__ out, uint8_t* __restrict__ out_scales) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (gw >= T * parts) return;
-  const int t = gw / parts;
-  const int nb = H / MOE_MX_BLOCK;
-  const int nch = H / 8;
-  const int b0 = (gw - t * parts) * bpp;
-  const int nbp = min(bpp, nb - b0);
-  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const int blk = lane >> 2;         // block inside the step
-  const int sub = lane & 3;          // 16-byte chunk inside the block
-  const u32x4* src = x + (size_t)t * nch;
-
-  uint32_t sreg[kScaleSlots];        // E8M0 byte of part-local block (s*64 + lane)
-#pragma unroll
-  for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0u;
-
-  for (int st = 0; st * kMxStepBlocks < nbp; ++st) {
-    const int bl = st * kMxStepBlocks + blk;
-    const bool act = bl < nbp;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (act) v = stream_load(src + (b0 + bl) * 4 + sub);
-
-    uint32_t m = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = v[q] & 0x7FFF7FFFu;
-      m = max(m, max(w & 0xFFFFu, w >> 16));
-    }
-    m = max(m, dpp_u32<0xB1>(m));
-    m = max(m, dpp_u32<0x4E>(m));
-    const float amax = __uint_as_float(m << 16);
-    int e = amax == 0.0f ? -127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
-    e = min(max(e, -127), 127);
-    const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
-    u32x2 q;
-    q[0] = quant_pair_hw(v[0], inv) | (quant_pair_hw(v[1], inv) << 16);
-    q[1] = quant_pair_hw(v[2], inv) | (quant_pair_hw(v[3], inv) << 16);
-
-    // lane L keeps the byte of part-local block L + 64*slot: in step st the
-    // lanes of row (st % 4) receive block (st*16 + L % 16) from its first lane
-    const uint32_t sb = (uint32_t)(e + 127);
-    const uint32_t got = (uint32_t)__shfl((int)sb, 4 * (lane & 15));
-#pragma unroll
-    for (int s = 0; s < kScaleSlots; ++s)
-      if (st / 4 == s && (lane >> 4) == (st & 3)) sreg[s] = got;
-
-    if (act) {
-      for (int j = 0; j < k; ++j) {
-        const int d = read_lane(my_dst, j);
-        if (d < 0 || d >= num_rows) continue;
-        u32x2* dst = reinterpret_cast<u32x2*>(out + (size_t)d * H + (size_t)(b0 + bl) * MOE_MX_BLOCK) + sub;
-        stream_store(q, dst);
-      }
-    }
-  }
-
-  for (int j = 0; j < k; ++j) {
-    const int d = read_lane(my_dst, j);
-    if (d < 0 || d >= num_rows) continue;
-    uint8_t* srow = out_scales + (size_t)d * nb + b0;
-#pragma unroll
-    for (int s = 0; s < kScaleSlots; ++s) {
-      const int b = s * 64 + lane;
-      if (b < nbp) srow[b] = (uint8_t)sreg[s];
-    }
-  }
-}
-
-// Split a row of `units` into parts so that the launch has about
-// kTargetWaves waves, each part a multiple of `align` units (but at least
-// `min_units` and at most `max_units` units).
-void split_row(int T, int units, int align, int max_units, int* parts, int* per_part) {
-  int p = T > 0 ? (kTargetWaves + T - 1) / T : 1;
-  p = max(1, min(p, units / align));
-  int per = (units + p - 1) / p;
-  per = (per + align - 1) / align * align;
-  if (per > max_units) per = max_units;
-  *per_part = per;
-  *parts = (units + per - 1) / per;
+  dispatch_mxfp8_body(blockIdx.x, T, k, H, parts, bpp, num_rows, x, DstRows{dst_row}, out,
+                      out_scales);
 }
 
 }  // namespace

@@ -26,6 +26,17 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
                          int32_t* src_pair, int32_t* overflow, void* workspace,
                          hipStream_t stream);
 
+// Layout followed by dispatch; one launch when all pairs fit one tile in
+// capacity mode (layout_dispatch_fused), else the two launches above.
+bool layout_dispatch_fused(int T, int k, int cap);
+hipError_t launch_layout_dispatch(int T, int E, int k, int R, int cap, const int32_t* idx,
+                                  int32_t* expert_counts, int32_t* expert_offsets,
+                                  int32_t* rank_counts, int32_t* rank_offsets,
+                                  int32_t* rank_token_counts, int32_t* dst_row,
+                                  int32_t* src_pair, int32_t* overflow, void* workspace,
+                                  int H, const void* x, int dtype, void* out, void* out_scales,
+                                  hipStream_t stream);
+
 // (token, rank) rows of the deduplicated dispatch.
 size_t rank_layout_workspace_bytes(int T, int k, int R);
 hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,

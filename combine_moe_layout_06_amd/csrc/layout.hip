@@ -23,6 +23,7 @@
 // staging pass), so the pass grows with tiles^2 * E over the grid: one
 // staging pass up to 8192 / E tiles (32 for E = 256, 1024 for E = 8).
 
+#include "dispatch_body.h"
 #include "kernels.h"
 #include "wave.h"
 
@@ -179,7 +180,10 @@ __device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, i
 // pairs are then loaded chunk-major (chunk c of wave w = pairs
 // [(4c + w)*64, +64)), and block b places chunk b only, after the pairs of
 // the chunks before it, so up to four blocks share the placement.
-__global__ __launch_bounds__(kThreads) void layout_place_kernel(
+// Block `tile` of `nblocks` (the place kernel's blockIdx.x and gridDim.x, or
+// the layout blocks of the fused layout + dispatch launch).
+__device__ __forceinline__ void layout_place_body(
+    int tile, int nblocks,
     int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
     int self_count, int num_rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_hist,
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   __shared__ uint32_t s_rmask[kRankMaskWords];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x;   // blocks at or past ntiles only fill unused rows
+  // blocks at or past ntiles only fill unused rows
   const int tok0 = tile * tt;
   const int np = tile < ntiles ? min(tt, T - tok0) * k : 0;
   const size_t pair0 = (size_t)tok0 * k;
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   // block (which has no other extra work) writes the rest
   if (tile == 0 && rank_token_counts != nullptr)
     for (int r = tid; r < R; r += kThreads) rank_token_counts[r] = s_rtc[r];
-  if (tile == (int)gridDim.x - 1) {
+  if (tile == nblocks - 1) {
     for (int e = tid; e < E; e += kThreads) {
       expert_counts[e] = s_tot[e];
       expert_offsets[e] = s_off[e];
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
   }
 
   // rows that receive no pair are marked -1; all waves of the grid share it
-  const int gwave = tile * kWaves + wave, nwaves = gridDim.x * kWaves;
+  const int gwave = tile * kWaves + wave, nwaves = nblocks * kWaves;
   if (cap == 0) {
     for (int row = s_off[E] + gwave * MOE_WAVE + lane; row < num_rows; row += nwaves * MOE_WAVE)
       src_pair[row] = -1;
@@ -403,6 +407,53 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
         src_pair[row] = -1;
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void layout_place_kernel(
+    int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
+    int self_count, int num_rows,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_hist,
+    const int32_t* __restrict__ ws_rhist, int32_t* __restrict__ expert_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ rank_token_counts,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_pair,
+    int32_t* __restrict__ overflow) {
+  layout_place_body(blockIdx.x, gridDim.x, T, E, k, R, epr, epr_shift, cap, tt, ntiles,
+                    self_count, num_rows, idx, ws_hist, ws_rhist, expert_counts, expert_offsets,
+                    rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
+}
+
+// Fused layout + dispatch for one tile in capacity mode (decode-sized
+// inputs): blocks [0, nl) run the single-launch layout above, blocks from nl
+// on run the dispatch of DT (MOE_DTYPE_*), whose waves compute their token's
+// rows from the routing (DstCapacity) instead of waiting for dst_row. The
+// two halves share nothing, so they overlap completely.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
+    int nl, int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int num_rows,
+    const int32_t* __restrict__ idx, int32_t* __restrict__ expert_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ rank_token_counts,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_pair,
+    int32_t* __restrict__ overflow, int H, int parts, int per_part,
+    const u32x4* __restrict__ x, void* __restrict__ out, void* __restrict__ out_scales) {
+  if ((int)blockIdx.x < nl) {
+    layout_place_body(blockIdx.x, nl, T, E, k, R, epr, epr_shift, cap, tt, 1, 1, num_rows, idx,
+                      nullptr, nullptr, expert_counts, expert_offsets, rank_counts,
+                      rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
+    return;
+  }
+  const int b = blockIdx.x - nl;
+  const DstCapacity dst{idx, E, cap};
+  if (DT == MOE_DTYPE_BF16)
+    dispatch_bf16_body(b, T, k, H / 8, parts, per_part, num_rows, x, dst,
+                       static_cast<u32x4*>(out));
+  else if (DT == MOE_DTYPE_FP8_E4M3)
+    dispatch_fp8_body(b, T, k, H, parts, per_part, num_rows, x, dst,
+                      static_cast<uint8_t*>(out), static_cast<float*>(out_scales));
+  else
+    dispatch_mxfp8_body(b, T, k, H, parts, per_part, num_rows, x, dst,
+                        static_cast<uint8_t*>(out), static_cast<uint8_t*>(out_scales));
 }
 
 // ---------------------------------------------------------------------------
@@ -668,6 +719,65 @@ hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
   hipLaunchKernelGGL(rank_place_kernel, dim3(blocks), dim3(kThreads), 0, stream, T, E, k, R,
                      epr, epr_shift, tt, ntiles, max_rows, idx, ws, counts, offsets, rank_row,
                      send_row, row_token);
+  return hipGetLastError();
+}
+
+bool layout_dispatch_fused(int T, int k, int cap) {
+  return cap > 0 && T > 0 && T * k <= kTilePairs;
+}
+
+hipError_t launch_layout_dispatch(int T, int E, int k, int R, int cap, const int32_t* idx,
+                                  int32_t* expert_counts, int32_t* expert_offsets,
+                                  int32_t* rank_counts, int32_t* rank_offsets,
+                                  int32_t* rank_token_counts, int32_t* dst_row,
+                                  int32_t* src_pair, int32_t* overflow, void* workspace,
+                                  int H, const void* x, int dtype, void* out, void* out_scales,
+                                  hipStream_t stream) {
+  const int num_rows = cap > 0 ? E * cap : T * k;
+  if (!layout_dispatch_fused(T, k, cap)) {
+    hipError_t err = launch_layout(T, E, k, R, cap, idx, expert_counts, expert_offsets,
+                                   rank_counts, rank_offsets, rank_token_counts, dst_row,
+                                   src_pair, overflow, workspace, stream);
+    if (err != hipSuccess) return err;
+    if (dtype == MOE_DTYPE_FP8_E4M3)
+      return launch_dispatch_fp8(T, H, k, num_rows, x, dst_row, out,
+                                 static_cast<float*>(out_scales), stream);
+    if (dtype == MOE_DTYPE_MXFP8_E4M3)
+      return launch_dispatch_mxfp8(T, H, k, num_rows, x, dst_row, out,
+                                   static_cast<uint8_t*>(out_scales), stream);
+    return launch_dispatch_bf16(T, H, k, num_rows, x, dst_row, out, stream);
+  }
+  const int tt = layout_tile_tokens(k);
+  const int epr = E / R;
+  const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
+  // layout blocks as in the single-launch layout (capacity mode)
+  const int fill_blocks = (E + kWaves - 1) / kWaves;
+  const int place_blocks = (T * k + kThreads - 1) / kThreads;
+  const int nl = place_blocks > fill_blocks ? place_blocks : fill_blocks;
+  // dispatch blocks as in the dispatch launches
+  int parts, per_part;
+  if (dtype == MOE_DTYPE_FP8_E4M3)
+    split_row(T, H / MOE_FP8_BLOCK, kFp8StepBlocks, 64 * kScaleSlots, &parts, &per_part);
+  else if (dtype == MOE_DTYPE_MXFP8_E4M3)
+    split_row(T, H / MOE_MX_BLOCK, kMxStepBlocks, 64 * kScaleSlots, &parts, &per_part);
+  else
+    split_row(T, H / 8, MOE_WAVE, 1 << 30, &parts, &per_part);
+  const int nd = (T * parts + kWavesPerBlock - 1) / kWavesPerBlock;
+  const dim3 grid(nl + nd), block(kThreads);
+  const u32x4* xs = static_cast<const u32x4*>(x);
+#define MOE_LD_ARGS nl, T, E, k, R, epr, epr_shift, cap, tt, num_rows, idx, expert_counts, \
+    expert_offsets, rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow, \
+    H, parts, per_part, xs, out, out_scales
+  if (dtype == MOE_DTYPE_FP8_E4M3)
+    hipLaunchKernelGGL(layout_dispatch_kernel<MOE_DTYPE_FP8_E4M3>, grid, block, 0, stream,
+                       MOE_LD_ARGS);
+  else if (dtype == MOE_DTYPE_MXFP8_E4M3)
+    hipLaunchKernelGGL(layout_dispatch_kernel<MOE_DTYPE_MXFP8_E4M3>, grid, block, 0, stream,
+                       MOE_LD_ARGS);
+  else
+    hipLaunchKernelGGL(layout_dispatch_kernel<MOE_DTYPE_BF16>, grid, block, 0, stream,
+                       MOE_LD_ARGS);
+#undef MOE_LD_ARGS
   return hipGetLastError();
 }
 

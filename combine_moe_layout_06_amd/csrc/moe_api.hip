@@ -110,12 +110,15 @@ size_t moe_layout_workspace_bytes(int num_tokens, int num_experts, int top_k) {
   return moe::layout_workspace_bytes(num_tokens, num_experts, top_k);
 }
 
-int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int capacity,
-               const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
-               int32_t* rank_counts, int32_t* rank_offsets, int32_t* rank_token_counts,
-               int32_t* dst_row, int32_t* src_pair, int32_t* overflow, void* workspace,
-               size_t workspace_bytes, void* stream) {
-  const char* fn = "moe_layout";
+}  // extern "C"
+
+namespace {
+
+int check_layout(const char* fn, int num_tokens, int num_experts, int top_k, int num_ranks,
+                 int capacity, const int32_t* topk_idx, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                 int32_t* rank_token_counts, int32_t* dst_row, int32_t* src_pair,
+                 int32_t* overflow, void* workspace, size_t workspace_bytes) {
   int st = check_topk(fn, num_tokens, num_experts, top_k);
   if (st != MOE_OK) return st;
   if (num_ranks < 1 || num_ranks > num_experts || num_experts % num_ranks != 0)
@@ -140,17 +143,12 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int ca
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace_bytes);
   if (!aligned(workspace, 4)) return fail(MOE_ERR_INVALID, "%s: workspace not aligned", fn);
-  return from_hip(moe::launch_layout(num_tokens, num_experts, top_k, num_ranks, capacity,
-                                     topk_idx, expert_counts, expert_offsets, rank_counts,
-                                     rank_offsets, rank_token_counts, dst_row, src_pair,
-                                     overflow, workspace, static_cast<hipStream_t>(stream)),
-                  fn);
+  return MOE_OK;
 }
 
-int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows, const void* x_bf16,
-                 const int32_t* dst_row, int out_dtype, void* out, void* out_scales,
-                 void* stream) {
-  const char* fn = "moe_dispatch";
+int check_dispatch(const char* fn, int num_tokens, int hidden, int top_k, int num_rows,
+                   const void* x_bf16, const int32_t* dst_row, int out_dtype, void* out,
+                   void* out_scales) {
   int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
   if (st != MOE_OK) return st;
   if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_FP8_E4M3 &&
@@ -174,6 +172,72 @@ int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows, const void
     return fail(MOE_ERR_INVALID, "%s: x and out must be 16-byte aligned", fn);
   if (!aligned(dst_row, 4) || (fp8 && !aligned(out_scales, 4)))
     return fail(MOE_ERR_INVALID, "%s: dst_row/out_scales must be 4-byte aligned", fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int capacity,
+               const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
+               int32_t* rank_counts, int32_t* rank_offsets, int32_t* rank_token_counts,
+               int32_t* dst_row, int32_t* src_pair, int32_t* overflow, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_layout";
+  const int st = check_layout(fn, num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
+                              expert_counts, expert_offsets, rank_counts, rank_offsets,
+                              rank_token_counts, dst_row, src_pair, overflow, workspace,
+                              workspace_bytes);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_layout(num_tokens, num_experts, top_k, num_ranks, capacity,
+                                     topk_idx, expert_counts, expert_offsets, rank_counts,
+                                     rank_offsets, rank_token_counts, dst_row, src_pair,
+                                     overflow, workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_layout_dispatch_is_fused(int num_tokens, int top_k, int capacity) {
+  if (num_tokens < 0 || top_k < 1 || top_k > MOE_MAX_TOPK || capacity < 0) return 0;
+  return moe::layout_dispatch_fused(num_tokens, top_k, capacity) ? 1 : 0;
+}
+
+int moe_layout_dispatch(int num_tokens, int num_experts, int top_k, int num_ranks,
+                        int capacity, const int32_t* topk_idx, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                        int32_t* rank_token_counts, int32_t* dst_row, int32_t* src_pair,
+                        int32_t* overflow, void* workspace, size_t workspace_bytes, int hidden,
+                        const void* x_bf16, int out_dtype, void* out, void* out_scales,
+                        void* stream) {
+  const char* fn = "moe_layout_dispatch";
+  int st = check_layout(fn, num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
+                        expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        rank_token_counts, dst_row, src_pair, overflow, workspace,
+                        workspace_bytes);
+  if (st != MOE_OK) return st;
+  const long long rows = capacity > 0 ? (long long)num_experts * capacity
+                                      : (long long)num_tokens * top_k;
+  st = check_dispatch(fn, num_tokens, hidden, top_k, (int)rows, x_bf16, dst_row, out_dtype, out,
+                      out_scales);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_layout_dispatch(num_tokens, num_experts, top_k, num_ranks,
+                                              capacity, topk_idx, expert_counts, expert_offsets,
+                                              rank_counts, rank_offsets, rank_token_counts,
+                                              dst_row, src_pair, overflow, workspace, hidden,
+                                              x_bf16, out_dtype, out, out_scales,
+                                              static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows, const void* x_bf16,
+                 const int32_t* dst_row, int out_dtype, void* out, void* out_scales,
+                 void* stream) {
+  const char* fn = "moe_dispatch";
+  const int st = check_dispatch(fn, num_tokens, hidden, top_k, num_rows, x_bf16, dst_row,
+                                out_dtype, out, out_scales);
+  if (st != MOE_OK) return st;
+  const bool fp8 = out_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool mx = out_dtype == MOE_DTYPE_MXFP8_E4M3;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (fp8)

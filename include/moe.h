@@ -190,6 +190,37 @@ int moe_dispatch(int num_tokens, int hidden, int top_k, int num_rows,
                  void* out, void* out_scales, void* stream);
 
 /*
+ * moe_layout_dispatch -- moe_layout followed by moe_dispatch, with the same
+ * arguments and the same results (num_rows = E*capacity, or T*k packed).
+ * For decode-sized inputs in capacity mode (capacity > 0 and T*k <= 1024)
+ * it is ONE launch: the layout blocks and the dispatch blocks run side by
+ * side, the dispatch waves computing their token's rows from topk_idx by the
+ * layout's own definition (row e*cap + number of earlier pairs of expert e,
+ * dropped at cap) instead of waiting for dst_row. This is the low-latency
+ * path of the DeepEP article ("Kernels low-latency dispatch et combine":
+ * kernels that fuse the steps of the exchange) on buffers preallocated at
+ * their maximum size (hyper.ai story on Hybrid-EP). Otherwise it runs the
+ * layout launches, then the dispatch.
+ *
+ *   layout arguments:   as moe_layout
+ *   hidden, x_bf16, out_dtype, out, out_scales:   as moe_dispatch
+ * Errors: those of moe_layout and moe_dispatch, checked before anything is
+ * enqueued.
+ */
+/* 1 when moe_layout_dispatch takes one launch for these sizes, else 0. */
+int moe_layout_dispatch_is_fused(int num_tokens, int top_k, int capacity);
+
+int moe_layout_dispatch(int num_tokens, int num_experts, int top_k, int num_ranks,
+                        int capacity, const int32_t* topk_idx,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* rank_counts, int32_t* rank_offsets,
+                        int32_t* rank_token_counts, int32_t* dst_row,
+                        int32_t* src_pair, int32_t* overflow,
+                        void* workspace, size_t workspace_bytes,
+                        int hidden, const void* x_bf16, int out_dtype,
+                        void* out, void* out_scales, void* stream);
+
+/*
  * moe_combine -- bring each token's k expert outputs back and sum them
  * weighted by the router scores (glossary "Expert Parallelism", Phase 2).
  *

@@ -316,3 +316,26 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=3), M.MOE_ERR_INVALID),              # layout check
+    (dict(cap=-1), M.MOE_ERR_INVALID),
+    (dict(wsb=0, T=5000), M.MOE_ERR_WORKSPACE),
+    (dict(H=100), M.MOE_ERR_INVALID),            # dispatch check
+    (dict(dt=1, H=192, sc=A16), M.MOE_ERR_INVALID),
+    (dict(dt=1, sc=None), M.MOE_ERR_INVALID),
+    (dict(x=None), M.MOE_ERR_INVALID),
+    (dict(out=A16b + 4), M.MOE_ERR_INVALID),
+])
+def test_layout_dispatch_rejects(kw, status):
+    _no_gpu()
+    a = dict(T=64, E=16, k=4, R=4, cap=8, idx=A16, ec=A16, eo=A16, rc=A16, ro=A16, rtc=A16,
+             dst=A16, src=A16, ov=A16, ws=A16b, wsb=1 << 20, H=256, x=A16, dt=0, out=A16b,
+             sc=None)
+    a.update(kw)
+    assert M.lib().moe_layout_dispatch(a["T"], a["E"], a["k"], a["R"], a["cap"], a["idx"],
+                                       a["ec"], a["eo"], a["rc"], a["ro"], a["rtc"], a["dst"],
+                                       a["src"], a["ov"], a["ws"], a["wsb"], a["H"], a["x"],
+                                       a["dt"], a["out"], a["sc"], None) == status
+    assert M.moe_last_error().startswith("moe_layout_dispatch")
