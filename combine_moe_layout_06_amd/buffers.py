@@ -203,7 +203,7 @@ class RankBuffers:
 
 def run_layer(buf: LayerBuffers, logits, bias, x, score_fn, num_groups=1, topk_groups=1,
               stream: Optional[object] = None) -> None:
-    """Route, lay out and dispatch one layer pass (combine follows the experts)."""
+    """Route, lay out and dispatch one layer pass (combine follows the experts);
+    layout and dispatch go through moe_layout_dispatch."""
     buf.route(logits, bias, score_fn, num_groups, topk_groups, stream)
-    buf.layout(stream)
-    buf.dispatch(x, stream)
+    buf.layout_dispatch(x, stream)

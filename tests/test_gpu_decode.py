@@ -2,7 +2,8 @@
 (seeds 1000..1999), H=7168, E=256, k=8, group-limited routing, FP8 dispatch
 into capacity-128 buffers.
 
-Every step: expert choices (up to logged near-ties) and weights against the
+Layout and dispatch run as the single launch of moe_layout_dispatch. Every
+step: expert choices (up to logged near-ties) and weights against the
 oracle, the whole layout bit for bit, and overflow 0 (capacity 128 = T, and a
 token sends at most one copy to an expert). Every 20th step also: the FP8
 rows and scales bit for bit and the combine within the combine bound.
@@ -44,8 +45,7 @@ def test_decode_sequence_every_step():
         seed = w.step_seed0 + step
         inp = W.make_inputs(w, seed)
         b.route(dev(inp.logits), dev(inp.bias), w.score_fn, w.groups, w.topk_groups)
-        b.layout()
-        b.dispatch(dev(inp.x))
+        b.layout_dispatch(dev(inp.x))      # one launch at this size
         idx_g, w_g = host(b.topk_idx), host(b.topk_weights)
         idx_o, w_o = O.route(inp.logits, k, w.score_fn, w.groups, w.topk_groups, inp.bias)
         near_ties += assert_route_close(idx_g, w_g, idx_o, w_o, oracle_keys(inp.logits, inp.bias),

@@ -618,8 +618,8 @@ def test_combine_backward_parity(case):
 # ------------------------------------------------------------ graph replay
 
 def test_decode_steps_replay_in_a_graph():
-    """Three decode steps (route, layout, FP8 dispatch into capacity buffers,
-    combine) captured in one HIP graph; the graph is replayed three times with
+    """Three decode steps (route, layout + FP8 dispatch into capacity buffers
+    as one launch, combine) captured in one HIP graph; the graph is replayed three times with
     eager work and synchronisations between replays, and every replay must
     equal the eager run bit for bit."""
     w = W.WORKLOADS["decode"]
