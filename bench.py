@@ -327,15 +327,18 @@ def sha_of(paths):
     return h.hexdigest()
 
 
-def load_traffic():
+def load_traffic(algorithmic_bytes):
     """HBM bytes per combine launch from the committed counter summary, or
-    None when it is missing or was taken on a different kernel source."""
+    None when it is missing, was taken on a different kernel source, or on
+    a different workload (its algorithmic bytes differ)."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_sha256") != sha_of(COMBINE_SOURCES):
+        return None
+    if d.get("algorithmic_bytes_per_launch") != algorithmic_bytes:
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -579,7 +582,8 @@ def main():
     achieved = nbytes["combine"] / comb_s / 1e9
     roof = {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(), "algorithmic_bytes_per_launch": nbytes["combine"]}
+            "traffic": load_traffic(nbytes["combine"]),
+            "algorithmic_bytes_per_launch": nbytes["combine"]}
 
     out = {
         "metric": "dispatch+combine tokens/s and HBM GB/s (% of peak), DeepSeek-V3 shape, 1 GPU",
