@@ -22,6 +22,10 @@
 // Every place block reads the whole [tiles, E] histogram (8192 ints per
 // staging pass), so the pass grows with tiles^2 * E over the grid: one
 // staging pass up to 8192 / E tiles (32 for E = 256, 1024 for E = 8).
+//
+// Also here: the (token, rank) rows of the deduplicated dispatch
+// (rank_count_kernel, rank_place_kernel), and the fused layout + dispatch
+// launch for decode-sized inputs in capacity mode (layout_dispatch_kernel).
 
 #include "dispatch_body.h"
 #include "kernels.h"
