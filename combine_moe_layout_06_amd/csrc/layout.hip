@@ -9,8 +9,8 @@
 // sections "Megatron-LM (NVIDIA)" and "Défis et optimisations" (capacity
 // and token dropping).
 //
-// Two launches (one when all pairs fit in one tile), no global atomics,
-// deterministic:
+// Two launches (one when all pairs fit in one tile, three for many tiles), no
+// global atomics, deterministic:
 //   1. count: one block per tile of whole tokens builds the tile's expert
 //      histogram (and per-rank distinct-token counts) in LDS and writes it
 //      to the workspace.
@@ -21,7 +21,10 @@
 //      ranked by their lane order; waves of a tile are chained through LDS.
 // Every place block reads the whole [tiles, E] histogram (8192 ints per
 // staging pass), so the pass grows with tiles^2 * E over the grid: one
-// staging pass up to 8192 / E tiles (32 for E = 256, 1024 for E = 8).
+// staging pass up to 8192 / E tiles (32 for E = 256, 1024 for E = 8). For
+// many tiles a scan pass between the two (layout_scan_kernel) rewrites the
+// histogram as per-tile bases plus totals, and each place block reads only
+// its own row: linear in tiles * E.
 //
 // Also here: the (token, rank) rows of the deduplicated dispatch
 // (rank_count_kernel, rank_place_kernel), and the fused layout + dispatch
@@ -40,6 +43,14 @@ constexpr int kTilePairs = 1024;                          // pairs per tile (max
 constexpr int kChunks = kTilePairs / kWaves / MOE_WAVE;   // 64-pair chunks per wave
 constexpr int kStage = 8192;                              // histogram ints staged per pass
 constexpr int kRankMaskWords = 256;                       // per-rank token bitmasks (one tile)
+// A scan pass feeds the place pass from kScanMinTiles tiles on, or once the
+// histogram outgrows two staging passes (measured crossovers: ~96 tiles for
+// E = 256, ~200 for E = 8)
+constexpr int kScanMinTiles = 256;
+constexpr int kScanThreads = 1024;
+constexpr int kScanCols = 16;                             // histogram columns per scan block
+constexpr int kScanGroups = kScanThreads / kScanCols;     // row groups per scan block
+constexpr int kScanBatch = 16;                            // loads in flight per thread
 
 __device__ __forceinline__ int clean_expert(int v, int E) {
   return (v >= 0 && v < E) ? v : -1;
@@ -178,12 +189,67 @@ __device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, i
   *pre += p;
 }
 
+// Column scan of the per-tile histograms, for many tiles. Matrix `a`
+// ([ntiles, wa]) is replaced in place by its exclusive prefix over tiles (the
+// base of every tile) and its column totals go to a_tot; matrix `b`
+// ([ntiles, wb], nullable) only yields its column totals. Blocks [0, ga)
+// take 16 columns of a each, the others 16 columns of b. The 64 row groups of
+// a block (4 per wave: lane = group_in_wave * 16 + column) each own a run of
+// consecutive tiles, summed in one batch of loads; the groups' sums meet in
+// LDS, and a second pass rewrites the run as prefixes.
+__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
+    int ntiles, int wa, int ga, int32_t* __restrict__ a, int32_t* __restrict__ a_tot, int wb,
+    const int32_t* __restrict__ b, int32_t* __restrict__ b_tot) {
+  __shared__ int s_sum[kScanGroups][kScanCols];
+  const int tid = threadIdx.x;
+  const int col = tid & (kScanCols - 1), grp = tid / kScanCols;
+  const bool is_a = (int)blockIdx.x < ga;
+  const int W = is_a ? wa : wb;
+  const int32_t* m = is_a ? a : b;
+  const int c = (is_a ? (int)blockIdx.x : (int)blockIdx.x - ga) * kScanCols + col;
+  const bool live = c < W;
+  const int rpg = (ntiles + kScanGroups - 1) / kScanGroups;   // tiles per row group
+  const int r0 = min(grp * rpg, ntiles), r1 = min(r0 + rpg, ntiles);
+
+  int sum = 0;
+  for (int r = r0; r < r1; r += kScanBatch) {
+    int x[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) x[u] = live && r + u < r1 ? m[(size_t)(r + u) * W + c] : 0;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) sum += x[u];
+  }
+  s_sum[grp][col] = sum;
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int g = 0; g < kScanGroups; ++g) {
+    const int s = s_sum[g][col];
+    run += g < grp ? s : 0;
+    total += s;
+  }
+  if (!live) return;
+  if (grp == 0) (is_a ? a_tot : b_tot)[c] = total;
+  if (!is_a) return;
+  for (int r = r0; r < r1; r += kScanBatch) {
+    int x[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) x[u] = r + u < r1 ? a[(size_t)(r + u) * W + c] : 0;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      if (r + u < r1) a[(size_t)(r + u) * W + c] = run;
+      run += x[u];
+    }
+  }
+}
+
 // self_count: all pairs form one tile (T*k <= kTilePairs) and no count pass
 // ran. Every block loads all pairs and builds the histogram itself (block 0
 // also the distinct-token counts), so the layout takes a single launch; the
 // pairs are then loaded chunk-major (chunk c of wave w = pairs
 // [(4c + w)*64, +64)), and block b places chunk b only, after the pairs of
 // the chunks before it, so up to four blocks share the placement.
+// ws_tot != nullptr: the scan pass has run, ws_hist holds the base of every
+// tile and ws_tot / ws_rtot the totals, so the block reads its own row only.
 // Block `tile` of `nblocks` (the place kernel's blockIdx.x and gridDim.x, or
 // the layout blocks of the fused layout + dispatch launch).
 __device__ __forceinline__ void layout_place_body(
@@ -191,7 +257,8 @@ __device__ __forceinline__ void layout_place_body(
     int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
     int self_count, int num_rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_hist,
-    const int32_t* __restrict__ ws_rhist, int32_t* __restrict__ expert_counts,
+    const int32_t* __restrict__ ws_rhist, const int32_t* __restrict__ ws_tot,
+    const int32_t* __restrict__ ws_rtot, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ rank_token_counts,
     int32_t* __restrict__ dst_row, int32_t* __restrict__ src_pair,
@@ -226,21 +293,36 @@ __device__ __forceinline__ void layout_place_body(
     const int p = pair_of(c);
     v[c] = p < np_load ? idx[base + p] : -1;
   }
-  const int hist_n = self_count ? 0 : ntiles * E;
+  const bool scanned = ws_tot != nullptr;
+  const int hist_n = self_count || scanned ? 0 : ntiles * E;
   int h[kStage / kThreads];
   stage_load(h, ws_hist, min(kStage, hist_n));
   // block 0 also sums the per-tile distinct-token counts: its first chunk
   // is loaded now, with everything else
   const bool sum_rtc = !self_count && tile == 0 && rank_token_counts != nullptr;
-  const int rn = sum_rtc ? ntiles * R : 0;
+  const int rn = sum_rtc && !scanned ? ntiles * R : 0;
   int hr[kStage / kThreads];
   stage_load(hr, ws_rhist, min(kStage, rn));
+  // after a scan pass: this tile's bases and the totals, also loaded now
+  constexpr int kPerThread = MOE_MAX_EXPERTS / kThreads;
+  int pre0[kPerThread], tot0[kPerThread], rtc0[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = q * kThreads + tid;
+    pre0[q] = scanned && e < E && tile < ntiles ? ws_hist[(size_t)tile * E + e] : 0;
+    tot0[q] = scanned && e < E ? ws_tot[e] : 0;
+    rtc0[q] = scanned && sum_rtc && e < R ? ws_rtot[e] : 0;
+  }
 
-  for (int e = tid; e < E; e += kThreads) {
-    s_tot[e] = 0;
-    s_pre[e] = 0;
-    s_rtc[e] = 0;
-    for (int w = 0; w < kWaves; ++w) s_cnt[w][e] = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = q * kThreads + tid;
+    if (e < E) {
+      s_tot[e] = tot0[q];
+      s_pre[e] = pre0[q];
+      s_rtc[e] = rtc0[q];
+      for (int w = 0; w < kWaves; ++w) s_cnt[w][e] = 0;
+    }
   }
   if (tid == 0) s_overflow = 0;
   // distinct tokens per rank as per-rank token bitmasks (one tile, small T*R)
@@ -417,14 +499,16 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
     int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
     int self_count, int num_rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_hist,
-    const int32_t* __restrict__ ws_rhist, int32_t* __restrict__ expert_counts,
+    const int32_t* __restrict__ ws_rhist, const int32_t* __restrict__ ws_tot,
+    const int32_t* __restrict__ ws_rtot, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ rank_token_counts,
     int32_t* __restrict__ dst_row, int32_t* __restrict__ src_pair,
     int32_t* __restrict__ overflow) {
   layout_place_body(blockIdx.x, gridDim.x, T, E, k, R, epr, epr_shift, cap, tt, ntiles,
-                    self_count, num_rows, idx, ws_hist, ws_rhist, expert_counts, expert_offsets,
-                    rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
+                    self_count, num_rows, idx, ws_hist, ws_rhist, ws_tot, ws_rtot,
+                    expert_counts, expert_offsets, rank_counts, rank_offsets, rank_token_counts,
+                    dst_row, src_pair, overflow);
 }
 
 // Fused layout + dispatch for one tile in capacity mode (decode-sized
@@ -443,8 +527,8 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_kernel(
     const u32x4* __restrict__ x, void* __restrict__ out, void* __restrict__ out_scales) {
   if ((int)blockIdx.x < nl) {
     layout_place_body(blockIdx.x, nl, T, E, k, R, epr, epr_shift, cap, tt, 1, 1, num_rows, idx,
-                      nullptr, nullptr, expert_counts, expert_offsets, rank_counts,
-                      rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
+                      nullptr, nullptr, nullptr, nullptr, expert_counts, expert_offsets,
+                      rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
     return;
   }
   const int b = blockIdx.x - nl;
@@ -525,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void rank_count_kernel(
 __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     int T, int E, int k, int R, int epr, int epr_shift, int tt, int ntiles, int max_rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_rhist,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ ws_tot, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ rank_row, int32_t* __restrict__ send_row,
     int32_t* __restrict__ row_token) {
   __shared__ int s_tot[MOE_MAX_EXPERTS];
@@ -551,14 +635,29 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     const int p = (wave * kChunks + c) * MOE_WAVE + lane;
     v[c] = p < np ? idx[pair0 + p] : -1;
   }
-  const int hist_n = self_count ? 0 : ntiles * R;
+  // ws_tot != nullptr: the scan pass has run; ws_rhist holds the base of
+  // every tile, and the block reads its own row and the totals
+  const bool scanned = ws_tot != nullptr;
+  const int hist_n = self_count || scanned ? 0 : ntiles * R;
   int h[kStage / kThreads];
   stage_load(h, ws_rhist, min(kStage, hist_n));
+  constexpr int kPerThread = MOE_MAX_EXPERTS / kThreads;
+  int pre0[kPerThread], tot0[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int r = q * kThreads + tid;
+    pre0[q] = scanned && r < R ? ws_rhist[(size_t)tile * R + r] : 0;
+    tot0[q] = scanned && r < R ? ws_tot[r] : 0;
+  }
 
-  for (int r = tid; r < R; r += kThreads) {
-    s_tot[r] = 0;
-    s_pre[r] = 0;
-    for (int w = 0; w < kWaves; ++w) s_cnt[w][r] = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int r = q * kThreads + tid;
+    if (r < R) {
+      s_tot[r] = tot0[q];
+      s_pre[r] = pre0[q];
+      for (int w = 0; w < kWaves; ++w) s_cnt[w][r] = 0;
+    }
   }
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
@@ -658,9 +757,18 @@ int layout_num_tiles(int T, int k) {
   return (T + tt - 1) / tt;
 }
 
+// Many tiles: a scan pass turns the per-tile counts ([ntiles, W]) into
+// per-tile bases, so that a place block reads one row instead of the whole
+// histogram.
+static bool layout_scans(int ntiles, int W) {
+  return ntiles >= kScanMinTiles || (long long)ntiles * W > 2 * kStage;
+}
+
 size_t layout_workspace_bytes(int T, int E, int k) {
-  // per tile: E expert counts + up to E rank counts
-  return (size_t)layout_num_tiles(T, k) * (size_t)(2 * E) * sizeof(int32_t);
+  // per tile: E expert counts + up to E rank counts; with a scan pass also
+  // the E expert and up to E rank totals
+  const size_t tiles = (size_t)layout_num_tiles(T, k);
+  return (tiles + (layout_scans((int)tiles, E) ? 1 : 0)) * (size_t)(2 * E) * sizeof(int32_t);
 }
 
 hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx,
@@ -677,11 +785,22 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   int32_t* ws_rhist = rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
   const int self_count = T * k <= kTilePairs ? 1 : 0;
+  const bool scan = !self_count && layout_scans(ntiles, E);
+  int32_t* ws_tot = scan ? ws_hist + (size_t)2 * ntiles * E : nullptr;
+  int32_t* ws_rtot = scan && ws_rhist != nullptr ? ws_tot + E : nullptr;
   if (ntiles > 0 && !self_count) {
     hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
                        T, E, k, R, epr, epr_shift, tt, idx, ws_hist, ws_rhist);
-    const hipError_t err = hipGetLastError();
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (scan) {
+      const int ga = (E + kScanCols - 1) / kScanCols;
+      const int gb = ws_rhist != nullptr ? (R + kScanCols - 1) / kScanCols : 0;
+      hipLaunchKernelGGL(layout_scan_kernel, dim3(ga + gb), dim3(kScanThreads), 0, stream,
+                         ntiles, E, ga, ws_hist, ws_tot, R, ws_rhist, ws_rtot);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   // padded buffers: enough waves that each fills the unused rows of about
   // one expert
@@ -691,16 +810,17 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   const int blocks = place_blocks > fill_blocks ? place_blocks : fill_blocks;
   hipLaunchKernelGGL(layout_place_kernel, dim3(blocks), dim3(kThreads), 0,
                      stream, T, E, k, R, epr, epr_shift, cap, tt, ntiles, self_count, num_rows,
-                     idx, ws_hist,
-                     ws_rhist, expert_counts, expert_offsets, rank_counts, rank_offsets,
-                     rank_token_counts, dst_row, src_pair, overflow);
+                     idx, ws_hist, ws_rhist, ws_tot, ws_rtot, expert_counts, expert_offsets,
+                     rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
   return hipGetLastError();
 }
 
 
 
 size_t rank_layout_workspace_bytes(int T, int k, int R) {
-  return (size_t)layout_num_tiles(T, k) * (size_t)R * sizeof(int32_t);
+  // per tile: R counts; with a scan pass also the R totals
+  const size_t tiles = (size_t)layout_num_tiles(T, k);
+  return (tiles + (layout_scans((int)tiles, R) ? 1 : 0)) * (size_t)R * sizeof(int32_t);
 }
 
 hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
@@ -713,16 +833,26 @@ hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
   const int max_rows = T * (k < R ? k : R);
   int32_t* ws = static_cast<int32_t*>(workspace);
+  const bool scan = ntiles > 1 && layout_scans(ntiles, R);
+  int32_t* ws_tot = scan ? ws + (size_t)ntiles * R : nullptr;
   if (ntiles > 1) {
     hipLaunchKernelGGL(rank_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
                        T, E, k, R, epr, epr_shift, tt, idx, ws);
-    const hipError_t err = hipGetLastError();
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (scan) {
+      hipLaunchKernelGGL(layout_scan_kernel, dim3((R + kScanCols - 1) / kScanCols),
+                         dim3(kScanThreads), 0, stream, ntiles, R,
+                         (R + kScanCols - 1) / kScanCols, ws, ws_tot, 0,
+                         static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   const int blocks = ntiles > 1 ? ntiles : 1;
   hipLaunchKernelGGL(rank_place_kernel, dim3(blocks), dim3(kThreads), 0, stream, T, E, k, R,
-                     epr, epr_shift, tt, ntiles, max_rows, idx, ws, counts, offsets, rank_row,
-                     send_row, row_token);
+                     epr, epr_shift, tt, ntiles, max_rows, idx, ws, ws_tot, counts, offsets,
+                     rank_row, send_row, row_token);
   return hipGetLastError();
 }
 

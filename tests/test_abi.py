@@ -171,6 +171,10 @@ def test_workspace_bytes():
     # one tile per 1024 pairs, 2*E ints per tile
     assert M.moe_layout_workspace_bytes(4096, 256, 8) == 32 * 2 * 256 * 4
     assert M.moe_layout_workspace_bytes(4097, 256, 8) == 33 * 2 * 256 * 4
+    # past 64 tiles of E = 256: one more row for the totals of the scan pass
+    assert M.moe_layout_workspace_bytes(8192, 256, 8) == 64 * 2 * 256 * 4
+    assert M.moe_layout_workspace_bytes(8193, 256, 8) == 66 * 2 * 256 * 4
+    assert M.moe_layout_workspace_bytes(131072, 8, 2) == 256 * 2 * 8 * 4 + 2 * 8 * 4
 
 
 def test_binding_raises_with_message():
@@ -247,6 +251,8 @@ def test_rank_layout_workspace_bytes():
     assert M.moe_rank_layout_workspace_bytes(-1, 8, 32) == 0
     assert M.moe_rank_layout_workspace_bytes(4096, 8, 32) == 32 * 32 * 4   # R ints per tile
     assert M.moe_rank_layout_workspace_bytes(4097, 8, 32) == 33 * 32 * 4
+    assert M.moe_rank_layout_workspace_bytes(32640, 8, 32) == 255 * 32 * 4
+    assert M.moe_rank_layout_workspace_bytes(32768, 8, 32) == 257 * 32 * 4
 
 
 def _expand(**kw):

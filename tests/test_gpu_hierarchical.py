@@ -84,6 +84,12 @@ RANK_CASES = [
     (1, 512, 32, 16, True, 0.0),
     (0, 8, 2, 4, True, 0.0),             # empty
     (777, 20, 6, 5, True, 1.0),          # every slot masked
+    # many tiles: from 256 tiles (or a histogram over two staging passes) a
+    # scan pass feeds the place pass
+    (8191, 256, 8, 32, True, 0.0),       # 64 tiles, ragged: staged
+    (32773, 256, 8, 32, True, 0.0),      # 257 tiles, ragged: scanned
+    (131073, 8, 2, 4, False, 0.05),      # 257 tiles of 512 tokens
+    (2100, 512, 32, 512, True, 0.0),     # 66 tiles, 512 ranks: scanned
 ]
 
 

@@ -170,6 +170,15 @@ LAYOUT_CASES = [
     (0, 8, 2, 4, 0, True, 0.0),             # empty, packed
     (0, 8, 2, 4, 3, True, 0.0),             # empty, capacity
     (777, 20, 6, 5, 50, True, 1.0),         # every slot masked
+    # many tiles: up to 64 tiles of E = 256 the place blocks stage the whole
+    # histogram, beyond that (or from 256 tiles) a scan pass feeds them
+    (8191, 256, 8, 32, 0, True, 0.0),       # 64 tiles, ragged: staged
+    (8300, 256, 8, 32, 0, True, 0.0),       # 65 tiles, ragged: scanned
+    (65613, 256, 8, 32, 0, True, 0.02),     # 513 tiles, masked slots
+    (131073, 8, 2, 4, 0, True, 0.0),        # 257 tiles of 512 tokens
+    (70000, 64, 4, 8, 4300, False, 0.1),    # 274 tiles, capacity with drops
+    (2100, 512, 32, 512, 0, True, 0.05),    # 66 tiles, 512 ranks
+    (2100, 512, 32, 16, 5, True, 0.0),      # more fill blocks than tiles
 ]
 
 
@@ -212,9 +221,10 @@ def test_layout_ignores_out_of_range_ids():
         assert np.array_equal(val, want[name].reshape(val.shape)), name
 
 
-def test_layout_without_rank_token_counts():
+@pytest.mark.parametrize("t,k", [(900, 4), (33000, 8)], ids=["staged", "scanned"])
+def test_layout_without_rank_token_counts(t, k):
     g = np.random.Generator(np.random.PCG64(5))
-    idx = W.random_topk_idx(g, 900, 32, 4)
+    idx = W.random_topk_idx(g, t, 32, k)
     got = gpu_layout(idx, 32, 8, 0, with_rtc=False)
     want = O.layout(idx, 32, 8, 0)
     for name, val in got.items():
