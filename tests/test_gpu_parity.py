@@ -170,6 +170,9 @@ LAYOUT_CASES = [
     (0, 8, 2, 4, 0, True, 0.0),             # empty, packed
     (0, 8, 2, 4, 3, True, 0.0),             # empty, capacity
     (777, 20, 6, 5, 50, True, 1.0),         # every slot masked
+    (4097, 256, 8, 32, 0, True, 0.0),       # one token past 32 tiles
+    (4000, 96, 8, 48, 0, True, 0.0),        # R not a power of two, E/R = 2
+    (32768, 512, 1, 512, 0, True, 0.0),     # k = 1, 512 ranks
     # many tiles: up to 64 tiles of E = 256 the place blocks stage the whole
     # histogram, beyond that (or from 256 tiles) a scan pass feeds them
     (8191, 256, 8, 32, 0, True, 0.0),       # 64 tiles, ragged: staged
