@@ -16,10 +16,11 @@ in HBM when timing starts.
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      HBM roofline of the dominant kernel (combine): algorithmic
-                bytes per launch / average launch time from HIP events
-                recorded on the launch stream; `traffic` comes from the
-                committed rocprofv3 counter summary when it was taken on the
-                current kernel source, else null
+                bytes per launch / average launch time, from HIP events on
+                the launch stream around 20 back-to-back launches (no event
+                between launches, so it matches the profiler's kernel time);
+                `traffic` comes from the committed rocprofv3 counter summary
+                when it was taken on the current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
   phases_us     average per-phase times from HIP events, taken in a second
                 pass over the same steps (the timed loop itself has no events)
@@ -43,7 +44,25 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_traffic.json")
 COMBINE_SOURCES = [os.path.join(ROOT, "combine_moe_layout_06_amd", "csrc", f)
-                   for f in ("combine.hip", "wave.h")]
+                   for f in ("combine.hip", "wave.h", "kernels.h")]
+ROOF_REPS = 20   # back-to-back launches timed for the roofline kernel
+
+
+def launch_us(torch, fn, reps=ROOF_REPS):
+    """Average duration of one launch of `fn`: HIP events on the current
+    (launch) stream around `reps` back-to-back launches, so that no event
+    sits between two launches."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps * 1e3
+
+
+def roofline_timing():
+    return "HIP events around %d back-to-back launches on the launch stream" % ROOF_REPS
 
 
 def parse():
@@ -146,7 +165,9 @@ def run_backward(args, w, M, W, torch, np):
     nb = backward_bytes(w, rows_live)
     ms = wall * 1e3 / args.steps
     total = sum(nb.values())
-    achieved = nb["combine_backward"] / cb / 1e9
+    cb_us = launch_us(torch, lambda: M.moe_combine_backward(T, H, k, rows, dout, y, buf.dst_row,
+                                                             buf.topk_weights, dy, dw))
+    achieved = nb["combine_backward"] / (cb_us * 1e-6) / 1e9
     print(json.dumps({
         "metric": "backward dispatch+combine tokens/s and HBM GB/s, %s shape, 1 GPU" % w.name,
         "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -162,7 +183,8 @@ def run_backward(args, w, M, W, torch, np):
         "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": nb["combine_backward"]},
+                     "algorithmic_bytes_per_launch": nb["combine_backward"],
+                     "launch_us": round(cb_us, 2), "timing": roofline_timing()},
         "cpu_baseline": None}), flush=True)
 
 
@@ -260,7 +282,8 @@ def run_hierarchical(args, w, M, W, torch, np):
     ms = wall * 1e3 / args.steps
     total = sum(nb.values())
     dom = max(("dispatch", "expand", "combine_local", "combine_partials"), key=lambda n: ph[n])
-    achieved = nb[dom] / (ph[dom] * 1e-6) / 1e9
+    dom_us = launch_us(torch, calls(args.warmup)[phases.index(dom)])
+    achieved = nb[dom] / (dom_us * 1e-6) / 1e9
     row = (H if dtype else 2 * H) + scale_bytes(H, dtype)
     out = {
         "metric": "hierarchical dispatch+combine tokens/s, %s shape, 1 GPU" % w.name,
@@ -283,7 +306,8 @@ def run_hierarchical(args, w, M, W, torch, np):
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": nb[dom]},
+                     "algorithmic_bytes_per_launch": nb[dom],
+                     "launch_us": round(dom_us, 2), "timing": roofline_timing()},
         "cpu_baseline": None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_hierarchical(w, args.seed, args.cpu_seconds, dtype)
@@ -578,12 +602,13 @@ def main():
         cold.append(s.elapsed_time(e))
     del flush
 
-    comb_s = phase_ms["combine"] * 1e-3
-    achieved = nbytes["combine"] / comb_s / 1e9
+    comb_us = launch_us(torch, lambda: buf.combine(y))
+    achieved = nbytes["combine"] / (comb_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(nbytes["combine"]),
-            "algorithmic_bytes_per_launch": nbytes["combine"]}
+            "algorithmic_bytes_per_launch": nbytes["combine"],
+            "launch_us": round(comb_us, 2), "timing": roofline_timing()}
 
     out = {
         "metric": "dispatch+combine tokens/s and HBM GB/s (% of peak), DeepSeek-V3 shape, 1 GPU",

@@ -81,4 +81,16 @@ hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void
 #endif
 constexpr int kTargetWaves = MOE_TARGET_WAVES;
 
+// Occupancy caps. A streaming kernel that fills each CU with as many waves as
+// its registers allow can keep far more HBM requests in flight than the
+// memory needs, and then runs slower: the extra queued reads and writes
+// turn the bus around more often. A launch caps its workgroups per CU by
+// reserving dynamic LDS that the kernel never touches (gfx950: 160 KiB of
+// LDS per CU). Dynamic LDS bytes that leave room for at most `blocks`
+// workgroups on a CU; 0 = no cap.
+constexpr int kLdsPerCu = 160 * 1024;
+inline size_t lds_cap_bytes(int blocks) {
+  return blocks > 0 ? (size_t)(kLdsPerCu / (blocks + 1) + 1024) : 0;
+}
+
 }  // namespace moe
