@@ -74,8 +74,9 @@ hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void
                                    const void* y, const int32_t* dst_row, const float* w,
                                    void* dy, float* dw, hipStream_t stream);
 
-// Number of waves a row-parallel kernel aims for: about four times the
-// 256 CUs x 32 wave slots, so that short waves keep every CU busy to the end.
+// Number of waves a row-parallel kernel aims for: several times what the
+// 256 CUs hold at once (8 to 32 waves each, by kernel), so that short waves
+// keep every CU busy to the end.
 #ifndef MOE_TARGET_WAVES
 #define MOE_TARGET_WAVES 32768
 #endif
