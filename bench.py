@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -343,11 +344,20 @@ def cpu_baseline_hierarchical(w, seed, budget_s, dtype):
                       "in %.1f s (numpy, single thread)" % (w.name, ts, w.tokens, reps, el)}
 
 
+def code_only(text):
+    """C/C++ source text without comments and whitespace, so that edits to
+    comments or layout leave the source hash unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def sha_of(paths):
+    """SHA-256 over the code (comments and whitespace removed) of `paths`."""
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()
 
 
