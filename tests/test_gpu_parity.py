@@ -630,6 +630,26 @@ def test_combine_backward_parity(case):
 
 # ------------------------------------------------------------ graph replay
 
+def test_binding_enqueues_on_torch_current_stream():
+    """Calls without a stream argument go to torch's current stream, also
+    inside a `torch.cuda.stream` block."""
+    assert M._stream(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert M._stream(None) == side.cuda_stream
+        # and the work really lands there: a combine ordered after a fill
+        # on the side stream sees the filled rows
+        y = torch.zeros((4, 8), dtype=torch.int16, device="cuda")
+        dst = torch.arange(4, dtype=torch.int32, device="cuda").view(4, 1)
+        w = torch.ones((4, 1), dtype=torch.float32, device="cuda")
+        out = torch.zeros((4, 8), dtype=torch.int16, device="cuda")
+        y.fill_(0x3F80)                       # bf16 1.0
+        M.moe_combine(4, 8, 1, 4, y, dst, w, out)
+    side.synchronize()
+    assert (out == 0x3F80).all()
+    assert M._stream(None) == torch.cuda.current_stream().cuda_stream
+
+
 def test_decode_steps_replay_in_a_graph():
     """Three decode steps (route, layout + FP8 dispatch into capacity buffers
     as one launch, combine) captured in one HIP graph; the graph is replayed three times with
