@@ -14,7 +14,10 @@ experts per token, and a fraction of masked slots. It then checks:
   - moe_combine on random rows and weights, within the combine bound;
   - the hierarchical pass (rank layout, send, fan-out, per-rank partials,
     their sum): rows bit for bit, partials within the combine bound, the
-    final sum within the two-level bound.
+    final sum within the two-level bound;
+  - the backward pair on the draw's layout: row gradients within one bf16
+    ulp, weight gradients within the dot-product bound, dx within the
+    combine bound (computed by the oracle from the GPU's row gradients).
 """
 
 import sys
@@ -27,8 +30,8 @@ torch = pytest.importorskip("torch")
 
 import combine_moe_layout_06_amd as M  # noqa: E402
 from combine_moe_layout_06_amd import LayerBuffers, RankBuffers  # noqa: E402
-from gpu_helpers import (assert_combine_close, assert_route_close, dev, host,  # noqa: E402
-                         poison_like)
+from gpu_helpers import (assert_bf16_within_ulp, assert_combine_close,  # noqa: E402
+                         assert_route_close, dev, dot_tolerance, host, poison_like)
 from oracle import moe_oracle as O  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
@@ -202,3 +205,37 @@ def test_hierarchical_pass(seed):
     ref, mag = O.combine_partials(part_g, RL["send_row"])
     assert_combine_close(host(out, np.uint16)[:T], ref, mag, min(k, R), "sum %d" % seed)
     say("  ok: rows sent", int(RL["rank_token_offsets"][-1]))
+
+
+@pytest.mark.parametrize("seed", range(1, N_CASES, 2))
+def test_backward_pair(seed):
+    c = draw(seed)
+    T, E, k, R, cap, H = c["T"], c["E"], c["k"], c["R"], c["cap"], c["H"]
+    say("random backward case", seed, c)
+    g = W.rng(70000 + seed)
+    idx = W.random_topk_idx(g, T, E, k, distinct=c["distinct"], mask_frac=c["mask"])
+    L = O.layout(idx, E, R, cap)
+    rows, dst = L["num_rows"], L["dst_row"]
+    dout = W.random_bf16_rows(g, T, H)
+    y = W.random_bf16_rows(g, max(rows, 1), H)
+    w = W.random_weights(g, T, k)
+    dy_full = poison_like((max(rows, 1), H), torch.int16)
+    dw_full = poison_like((max(T, 1), k), torch.float32)
+    dx_full = poison_like((max(T, 1), H), torch.int16)
+    live_in = (lambda a: dev(a)) if T else (lambda a: None)
+    M.moe_combine_backward(T, H, k, rows, live_in(dout), dev(y), live_in(dst), live_in(w),
+                           dy_full, dw_full)
+    M.moe_dispatch_backward(T, H, k, rows, dy_full, live_in(dst), dx_full)
+    if T == 0:
+        return
+    dy = host(dy_full, np.uint16)
+    dw = host(dw_full)[:T]
+    want_dy, written, want_dw, dw_abs = O.combine_backward(dout, y, dst, w, rows)
+    assert np.all(dy[:rows][~written] == 0xFFFF)          # rows of no pair stay untouched
+    assert_bf16_within_ulp(dy[:rows][written], want_dy[written], "case %d dy" % seed)
+    live = dst >= 0
+    assert np.all(dw[~live] == 0.0)
+    err = np.abs(dw.astype(np.float64) - want_dw.astype(np.float64))
+    assert np.all(err <= dot_tolerance(H, want_dw.astype(np.float64), dw_abs))
+    want_dx, mag = O.dispatch_backward(dy[:max(rows, 1)], dst)
+    assert_combine_close(host(dx_full, np.uint16)[:T], want_dx, mag, k, "case %d dx" % seed)
