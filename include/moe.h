@@ -141,7 +141,10 @@ size_t moe_layout_workspace_bytes(int num_tokens, int num_experts, int top_k);
  *   sizes: expert_counts [E], expert_offsets [E+1], rank_counts [R],
  *          rank_offsets [R+1], rank_token_counts [R], dst_row [T, k],
  *          src_pair [T*k] (packed) or [E*capacity], overflow [1]
- *   workspace  device scratch of at least moe_layout_workspace_bytes()
+ *   workspace  device scratch of at least moe_layout_workspace_bytes();
+ *              it needs no initialisation and is overwritten (per-tile
+ *              counts, for many tiles rewritten in place as per-tile bases),
+ *              so calls that may overlap must not share one
  *
  * Placement uses no atomics on global memory: results are deterministic.
  * Requires num_experts % num_ranks == 0 and the limits of moe_route.
@@ -324,7 +327,9 @@ size_t moe_rank_layout_workspace_bytes(int num_tokens, int top_k, int num_ranks)
  *   row_token          [T*min(k,R)] int32 out: token of each row, -1 past
  *                      the last row
  * Requires R to divide E. Deterministic; two launches (one when all T*k
- * pairs fit in one tile of 1024 pairs).
+ * pairs fit in one tile of 1024 pairs, three for many tiles). The workspace
+ * needs no initialisation and is overwritten, so calls that may overlap must
+ * not share one.
  */
 int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
                     const int32_t* topk_idx, int32_t* rank_token_counts,
