@@ -1,0 +1,87 @@
+"""CPU tests of the measurement helpers in bench.py: the algorithmic byte
+counts the roofline divides by, and the source hash that decides whether the
+committed HBM-traffic record still describes the combine kernel."""
+
+import json
+
+import pytest
+
+import bench
+from synth import workloads as W
+
+
+def test_dsv3_step_bytes_are_the_documented_figures():
+    w = W.WORKLOADS["dsv3"]
+    b = bench.step_bytes(w, w.tokens * w.top_k)
+    T, H, k = w.tokens, w.hidden, w.top_k
+    # combine: every row read once (2H), weights + dst_row (8 per pair), out written
+    assert b["combine"] == T * k * 2 * H + T * k * 8 + T * 2 * H == 528744448
+    # FP8 dispatch: x read, dst_row read, k copies of H codes + H/128 fp32 scales
+    assert b["dispatch"] == T * 2 * H + T * k * 4 + T * k * (H + H // 128 * 4) == 301072384
+    assert sum(b.values()) == 834670988
+
+
+def test_mxfp8_moves_the_same_bytes_as_fp8_at_h_7168():
+    # 1x32 byte scales and 1x128 fp32 scales both add H/32 bytes per row
+    w = W.WORKLOADS["dsv3"]
+    rows = w.tokens * w.top_k
+    assert bench.step_bytes(w, rows, 1) == bench.step_bytes(w, rows, 2)
+
+
+def test_dropped_rows_are_not_counted():
+    w = W.WORKLOADS["dsv3"]
+    full = bench.step_bytes(w, w.tokens * w.top_k)
+    fewer = bench.step_bytes(w, w.tokens * w.top_k - 100)
+    assert full["combine"] - fewer["combine"] == 100 * 2 * w.hidden
+    assert full["dispatch"] - fewer["dispatch"] == 100 * (w.hidden + w.hidden // 128 * 4)
+
+
+def test_backward_bytes():
+    w = W.WORKLOADS["dsv3"]
+    rows = w.tokens * w.top_k
+    b = bench.backward_bytes(w, rows)
+    T, H, k = w.tokens, w.hidden, w.top_k
+    assert b["combine_backward"] == T * H * 2 + 2 * rows * H * 2 + T * k * 12
+    assert b["dispatch_backward"] == rows * H * 2 + T * k * 4 + T * H * 2
+
+
+def test_code_only_drops_comments_and_whitespace():
+    src = "int a = 1; // one\n/* block\n comment */ int  b =\n 2;"
+    assert bench.code_only(src) == "inta=1;intb=2;"
+
+
+def _write(tmp_path, name, text):
+    p = tmp_path / name
+    p.write_text(text)
+    return str(p)
+
+
+def test_traffic_record_follows_the_code_not_the_comments(tmp_path, monkeypatch):
+    src = _write(tmp_path, "k.hip", "// combine\n__global__ void k() { x += 1; }\n")
+    monkeypatch.setattr(bench, "COMBINE_SOURCES", [src])
+    rec = {"kernel_source_sha256": bench.sha_of([src]), "algorithmic_bytes_per_launch": 1000,
+           "traffic_bytes_per_launch": 1234}
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _write(tmp_path, "t.json", json.dumps(rec)))
+    assert bench.load_traffic(1000) == 1234
+    assert bench.load_traffic(999) is None              # another workload
+    # a comment edit keeps the record
+    _write(tmp_path, "k.hip", "// the combine kernel\n__global__ void k() {\n  x += 1;\n}\n")
+    assert bench.load_traffic(1000) == 1234
+    # a code edit drops it
+    _write(tmp_path, "k.hip", "__global__ void k() { x += 2; }\n")
+    assert bench.load_traffic(1000) is None
+
+
+def test_missing_traffic_record(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.load_traffic(1000) is None
+
+
+def test_committed_traffic_record_describes_the_dsv3_combine():
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec["kernel_source_sha256"] != bench.sha_of(bench.COMBINE_SOURCES):
+        pytest.skip("the combine code changed since its HBM counters were taken; "
+                    "bench.py reports traffic as null until they are taken again")
+    w = W.WORKLOADS["dsv3"]
+    assert rec["algorithmic_bytes_per_launch"] == bench.step_bytes(w, w.tokens * w.top_k)["combine"]
