@@ -9,15 +9,64 @@
 // all-to-all", Phase 2 (outputs are weighted by the router scores).
 //
 // Precision: sigmoid and exp run in fp64 and each result is rounded once to
-// fp32; selection keys are fp32; weight sums run in fp64.
+// fp32; selection keys are fp32; weight sums run in fp64. The fp64 exp and
+// reciprocal are this file's own (exp_f64, sigmoid_f32 below).
 
 #include "kernels.h"
 #include "wave.h"
 
 namespace moe {
+
+// Taylor coefficients of exp_f64 below (1/13!, ..., 1/0!). Declared with
+// external linkage on purpose: the compiler then cannot fold them into
+// literals, and reads them as scalar loads.
+__constant__ double route_exp_taylor[14] = {
+    0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26,   // 1/13!, 1/12!, 1/11!
+    0x1.27e4fb7789f5cp-22, 0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16,   // 1/10!, 1/9!, 1/8!
+    0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10, 0x1.1111111111111p-7,    // 1/7!, 1/6!, 1/5!
+    0x1.5555555555555p-5, 0x1.5555555555555p-3, 0x1p-1, 0x1p+0, 0x1p+0};  // 1/4!, ..., 1/0!
+
 namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
+
+// e^x in fp64 for the routing scores, by Cody and Waite's range reduction
+// and the Taylor series:
+//   x = n*ln2 + r, n = rint(x * log2(e)), |r| <= ln2/2,
+// with ln2 split into a head of 32 significant bits (so n * head is exact
+// for |n| < 2^21) and a tail; e^r is the Taylor polynomial of degree 13
+// (truncation below 3e-18 relative) by Horner's rule, and e^x = 2^n * e^r.
+// x is clamped to [-800, 700]: there e^x is 0 or finite with room to spare,
+// and the results that use it round to the same fp32 values as without the
+// clamp. The coefficients 1/j! (route_exp_taylor) are read from constant
+// memory with a wave-uniform index, so they load into scalar registers and
+// each Horner step is one fp64 FMA (as literals they would cost two vector
+// moves each).
+  // 1/4! ... 1/0!
+constexpr double kLog2e = 0x1.71547652b82fep+0;       // log2(e), nearest double
+constexpr double kLn2Hi = 0x1.62e42ffp-1;             // ln2 to 32 significant bits
+constexpr double kLn2Lo = -0x1.718432a1b0e26p-35;     // ln2 - kLn2Hi, nearest double
+
+__device__ __forceinline__ double exp_f64(double x) {
+  x = __builtin_fmin(__builtin_fmax(x, -800.0), 700.0);
+  const double n = __builtin_rint(x * kLog2e);
+  double r = __builtin_fma(-n, kLn2Hi, x);
+  r = __builtin_fma(-n, kLn2Lo, r);
+  double p = route_exp_taylor[0];
+#pragma unroll
+  for (int j = 1; j < 14; ++j) p = __builtin_fma(p, r, route_exp_taylor[j]);
+  return ldexp(p, (int)n);
+}
+
+// fp32(1 / (1 + e^-l)). The reciprocal is the hardware estimate refined by
+// two Newton steps; 1 + e^-l stays below 1e305, so every step is finite.
+__device__ __forceinline__ float sigmoid_f32(float l) {
+  const double d = 1.0 + exp_f64(-(double)l);
+  double y = __builtin_amdgcn_rcp(d);
+  y = __builtin_fma(y, __builtin_fma(-d, y, 1.0), y);
+  y = __builtin_fma(y, __builtin_fma(-d, y, 1.0), y);
+  return (float)y;
+}
 
 // Monotone map fp32 -> uint32 (larger float -> larger integer); -0 and +0
 // compare equal, as they do as floats.
@@ -99,7 +148,7 @@ __global__ __launch_bounds__(256) void route_kernel(
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     ok[i] = live && e0 + i < E;
-    const float s = sigmoid ? (float)(1.0 / (1.0 + exp(-(double)lg[i]))) : lg[i];
+    const float s = sigmoid ? sigmoid_f32(lg[i]) : lg[i];
     score[i] = s;
     key[i] = (bias != nullptr && ok[i]) ? s + bs[i] : s;
   }
@@ -213,7 +262,7 @@ __global__ __launch_bounds__(256) void route_kernel(
     u = lane < k ? (double)my_score : 0.0;
   } else {
     const float m = wave_max_f32(lane < k ? my_score : -INFINITY);
-    u = lane < k ? exp((double)my_score - (double)m) : 0.0;
+    u = lane < k ? exp_f64((double)my_score - (double)m) : 0.0;
   }
   const double total = wave_sum_f64(u);
   if (lane < k) {
@@ -291,7 +340,7 @@ __global__ __launch_bounds__(256) void route_team_kernel(
     const int e = tl + L * i;
     ok[i] = live && e < E;
     const float l = ok[i] ? logits[(size_t)t * E + e] : 0.0f;
-    const float sv = sigmoid ? (float)(1.0 / (1.0 + exp(-(double)l))) : l;
+    const float sv = sigmoid ? sigmoid_f32(l) : l;
     score[i] = sv;
     key[i] = (bias != nullptr && ok[i]) ? sv + bias[e] : sv;
   }
@@ -346,7 +395,7 @@ __global__ __launch_bounds__(256) void route_team_kernel(
     u = tl < k ? (double)my_score : 0.0;
   } else {
     const float m = team_max_f32<L>(tl < k ? my_score : -INFINITY);
-    u = tl < k ? exp((double)my_score - (double)m) : 0.0;
+    u = tl < k ? exp_f64((double)my_score - (double)m) : 0.0;
   }
   const double total = team_sum_f64<L>(u);
   if (live && tl < k) {
