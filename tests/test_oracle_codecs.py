@@ -49,7 +49,8 @@ def test_e4m3_encode_all_bf16_patterns_times_scales():
     v = (bits << 16).view(np.float32)
     v = v[np.isfinite(v)]
     for mult in [1.0, 0.5, 3.0, 448.0 / 3.1640625, 123.456, 2.0 ** -5, 1e4]:
-        x = (v * np.float32(mult)).astype(np.float32)
+        with np.errstate(over="ignore"):       # products past fp32 are dropped next
+            x = (v * np.float32(mult)).astype(np.float32)
         x = x[np.isfinite(x)]
         for chunk in np.array_split(x, 16):
             assert np.array_equal(O.e4m3_encode(chunk), _e4m3_brute(chunk))
