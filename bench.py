@@ -12,7 +12,9 @@ path: its output (dequantised rows) is prepared once before timing.
 Default workload: the DeepSeek-V3-shaped layer, T=4096 tokens, hidden 7168,
 256 experts in 8 groups (top-4 groups, top-8 experts), 32 simulated ranks,
 FP8 dispatch, bf16 combine. Inputs are seeded synthetic data already resident
-in HBM when timing starts.
+in HBM when timing starts. The timed steps are captured once into a HIP graph
+and replayed (every kernel of every step still runs; the host only stops
+issuing the launches one by one); --eager launches them from the host instead.
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      HBM roofline of the dominant kernel (combine): algorithmic
@@ -77,8 +79,11 @@ def parse():
     p.add_argument("--dispatch", default="auto", choices=["auto", "bf16", "fp8", "mxfp8"],
                    help="dispatched format (auto: the workload's own)")
     p.add_argument("--cold-steps", type=int, default=10)
-    p.add_argument("--graph", action="store_true",
-                   help="capture the timed steps into one HIP graph and replay it")
+    g = p.add_mutually_exclusive_group()
+    g.add_argument("--graph", dest="graph", action="store_true", default=True,
+                   help="capture the timed steps into one HIP graph and replay it (default)")
+    g.add_argument("--eager", dest="graph", action="store_false",
+                   help="launch the timed steps one by one from the host instead")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--pass", dest="pass_", default="forward",

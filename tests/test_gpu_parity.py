@@ -688,3 +688,60 @@ def test_decode_steps_replay_in_a_graph():
             for n, v in zip(names, e):
                 assert torch.equal(getattr(b, n), v), (rep, n)
             assert torch.equal(b.dispatched[b.src_pair >= 0], q), rep
+
+
+@pytest.mark.parametrize("shape", [
+    # DeepSeek-V3-shaped layer: 32 layout tiles, packed rows, FP8 dispatch
+    ("dsv3", None),
+    # a smaller softmax layer with bf16 dispatch over several tiles
+    ("qwen3_skew", 2048),
+], ids=lambda s: s[0] if s[1] is None else "%s_T%d" % s)
+def test_packed_layer_steps_replay_in_a_graph(shape):
+    """Two packed multi-tile layer passes (route, count + place layout, dispatch,
+    combine; each with its own inputs) captured in one HIP graph, as the
+    benchmark times them. The graph is replayed three times with eager work
+    and synchronisations between replays; every replay must equal the eager
+    run bit for bit, and the eager layout equals the oracle's."""
+    name, tokens = shape
+    w = W.WORKLOADS[name]
+    t = tokens or w.tokens
+    say("graph replay case", name, "T=%d" % t)
+    steps = [W.make_inputs(w, 11 + i, tokens=t) for i in range(2)]
+    ins = [(dev(s.logits), dev(s.bias) if s.bias is not None else None, dev(s.x)) for s in steps]
+    bufs = [LayerBuffers.allocate(t, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                  dtype=w.dispatch_dtype) for _ in steps]
+    g = np.random.Generator(np.random.PCG64(21))
+    y = dev(W.random_bf16_rows(g, bufs[0].num_rows, w.hidden))
+
+    def run():
+        for (lg, bi, x), b in zip(ins, bufs):
+            M.run_layer(b, lg, bi, x, w.score_fn, w.groups, w.topk_groups)
+            b.combine(y)
+
+    names = ("topk_idx", "topk_weights", "dst_row", "src_pair", "expert_counts",
+             "expert_offsets", "rank_counts", "rank_offsets", "rank_token_counts", "combined",
+             "dispatched")
+    if bufs[0].scales is not None:
+        names = names + ("scales",)
+    run()
+    torch.cuda.synchronize()
+    eager = [[getattr(b, n).clone() for n in names] for b in bufs]
+    for b in bufs:
+        L = O.layout(host(b.topk_idx), w.experts, w.ranks, 0)
+        assert np.array_equal(host(b.dst_row), L["dst_row"])
+        assert np.array_equal(host(b.expert_counts), L["expert_counts"])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for b in bufs:                       # eager work between replays
+            for n in names:
+                v = getattr(b, n)
+                v.fill_(-7.0 if v.dtype == torch.float32 else -7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            for n, v in zip(names, e):
+                assert torch.equal(getattr(b, n), v), (rep, n)
+    say("  3 replays equal the eager run")
