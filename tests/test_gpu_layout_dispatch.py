@@ -57,6 +57,12 @@ CASES = [
     (1, 512, 32, 16, 2, 1, 384, True, 0.0),        # one token, k = 32
     (64, 24, 6, 6, 1, 2, 96, True, 0.2),           # cap 1, MXFP8 with 3 blocks per row
     (0, 8, 2, 4, 3, 0, 256, True, 0.0),            # empty
+    # packed, many tiles: count + place, then dispatch
+    (4096, 256, 8, 32, 0, 1, 1024, True, 0.02),    # DeepSeek-V3 routing shape, FP8
+    (3000, 64, 4, 8, 0, 0, 256, False, 0.1),       # repeated experts, masked pairs, bf16
+    (1500, 8, 1, 2, 0, 2, 128, True, 0.0),         # k = 1, two tiles, MXFP8
+    (8192, 128, 8, 16, 0, 0, 256, True, 0.0),      # 64 tiles x 128 experts
+    (2048, 512, 8, 512, 0, 1, 128, True, 0.05),    # 16 tiles x 512 experts, 512 ranks
 ]
 
 
@@ -120,3 +126,32 @@ def test_layout_dispatch_equals_separate_calls_on_a_decode_step():
     for name in ("topk_idx", "dst_row", "src_pair", "expert_counts", "rank_token_counts",
                  "dispatched", "scales"):
         assert torch.equal(getattr(bufs[0], name), getattr(bufs[1], name)), name
+
+
+
+def test_layout_dispatch_reuses_its_workspace():
+    """Three packed calls on the same buffers with different routing (the
+    first on a workspace full of 0xFF bytes, the last without distinct-token
+    counts) each match the oracle: no call depends on what an earlier one
+    left in the workspace."""
+    t, e, k, r, h = 2048, 64, 8, 8, 256
+    b = LayerBuffers.allocate(t, h, e, k, r, 0, dtype=M.MOE_DTYPE_BF16)
+    b.workspace.fill_(0xFF)
+    for call in range(3):
+        g = W.rng(500 + call)
+        idx = W.random_topk_idx(g, t, e, k, distinct=call != 1, mask_frac=0.03 * call)
+        x = W.random_bf16_rows(g, t, h)
+        if call == 2:
+            b.rank_token_counts = None
+        b.topk_idx.copy_(dev(idx))
+        b.layout_dispatch(dev(x))
+        L = O.layout(idx, e, r, 0)
+        names = ["expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "dst_row",
+                 "src_pair", "overflow"] + (["rank_token_counts"] if call < 2 else [])
+        for name in names:
+            got = host(getattr(b, name))
+            assert np.array_equal(got.reshape(L[name].shape), L[name]), (call, name)
+        want, written = _oracle_rows(M.MOE_DTYPE_BF16, x, L["dst_row"], b.num_rows)
+        got = host(b.dispatched).view(np.uint16)
+        assert np.array_equal(got[written], want[0][written]), call
+        say("  call", call, "matches the oracle")
