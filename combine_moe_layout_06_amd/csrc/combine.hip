@@ -108,6 +108,98 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+// k = 8, held outputs: each wave takes IPW consecutive (token, part) items
+// (a part is 128 chunks of 16 bytes, two per lane), keeps their rounded
+// outputs in registers (8 per item) and stores all of them after the last
+// item's rows have been read. The next item's rows and weights are loaded
+// while the current rows are in flight. Launched at kHeldBlocksPerCu, so the
+// grid (at most kHeldWaves waves) is resident at once: the chip reads the
+// expert rows first and writes the outputs in one burst at the end, instead
+// of mixing the output stores into the read stream. The arithmetic is the
+// combine_kernel's: the same fma chain in slot order and one rounding.
+constexpr int kHeldPart = 2 * MOE_WAVE;              // chunks per item
+constexpr int kHeldBlocksPerCu = 2;                  // ~210 registers per lane
+constexpr int kHeldWaves = 256 * kHeldBlocksPerCu * kWavesPerBlock;   // 256 CUs
+constexpr int kHeldMinItems = 8, kHeldMaxItems = 16;
+
+template <int K, int IPW>
+__global__ __launch_bounds__(256) void combine_held_kernel(
+    int T, int nch, int parts, int num_rows, const u32x4* __restrict__ y,
+    const int32_t* __restrict__ dst_row, const float* __restrict__ w,
+    u32x4* __restrict__ out) {
+  constexpr int U = kHeldPart / MOE_WAVE;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int items = T * parts;
+  const int first = gw * IPW;
+  if (first >= items) return;
+  int tcur = first / parts;
+  int nd = lane < K ? dst_row[(size_t)tcur * K + lane] : -1;
+  float nwt = lane < K ? (w != nullptr ? w[(size_t)tcur * K + lane] : 1.0f) : 0.0f;
+
+  u32x4 res[IPW][U];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int it = first + i;
+#pragma unroll
+    for (int u = 0; u < U; ++u) res[i][u] = u32x4{0u, 0u, 0u, 0u};
+    if (it < items) {
+      const int t = it / parts;
+      const int c0 = (it - t * parts) * kHeldPart;
+      int d[K];
+      float wj[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        d[j] = read_lane(nd, j);
+        wj[j] = read_lane(nwt, j);
+        if (d[j] >= num_rows) d[j] = -1;
+      }
+      u32x4 v[K][U];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const u32x4* row = y + (size_t)(d[j] < 0 ? 0 : d[j]) * nch;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          v[j][u] = u32x4{0u, 0u, 0u, 0u};
+          if (d[j] >= 0 && c < nch) v[j][u] = stream_load(row + c);
+        }
+      }
+      // the next item's rows and weights, when it starts a new token
+      if (i + 1 < IPW && it + 1 < items) {
+        const int tn = (it + 1) / parts;
+        if (tn != tcur) {
+          tcur = tn;
+          nd = lane < K ? dst_row[(size_t)tn * K + lane] : -1;
+          nwt = lane < K ? (w != nullptr ? w[(size_t)tn * K + lane] : 1.0f) : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+          if (d[j] >= 0) fma_row(acc, wj[j], v[j][u]);
+        res[i][u] = pack_row(acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int it = first + i;
+    if (it < items) {
+      const int t = it / parts;
+      const int c0 = (it - t * parts) * kHeldPart;
+      u32x4* dst = out + (size_t)t * nch;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        if (c < nch) stream_store(res[i][u], dst + c);
+      }
+    }
+  }
+}
+
 // Any k: rows are loaded one slot at a time.
 __global__ __launch_bounds__(256) void combine_kernel_any_k(
     int T, int k, int nch, int parts, int cpp, int num_rows, const u32x4* __restrict__ y,
@@ -246,6 +338,36 @@ void launch_fixed(dim3 grid, hipStream_t stream, int T, int nch, int parts, int 
                      static_cast<const u32x4*>(y), dst_row, w, static_cast<u32x4*>(out));
 }
 
+template <int IPW>
+void launch_held(int waves, hipStream_t stream, int T, int nch, int parts, int num_rows,
+                 const void* y, const int32_t* dst_row, const float* w, void* out) {
+  hipLaunchKernelGGL((combine_held_kernel<8, IPW>),
+                     dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(256),
+                     lds_cap_bytes(kHeldBlocksPerCu), stream, T, nch, parts, num_rows,
+                     static_cast<const u32x4*>(y), dst_row, w, static_cast<u32x4*>(out));
+}
+
+// k = 8 with 8..16 items per wave over kHeldWaves waves: the held-output
+// kernel (returns false otherwise).
+bool try_launch_held(int T, int nch, int k, int num_rows, const void* y,
+                     const int32_t* dst_row, const float* w, void* out, hipStream_t stream) {
+  if (k != 8) return false;
+  const int parts = (nch + kHeldPart - 1) / kHeldPart;
+  const long long items = (long long)T * parts;
+  const long long ipw = (items + kHeldWaves - 1) / kHeldWaves;
+  if (ipw < kHeldMinItems || ipw > kHeldMaxItems) return false;
+  const int waves = (int)((items + ipw - 1) / ipw);
+#define MOE_HELD(n) \
+  case n: launch_held<n>(waves, stream, T, nch, parts, num_rows, y, dst_row, w, out); break;
+  switch ((int)ipw) {
+    MOE_HELD(8) MOE_HELD(9) MOE_HELD(10) MOE_HELD(11) MOE_HELD(12) MOE_HELD(13) MOE_HELD(14)
+    MOE_HELD(15) MOE_HELD(16)
+    default: return false;
+  }
+#undef MOE_HELD
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void* dout,
@@ -263,6 +385,7 @@ hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int nch = H / 8;
+  if (try_launch_held(T, nch, k, num_rows, y, dst_row, w, out, stream)) return hipGetLastError();
   int parts = T > 0 ? (kTargetWaves + T - 1) / T : 1;
   parts = max(1, min(parts, nch / MOE_WAVE));
   int cpp = (nch + parts - 1) / parts;
