@@ -121,6 +121,12 @@ constexpr int kHeldPart = 2 * MOE_WAVE;              // chunks per item
 constexpr int kHeldBlocksPerCu = 2;                  // ~210 registers per lane
 constexpr int kHeldWaves = 256 * kHeldBlocksPerCu * kWavesPerBlock;   // 256 CUs
 constexpr int kHeldMinItems = 8, kHeldMaxItems = 16;
+// Rows of at least 7 parts (hidden > 6144): measured against the per-item
+// kernel at k = 8, held outputs were 3-10% faster on rows of 7 parts (hidden
+// 7040 and 7168) and 0-7% slower on rows of 4 parts (hidden 4096), equal on
+// 2 parts. With short rows the wave's walk along a row costs more than the
+// burst saves.
+constexpr int kHeldMinParts = 7;
 
 template <int K, int IPW>
 __global__ __launch_bounds__(256) void combine_held_kernel(
@@ -347,12 +353,13 @@ void launch_held(int waves, hipStream_t stream, int T, int nch, int parts, int n
                      static_cast<const u32x4*>(y), dst_row, w, static_cast<u32x4*>(out));
 }
 
-// k = 8 with 8..16 items per wave over kHeldWaves waves: the held-output
-// kernel (returns false otherwise).
+// k = 8, rows of at least kHeldMinParts parts, 8..16 items per wave over
+// kHeldWaves waves: the held-output kernel (returns false otherwise).
 bool try_launch_held(int T, int nch, int k, int num_rows, const void* y,
                      const int32_t* dst_row, const float* w, void* out, hipStream_t stream) {
   if (k != 8) return false;
   const int parts = (nch + kHeldPart - 1) / kHeldPart;
+  if (parts < kHeldMinParts) return false;
   const long long items = (long long)T * parts;
   const long long ipw = (items + kHeldWaves - 1) / kHeldWaves;
   if (ipw < kHeldMinItems || ipw > kHeldMaxItems) return false;

@@ -354,11 +354,12 @@ COMBINE_CASES = [
     (128, 256, 2, 256, 0.0),
     (1000, 520, 3, 3000, 0.1),
     (4096, 7168, 8, 32768, 0.0),
-    # k = 8 with 8..16 items of 2 KiB per wave: outputs held in registers
+    # k = 8, rows of 7 parts of 2 KiB, 8..16 items per wave: outputs held in registers
     (2100, 7168, 8, 16800, 0.05),        # 8 items per wave, the last wave short
     (3000, 7040, 8, 24000, 0.1),         # 11 items; each row's last part is 112 chunks
     (4097, 7168, 8, 32776, 0.0),         # 15 items
-    (8192, 4096, 8, 65536, 0.02),        # 16 items, the skewed Qwen3 shape
+    (4600, 7168, 8, 36800, 0.02),        # 16 items
+    (8192, 4096, 8, 65536, 0.02),        # rows of 4 parts: the per-item kernel
     (777, 4096, 6, 5000, 0.2),
     (500, 1024, 4, 2000, 0.0),
     (300, 2048, 1, 300, 0.0),
