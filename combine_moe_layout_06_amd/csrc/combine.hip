@@ -389,10 +389,11 @@ hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void
 
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool allow_held) {
   if (T == 0) return hipSuccess;
   const int nch = H / 8;
-  if (try_launch_held(T, nch, k, num_rows, y, dst_row, w, out, stream)) return hipGetLastError();
+  if (allow_held && try_launch_held(T, nch, k, num_rows, y, dst_row, w, out, stream))
+    return hipGetLastError();
   int parts = T > 0 ? (kTargetWaves + T - 1) / T : 1;
   parts = max(1, min(parts, nch / MOE_WAVE));
   int cpp = (nch + parts - 1) / parts;

@@ -55,10 +55,11 @@ hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* 
                                  const int32_t* dst_row, void* out, uint8_t* out_scales,
                                  hipStream_t stream);
 
-// w == nullptr means unit weights (the gradient of dispatch).
+// w == nullptr means unit weights (the gradient of dispatch). allow_held:
+// the held-output kernel may serve the shapes it is chosen for.
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
-                          hipStream_t stream);
+                          hipStream_t stream, bool allow_held = true);
 
 // Fan-out of the (token, rank) rows to the expert rows, and the per-rank
 // partial combine.
