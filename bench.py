@@ -15,6 +15,11 @@ FP8 dispatch, bf16 combine. Inputs are seeded synthetic data already resident
 in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
+Steps are independent batches, so by default they are pipelined on two
+streams: the route and layout of step i+1 run beside the dispatch and combine
+of step i, on a second set of layer buffers (--serial: one step after the
+other; decode-sized fused launches default to it). The serial rate of the
+same steps is measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      HBM roofline of the dominant kernel (combine): algorithmic
@@ -28,6 +33,7 @@ Prints one JSON line. Besides the contract fields it carries:
                 pass over the same steps (the timed loop itself has no events)
   cold_us_per_step  the same step with a 1 GiB write between steps, which
                 evicts L2 and the 256 MB Infinity Cache
+  serial_ms_per_step  the timed steps run one after the other on one stream
 """
 
 from __future__ import annotations
@@ -84,6 +90,14 @@ def parse():
                    help="capture the timed steps into one HIP graph and replay it (default)")
     g.add_argument("--eager", dest="graph", action="store_false",
                    help="launch the timed steps one by one from the host instead")
+    o = p.add_mutually_exclusive_group()
+    o.add_argument("--overlap", dest="overlap", action="store_true", default=None,
+                   help="pipeline the steps on two streams: the route and layout of step i+1 "
+                        "run beside the dispatch and combine of step i (default when layout "
+                        "and dispatch are separate launches)")
+    o.add_argument("--serial", dest="overlap", action="store_false",
+                   help="run each step after the previous one on a single stream (default "
+                        "when layout and dispatch are one launch: decode-sized capacity mode)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--pass", dest="pass_", default="forward",
@@ -458,6 +472,55 @@ def cpu_baseline(w, seed, budget_s, dtype=None):
                       % (w.name, ts, w.tokens, reps, el)}
 
 
+def serial_steps(w, bufs, inputs, y, first, steps):
+    """`steps` steps one after the other on the current stream: route,
+    layout + dispatch (moe_layout_dispatch), combine; step i uses the inputs
+    of step first + i."""
+    b = bufs[0]
+    for i in range(steps):
+        d = inputs[(first + i) % len(inputs)]
+        b.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        b.layout_dispatch(d["x"])
+        b.combine(y)
+
+
+def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side):
+    """The same steps pipelined on two streams: the route and layout of
+    step i run on `side` while the current stream runs the dispatch and
+    combine of step i - 1; then the current stream dispatches and combines
+    step i. The two layer buffers in `bufs` alternate between steps, and a
+    step's route waits until the combine of the step before last has
+    released its buffer. Every step does all of its work; the results equal
+    those of serial_steps. When layout and dispatch are one launch, the
+    side stream runs the route only."""
+    main = torch.cuda.current_stream()
+    fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
+    free = []
+    for _ in bufs:
+        e = torch.cuda.Event()
+        e.record(main)
+        free.append(e)
+    for i in range(steps):
+        b = bufs[i % 2]
+        d = inputs[(first + i) % len(inputs)]
+        side.wait_event(free[i % 2])
+        with torch.cuda.stream(side):
+            b.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+            if not fused:
+                b.layout()
+        ready = torch.cuda.Event()
+        ready.record(side)
+        main.wait_event(ready)
+        if fused:
+            b.layout_dispatch(d["x"])
+        else:
+            b.dispatch(d["x"])
+        b.combine(y)
+        free[i % 2] = torch.cuda.Event()
+        free[i % 2].record(main)
+    main.wait_stream(side)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -505,6 +568,16 @@ def main():
 
     # layout + dispatch: one launch for decode-sized inputs in capacity mode
     fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
+    # pipelining hides the route and the layout launches; with one fused
+    # launch only the short route is left to hide, and the cross-stream
+    # waits cost more (decode: 21.9 against 20.1 us/step)
+    if args.overlap is None:
+        args.overlap = not fused
+    # pipelined steps alternate between two layer buffers
+    bufs = [buf] + ([M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
+                                             w.capacity, device=dev, dtype=dtype)]
+                    if args.overlap else [])
+    side = torch.cuda.Stream() if args.overlap else None
 
     def front(i):
         d = inputs[i % len(inputs)]
@@ -536,38 +609,35 @@ def main():
     total_bytes = sum(nbytes.values())
 
     # ---- warmup
-    for i in range(warm):
-        front(i)
-        buf.combine(y)
+    serial_steps(w, bufs, inputs, y, 0, warm)
+    if args.overlap:
+        overlapped_steps(torch, M, w, bufs, inputs, y, 0, warm, side)
     torch.cuda.synchronize()
 
-    # ---- timed steps: back to back, nothing but the path on the stream
-    def timed_steps():
-        for i in range(steps):
-            d = inputs[(warm + i) % len(inputs)]
-            buf.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-            buf.layout_dispatch(d["x"])
-            buf.combine(y)
+    # ---- timed steps: back to back, nothing but the path on the stream(s)
+    def timed(run):
+        if args.graph:
+            # all timed steps (each with its own inputs) in one graph: the
+            # launches are recorded once, replay issues them without the host
+            graph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph):
+                run()
+            graph.replay()                  # first replay uploads the graph
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
-    if args.graph:
-        # all timed steps (each with its own inputs) in one graph: the
-        # launches are recorded once, replay issues them without the host
-        graph = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            timed_steps()
-        graph.replay()                      # first replay uploads the graph
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        timed_steps()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    serial_wall = timed(lambda: serial_steps(w, bufs, inputs, y, warm, steps))
+    wall = (timed(lambda: overlapped_steps(torch, M, w, bufs, inputs, y, warm, steps, side))
+            if args.overlap else serial_wall)
 
     # ---- the same steps again with HIP events between the phases (on the
     # launch stream) for the per-phase times and the roofline; layout and
@@ -638,7 +708,11 @@ def main():
         "vs_baseline": None,
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
-        "launch": "hip graph replay" if args.graph else "eager stream",
+        "launch": ("hip graph replay" if args.graph else "eager launches") +
+                  ("; steps pipelined on two streams: the route and layout of step i+1 run "
+                   "beside the dispatch and combine of step i (two layer buffers in turn)"
+                   if args.overlap else "; one step after the other on one stream"),
+        "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
                    % (w.name, w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                       "group-limited sigmoid G=%d kg=%d" % (w.groups, w.topk_groups)

@@ -85,3 +85,13 @@ def test_committed_traffic_record_describes_the_dsv3_combine():
                     "bench.py reports traffic as null until they are taken again")
     w = W.WORKLOADS["dsv3"]
     assert rec["algorithmic_bytes_per_launch"] == bench.step_bytes(w, w.tokens * w.top_k)["combine"]
+
+
+def test_launch_flags(monkeypatch):
+    """Default: graph replay, pipelining decided by the workload (None);
+    --eager, --serial and --overlap override."""
+    for argv, graph, overlap in ([[], True, None], [["--eager"], False, None],
+                                 [["--serial"], True, False], [["--overlap", "--eager"], False, True]):
+        monkeypatch.setattr(bench.sys, "argv", ["bench.py"] + argv)
+        a = bench.parse()
+        assert (a.graph, a.overlap) == (graph, overlap), argv

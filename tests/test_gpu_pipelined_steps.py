@@ -1,0 +1,103 @@
+"""The benchmark's pipelined steps (route and layout of step i+1 on a side
+stream beside the dispatch and combine of step i, two layer buffers in turn)
+give the same results as the same steps run one after the other: eager, and
+captured in a HIP graph and replayed."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import combine_moe_layout_06_amd as M  # noqa: E402
+from gpu_helpers import dev  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+NAMES = ("topk_idx", "topk_weights", "dst_row", "src_pair", "expert_counts", "expert_offsets",
+         "rank_counts", "rank_token_counts", "overflow", "combined")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("the GPU tests need a visible MI355X")
+    M.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _state(b):
+    out = {n: getattr(b, n).clone() for n in NAMES}
+    live = b.src_pair >= 0
+    out["rows"] = b.dispatched[live].clone()
+    if b.scales is not None:
+        out["scales"] = b.scales[live].clone()
+    return out
+
+
+def _poison(bufs):
+    for b in bufs:
+        for n in NAMES:
+            v = getattr(b, n)
+            v.fill_(-7.0 if v.dtype == torch.float32 else -7)
+        b.dispatched.fill_(0x55)
+
+
+@pytest.mark.parametrize("name,steps", [("dsv3", 5), ("decode", 6)])
+def test_pipelined_steps_equal_serial_steps(name, steps):
+    w = W.WORKLOADS[name]
+    say("pipelined steps", name, "x", steps)
+    seeds = [w.step_seed0 + i for i in range(steps)] if w.steps > 1 else [0]
+    inputs = []
+    for s in seeds:
+        inp = W.make_inputs(w, s)
+        inputs.append(dict(logits=dev(inp.logits),
+                           bias=dev(inp.bias) if inp.bias is not None else None,
+                           x=dev(inp.x)))
+    bufs = [M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                    dtype=w.dispatch_dtype) for _ in range(2)]
+    g = np.random.Generator(np.random.PCG64(3))
+    y = dev(W.random_bf16_rows(g, bufs[0].num_rows, w.hidden))
+
+    # serial reference of the last two steps, each alone in bufs[0]
+    want = {}
+    for i in (steps - 2, steps - 1):
+        bench.serial_steps(w, bufs, inputs, y, i, 1)
+        torch.cuda.synchronize()
+        want[i] = _state(bufs[0])
+
+    side = torch.cuda.Stream()
+    _poison(bufs)
+    bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side)
+    torch.cuda.synchronize()
+    for i in (steps - 2, steps - 1):
+        got = _state(bufs[i % 2])
+        for n, v in want[i].items():
+            assert torch.equal(got[n], v), ("eager", i, n)
+    say("  eager pipelined steps equal the serial ones")
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side)
+    for rep in range(2):
+        _poison(bufs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in (steps - 2, steps - 1):
+            got = _state(bufs[i % 2])
+            for n, v in want[i].items():
+                assert torch.equal(got[n], v), ("graph", rep, i, n)
+    say("  graph replays equal the serial steps")
