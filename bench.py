@@ -16,9 +16,10 @@ in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
-streams: the route and layout of step i+1 run beside the dispatch and combine
-of step i, on a second set of layer buffers (--serial: one step after the
-other; decode-sized fused launches default to it). The serial rate of the
+streams in groups of 4 steps: the route and layout of one group run beside the
+dispatch and combine of the group before, on 8 sets of layer buffers used in
+turn (--serial: one step after the other; decode-sized fused launches default
+to it). The serial rate of the
 same steps is measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
@@ -92,9 +93,9 @@ def parse():
                    help="launch the timed steps one by one from the host instead")
     o = p.add_mutually_exclusive_group()
     o.add_argument("--overlap", dest="overlap", action="store_true", default=None,
-                   help="pipeline the steps on two streams: the route and layout of step i+1 "
-                        "run beside the dispatch and combine of step i (default when layout "
-                        "and dispatch are separate launches)")
+                   help="pipeline the steps on two streams: the route and layout of a group "
+                        "of steps run beside the dispatch and combine of the group before "
+                        "(default when layout and dispatch are separate launches)")
     o.add_argument("--serial", dest="overlap", action="store_false",
                    help="run each step after the previous one on a single stream (default "
                         "when layout and dispatch are one launch: decode-sized capacity mode)")
@@ -484,40 +485,51 @@ def serial_steps(w, bufs, inputs, y, first, steps):
         b.combine(y)
 
 
-def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side):
-    """The same steps pipelined on two streams: the route and layout of
-    step i run on `side` while the current stream runs the dispatch and
-    combine of step i - 1; then the current stream dispatches and combines
-    step i. The two layer buffers in `bufs` alternate between steps, and a
-    step's route waits until the combine of the step before last has
-    released its buffer. Every step does all of its work; the results equal
-    those of serial_steps. When layout and dispatch are one launch, the
+PIPE_GROUP = 4   # steps per cross-stream wait of the pipelined mode
+
+
+def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
+    """The same steps pipelined on two streams, in groups of `group` steps:
+    `side` runs the route and layout of the steps of one group while the
+    current stream dispatches and combines the group before; then the current
+    stream waits for the side stream once and dispatches and combines the
+    group. The 2 * group layer buffers in `bufs` are used in turn, and a
+    step's route waits until the combine of the step that last used its
+    buffer has released it. Every step does all of its work; the results
+    equal those of serial_steps. When layout and dispatch are one launch, the
     side stream runs the route only."""
-    main = torch.cuda.current_stream()
+    assert len(bufs) == 2 * group
+    main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
     fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
+    nb = len(bufs)
     free = []
     for _ in bufs:
         e = torch.cuda.Event()
         e.record(main)
         free.append(e)
-    for i in range(steps):
-        b = bufs[i % 2]
-        d = inputs[(first + i) % len(inputs)]
-        side.wait_event(free[i % 2])
-        with torch.cuda.stream(side):
-            b.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-            if not fused:
-                b.layout()
+    for g0 in range(0, steps, group):
+        grp = range(g0, min(g0 + group, steps))
+        for i in grp:
+            b = bufs[i % nb]
+            d = inputs[(first + i) % len(inputs)]
+            side.wait_event(free[i % nb])
+            with torch.cuda.stream(side):
+                b.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+                if not fused:
+                    b.layout()
         ready = torch.cuda.Event()
         ready.record(side)
         main.wait_event(ready)
-        if fused:
-            b.layout_dispatch(d["x"])
-        else:
-            b.dispatch(d["x"])
-        b.combine(y)
-        free[i % 2] = torch.cuda.Event()
-        free[i % 2].record(main)
+        for i in grp:
+            b = bufs[i % nb]
+            d = inputs[(first + i) % len(inputs)]
+            if fused:
+                b.layout_dispatch(d["x"])
+            else:
+                b.dispatch(d["x"])
+            b.combine(y)
+            free[i % nb] = torch.cuda.Event()
+            free[i % nb].record(main)
     main.wait_stream(side)
 
 
@@ -573,10 +585,10 @@ def main():
     # waits cost more (decode: 21.9 against 20.1 us/step)
     if args.overlap is None:
         args.overlap = not fused
-    # pipelined steps alternate between two layer buffers
+    # pipelined steps use 2 * PIPE_GROUP layer buffers in turn
     bufs = [buf] + ([M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
-                                             w.capacity, device=dev, dtype=dtype)]
-                    if args.overlap else [])
+                                             w.capacity, device=dev, dtype=dtype)
+                     for _ in range(2 * PIPE_GROUP - 1)] if args.overlap else [])
     side = torch.cuda.Stream() if args.overlap else None
 
     def front(i):
@@ -709,8 +721,9 @@ def main():
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams: the route and layout of step i+1 run "
-                   "beside the dispatch and combine of step i (two layer buffers in turn)"
+                  ("; steps pipelined on two streams in groups of %d: the route and layout "
+                   "of one group run beside the dispatch and combine of the group before "
+                   "(%d layer buffers in turn)" % (PIPE_GROUP, 2 * PIPE_GROUP)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"

@@ -1,7 +1,7 @@
-"""The benchmark's pipelined steps (route and layout of step i+1 on a side
-stream beside the dispatch and combine of step i, two layer buffers in turn)
-give the same results as the same steps run one after the other: eager, and
-captured in a HIP graph and replayed."""
+"""The benchmark's pipelined steps (the route and layout of a group of steps
+on a side stream beside the dispatch and combine of the group before, 2 *
+group layer buffers in turn) give the same results as the same steps run one
+after the other: eager, and captured in a HIP graph and replayed."""
 
 import os
 import sys
@@ -54,10 +54,10 @@ def _poison(bufs):
         b.dispatched.fill_(0x55)
 
 
-@pytest.mark.parametrize("name,steps", [("dsv3", 5), ("decode", 6)])
-def test_pipelined_steps_equal_serial_steps(name, steps):
+@pytest.mark.parametrize("name,steps,group", [("dsv3", 10, 4), ("dsv3", 5, 1), ("decode", 11, 4)])
+def test_pipelined_steps_equal_serial_steps(name, steps, group):
     w = W.WORKLOADS[name]
-    say("pipelined steps", name, "x", steps)
+    say("pipelined steps", name, "x", steps, "in groups of", group)
     seeds = [w.step_seed0 + i for i in range(steps)] if w.steps > 1 else [0]
     inputs = []
     for s in seeds:
@@ -66,7 +66,7 @@ def test_pipelined_steps_equal_serial_steps(name, steps):
                            bias=dev(inp.bias) if inp.bias is not None else None,
                            x=dev(inp.x)))
     bufs = [M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
-                                    dtype=w.dispatch_dtype) for _ in range(2)]
+                                    dtype=w.dispatch_dtype) for _ in range(2 * group)]
     g = np.random.Generator(np.random.PCG64(3))
     y = dev(W.random_bf16_rows(g, bufs[0].num_rows, w.hidden))
 
@@ -79,10 +79,10 @@ def test_pipelined_steps_equal_serial_steps(name, steps):
 
     side = torch.cuda.Stream()
     _poison(bufs)
-    bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side)
+    bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side, group)
     torch.cuda.synchronize()
     for i in (steps - 2, steps - 1):
-        got = _state(bufs[i % 2])
+        got = _state(bufs[i % (2 * group)])
         for n, v in want[i].items():
             assert torch.equal(got[n], v), ("eager", i, n)
     say("  eager pipelined steps equal the serial ones")
@@ -90,14 +90,14 @@ def test_pipelined_steps_equal_serial_steps(name, steps):
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side)
+        bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side, group)
     for rep in range(2):
         _poison(bufs)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         for i in (steps - 2, steps - 1):
-            got = _state(bufs[i % 2])
+            got = _state(bufs[i % (2 * group)])
             for n, v in want[i].items():
                 assert torch.equal(got[n], v), ("graph", rep, i, n)
     say("  graph replays equal the serial steps")
