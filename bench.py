@@ -18,8 +18,7 @@ issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
 streams in groups of 4 steps: the route and layout of one group run beside the
 dispatch and combine of the group before, on 8 sets of layer buffers used in
-turn (--serial: one step after the other; decode-sized fused launches default
-to it). The serial rate of the
+turn (--serial: one step after the other; the default with --eager). The serial rate of the
 same steps is measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
@@ -95,10 +94,10 @@ def parse():
     o.add_argument("--overlap", dest="overlap", action="store_true", default=None,
                    help="pipeline the steps on two streams: the route and layout of a group "
                         "of steps run beside the dispatch and combine of the group before "
-                        "(default when layout and dispatch are separate launches)")
+                        "(default with graph replay)")
     o.add_argument("--serial", dest="overlap", action="store_false",
                    help="run each step after the previous one on a single stream (default "
-                        "when layout and dispatch are one launch: decode-sized capacity mode)")
+                        "with --eager)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--pass", dest="pass_", default="forward",
@@ -580,11 +579,12 @@ def main():
 
     # layout + dispatch: one launch for decode-sized inputs in capacity mode
     fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
-    # pipelining hides the route and the layout launches; with one fused
-    # launch only the short route is left to hide, and the cross-stream
-    # waits cost more (decode: 21.9 against 20.1 us/step)
+    # pipelining by default when the steps are replayed from a graph, where
+    # the cross-stream order is graph edges; from the host, each step's event
+    # record and wait cost more than they hide (decode: 30.4 against 20.4
+    # us/step eager, 18.3 against 20.1 replayed)
     if args.overlap is None:
-        args.overlap = not fused
+        args.overlap = args.graph
     # pipelined steps use 2 * PIPE_GROUP layer buffers in turn
     bufs = [buf] + ([M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                                              w.capacity, device=dev, dtype=dtype)

@@ -88,8 +88,8 @@ def test_committed_traffic_record_describes_the_dsv3_combine():
 
 
 def test_launch_flags(monkeypatch):
-    """Default: graph replay, pipelining decided by the workload (None);
-    --eager, --serial and --overlap override."""
+    """Default: graph replay, pipelining decided later (None: it follows the
+    launch mode); --eager, --serial and --overlap override."""
     for argv, graph, overlap in ([[], True, None], [["--eager"], False, None],
                                  [["--serial"], True, False], [["--overlap", "--eager"], False, True]):
         monkeypatch.setattr(bench.sys, "argv", ["bench.py"] + argv)
