@@ -229,6 +229,29 @@ def hierarchical_bytes(w, rows_live, n_sent, dtype):
         combine_partials=n_sent * H * 2 + T * k * 4 + T * H * 2)
 
 
+def hierarchical_front(w, sets, inputs, i, s):
+    """The latency-bound front of hierarchical step i on buffer set s (a
+    LayerBuffers, RankBuffers pair): route, expert layout, (token, rank)
+    layout."""
+    d = inputs[i % len(inputs)]
+    lb, rb = sets[s]
+    lb.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+    lb.layout()
+    rb.rank_layout(lb.topk_idx)
+
+
+def hierarchical_back(sets, inputs, y, i, s):
+    """The rest of hierarchical step i: one copy per (token, rank), fan-out
+    to the expert rows, per-(token, rank) partial sums of the expert outputs
+    y, and the per-token sum."""
+    d = inputs[i % len(inputs)]
+    lb, rb = sets[s]
+    rb.dispatch(d["x"])
+    rb.expand(lb)
+    rb.combine_local(lb, y)
+    rb.combine_partials(lb.combined)
+
+
 def run_hierarchical(args, w, M, W, torch, np):
     """Deduplicated dispatch and hierarchical combine: route, expert layout,
     (token, rank) layout, one copy per (token, rank), fan-out to the expert
@@ -245,8 +268,13 @@ def run_hierarchical(args, w, M, W, torch, np):
             logits=torch.from_numpy(inp.logits).to(dev),
             bias=torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None,
             x=torch.from_numpy(inp.x.view(np.int16)).to(dev)))
-    lb = M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev, dtype=dtype)
-    rb = M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev)
+    overlap = args.graph if args.overlap is None else args.overlap
+    nsets = 2 * PIPE_GROUP if overlap else 1
+    sets = [(M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev,
+                                     dtype=dtype),
+             M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev))
+            for _ in range(nsets)]
+    lb, rb = sets[0]
 
     phases = ["route", "layout", "rank_layout", "dispatch", "expand", "combine_local",
               "combine_partials"]
@@ -257,6 +285,23 @@ def run_hierarchical(args, w, M, W, torch, np):
                 lb.layout, lambda: rb.rank_layout(lb.topk_idx), lambda: rb.dispatch(d["x"]),
                 lambda: rb.expand(lb), lambda: rb.combine_local(lb, y),
                 lambda: rb.combine_partials(lb.combined)]
+
+    def front(i, s):
+        hierarchical_front(w, sets, inputs, i, s)
+
+    def back(i, s):
+        hierarchical_back(sets, inputs, y, i, s)
+
+    def serial(first, n):
+        for i in range(first, first + n):
+            front(i, 0)
+            back(i, 0)
+
+    def piped(first, n):
+        pipelined(torch, lambda i, s: front(first + i, s), lambda i, s: back(first + i, s),
+                  nsets, n, side)
+
+    side = torch.cuda.Stream() if overlap else None
 
     # stand-in expert output: the fanned-out rows of step 0, dequantised
     y = None
@@ -277,16 +322,13 @@ def run_hierarchical(args, w, M, W, torch, np):
     rows_live = int((lb.dst_row >= 0).sum().item())
     n_sent = int(rb.rank_token_offsets[-1].item())
 
-    for i in range(args.warmup):
-        for c in calls(i):
-            c()
+    serial(0, args.warmup)
+    if overlap:
+        piped(0, args.warmup)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        for c in calls(args.warmup + i):
-            c()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    serial_wall = timed_run(torch, lambda: serial(args.warmup, args.steps), args.graph)
+    wall = (timed_run(torch, lambda: piped(args.warmup, args.steps), args.graph)
+            if overlap else serial_wall)
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
           for _ in range(args.steps)]
@@ -312,6 +354,13 @@ def run_hierarchical(args, w, M, W, torch, np):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
+        "launch": ("hip graph replay" if args.graph else "eager launches") +
+                  ("; steps pipelined on two streams in groups of %d: the route, expert layout "
+                   "and (token, rank) layout of one group run beside the send, fan-out and "
+                   "combines of the group before (%d buffer sets in turn)"
+                   % (PIPE_GROUP, 2 * PIPE_GROUP) if overlap
+                   else "; one step after the other on one stream"),
+        "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 5),
         "config": {"workload": "%s hierarchical: T=%d H=%d E=%d k=%d R=%d, one row per "
                    "(token, rank), bf16 partials" % (w.name, T, H, w.experts, k, w.ranks),
                    "tokens": T, "hidden": H, "experts": w.experts, "top_k": k,
@@ -487,49 +536,81 @@ def serial_steps(w, bufs, inputs, y, first, steps):
 PIPE_GROUP = 4   # steps per cross-stream wait of the pipelined mode
 
 
-def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
-    """The same steps pipelined on two streams, in groups of `group` steps:
-    `side` runs the route and layout of the steps of one group while the
-    current stream dispatches and combines the group before; then the current
-    stream waits for the side stream once and dispatches and combines the
-    group. The 2 * group layer buffers in `bufs` are used in turn, and a
-    step's route waits until the combine of the step that last used its
-    buffer has released it. Every step does all of its work; the results
-    equal those of serial_steps. When layout and dispatch are one launch, the
-    side stream runs the route only."""
-    assert len(bufs) == 2 * group
+def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP):
+    """Steps pipelined on two streams, in groups of `group` steps: `side`
+    runs front(i, s) for the steps of one group while the current stream runs
+    back(i, s) for the group before; then the current stream waits for the
+    side stream once and runs back() for the group. Step i uses buffer set
+    s = i % nsets (nsets = 2 * group), and its front waits until the back of
+    the step that last used that set has released it."""
+    assert nsets == 2 * group
     main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
-    fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
-    nb = len(bufs)
     free = []
-    for _ in bufs:
+    for _ in range(nsets):
         e = torch.cuda.Event()
         e.record(main)
         free.append(e)
     for g0 in range(0, steps, group):
         grp = range(g0, min(g0 + group, steps))
         for i in grp:
-            b = bufs[i % nb]
-            d = inputs[(first + i) % len(inputs)]
-            side.wait_event(free[i % nb])
+            side.wait_event(free[i % nsets])
             with torch.cuda.stream(side):
-                b.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-                if not fused:
-                    b.layout()
+                front(i, i % nsets)
         ready = torch.cuda.Event()
         ready.record(side)
         main.wait_event(ready)
         for i in grp:
-            b = bufs[i % nb]
-            d = inputs[(first + i) % len(inputs)]
-            if fused:
-                b.layout_dispatch(d["x"])
-            else:
-                b.dispatch(d["x"])
-            b.combine(y)
-            free[i % nb] = torch.cuda.Event()
-            free[i % nb].record(main)
+            back(i, i % nsets)
+            free[i % nsets] = torch.cuda.Event()
+            free[i % nsets].record(main)
     main.wait_stream(side)
+
+
+def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
+    """The steps of serial_steps pipelined on two streams (pipelined()): the
+    route and layout of a group of steps run beside the dispatch and combine
+    of the group before, on the 2 * group layer buffers in `bufs` in turn.
+    Every step does all of its work; the results equal those of
+    serial_steps. When layout and dispatch are one launch, the side stream
+    runs the route only."""
+    fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
+
+    def front(i, s):
+        d = inputs[(first + i) % len(inputs)]
+        bufs[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        if not fused:
+            bufs[s].layout()
+
+    def back(i, s):
+        d = inputs[(first + i) % len(inputs)]
+        if fused:
+            bufs[s].layout_dispatch(d["x"])
+        else:
+            bufs[s].dispatch(d["x"])
+        bufs[s].combine(y)
+
+    pipelined(torch, front, back, len(bufs), steps, side, group)
+
+
+def timed_run(torch, run, graph):
+    """Wall time of run(): captured into one HIP graph, replayed once to
+    upload it and once timed; or launched from the host."""
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            run()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def main():
@@ -627,29 +708,9 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed steps: back to back, nothing but the path on the stream(s)
-    def timed(run):
-        if args.graph:
-            # all timed steps (each with its own inputs) in one graph: the
-            # launches are recorded once, replay issues them without the host
-            graph = torch.cuda.CUDAGraph()
-            torch.cuda.synchronize()
-            with torch.cuda.graph(graph):
-                run()
-            graph.replay()                  # first replay uploads the graph
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graph.replay()
-            torch.cuda.synchronize()
-            return time.perf_counter() - t0
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run()
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    serial_wall = timed(lambda: serial_steps(w, bufs, inputs, y, warm, steps))
-    wall = (timed(lambda: overlapped_steps(torch, M, w, bufs, inputs, y, warm, steps, side))
-            if args.overlap else serial_wall)
+    serial_wall = timed_run(torch, lambda: serial_steps(w, bufs, inputs, y, warm, steps), args.graph)
+    wall = (timed_run(torch, lambda: overlapped_steps(torch, M, w, bufs, inputs, y, warm, steps, side),
+                      args.graph) if args.overlap else serial_wall)
 
     # ---- the same steps again with HIP events between the phases (on the
     # launch stream) for the per-phase times and the roofline; layout and

@@ -101,3 +101,46 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
             for n, v in want[i].items():
                 assert torch.equal(got[n], v), ("graph", rep, i, n)
     say("  graph replays equal the serial steps")
+
+
+def test_pipelined_hierarchical_steps_equal_serial_steps():
+    """The hierarchical pass pipelined the same way (route, expert layout and
+    (token, rank) layout of a group beside the send, fan-out and combines of
+    the group before), replayed from a graph, against the same steps run one
+    after the other."""
+    w = W.WORKLOADS["dsv3"]
+    group, steps = 2, 6
+    inp = W.make_inputs(w, 0)
+    inputs = [dict(logits=dev(inp.logits), bias=dev(inp.bias), x=dev(inp.x))]
+    sets = [(M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, 0,
+                                     dtype=w.dispatch_dtype),
+             M.RankBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
+                                    dtype=w.dispatch_dtype))
+            for _ in range(2 * group)]
+    g = np.random.Generator(np.random.PCG64(4))
+    y = dev(W.random_bf16_rows(g, sets[0][0].num_rows, w.hidden))
+    bench.hierarchical_front(w, sets, inputs, 0, 0)
+    bench.hierarchical_back(sets, inputs, y, 0, 0)
+    torch.cuda.synchronize()
+    n_sent = int(sets[0][1].rank_token_offsets[-1].item())   # partial rows written
+    want = [sets[0][0].combined.clone(), sets[0][1].send_row.clone(),
+            sets[0][1].partial[:n_sent].clone()]
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bench.pipelined(torch, lambda i, s: bench.hierarchical_front(w, sets, inputs, i, s),
+                        lambda i, s: bench.hierarchical_back(sets, inputs, y, i, s),
+                        2 * group, steps, side, group)
+    for rep in range(2):
+        for lb, rb in sets:
+            lb.combined.fill_(-7)
+            rb.send_row.fill_(-7)
+            rb.partial.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for lb, rb in sets:
+            assert torch.equal(lb.combined, want[0]), rep
+            assert torch.equal(rb.send_row, want[1]), rep
+            assert torch.equal(rb.partial[:n_sent], want[2]), rep
+    say("  pipelined hierarchical graph replays equal the serial step")
