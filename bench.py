@@ -541,28 +541,31 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP):
     runs front(i, s) for the steps of one group while the current stream runs
     back(i, s) for the group before; then the current stream waits for the
     side stream once and runs back() for the group. Step i uses buffer set
-    s = i % nsets (nsets = 2 * group), and its front waits until the back of
-    the step that last used that set has released it."""
+    s = i % nsets (nsets = 2 * group), so consecutive groups use the two
+    halves in turn, and the fronts of a group wait, once, until the backs of
+    the group before last (the same sets) are done. One event per group in
+    each direction: each cross-stream edge costs the stream after it a few
+    microseconds."""
     assert nsets == 2 * group
     main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
-    free = []
-    for _ in range(nsets):
+    released = []
+    for _ in range(2):
         e = torch.cuda.Event()
         e.record(main)
-        free.append(e)
-    for g0 in range(0, steps, group):
+        released.append(e)
+    for q, g0 in enumerate(range(0, steps, group)):
         grp = range(g0, min(g0 + group, steps))
-        for i in grp:
-            side.wait_event(free[i % nsets])
-            with torch.cuda.stream(side):
+        side.wait_event(released[q % 2])
+        with torch.cuda.stream(side):
+            for i in grp:
                 front(i, i % nsets)
         ready = torch.cuda.Event()
         ready.record(side)
         main.wait_event(ready)
         for i in grp:
             back(i, i % nsets)
-            free[i % nsets] = torch.cuda.Event()
-            free[i % nsets].record(main)
+        released[q % 2] = torch.cuda.Event()
+        released[q % 2].record(main)
     main.wait_stream(side)
 
 
