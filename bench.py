@@ -573,23 +573,19 @@ def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side, group=PIP
     """The steps of serial_steps pipelined on two streams (pipelined()): the
     route and layout of a group of steps run beside the dispatch and combine
     of the group before, on the 2 * group layer buffers in `bufs` in turn.
-    Every step does all of its work; the results equal those of
-    serial_steps. When layout and dispatch are one launch, the side stream
-    runs the route only."""
-    fused = M.moe_layout_dispatch_is_fused(w.tokens, w.top_k, w.capacity)
+    Layout and dispatch are separate launches here even where
+    moe_layout_dispatch would fuse them (decode-sized capacity mode): the
+    layout is latency-bound, and on the side stream it is hidden. Every step
+    does all of its work; the results equal those of serial_steps."""
 
     def front(i, s):
         d = inputs[(first + i) % len(inputs)]
         bufs[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        if not fused:
-            bufs[s].layout()
+        bufs[s].layout()
 
     def back(i, s):
         d = inputs[(first + i) % len(inputs)]
-        if fused:
-            bufs[s].layout_dispatch(d["x"])
-        else:
-            bufs[s].dispatch(d["x"])
+        bufs[s].dispatch(d["x"])
         bufs[s].combine(y)
 
     pipelined(torch, front, back, len(bufs), steps, side, group)
