@@ -569,7 +569,7 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP):
     main.wait_stream(side)
 
 
-def overlapped_steps(torch, M, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
+def overlapped_steps(torch, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
     """The steps of serial_steps pipelined on two streams (pipelined()): the
     route and layout of a group of steps run beside the dispatch and combine
     of the group before, on the 2 * group layer buffers in `bufs` in turn.
@@ -703,12 +703,12 @@ def main():
     # ---- warmup
     serial_steps(w, bufs, inputs, y, 0, warm)
     if args.overlap:
-        overlapped_steps(torch, M, w, bufs, inputs, y, 0, warm, side)
+        overlapped_steps(torch, w, bufs, inputs, y, 0, warm, side)
     torch.cuda.synchronize()
 
     # ---- timed steps: back to back, nothing but the path on the stream(s)
     serial_wall = timed_run(torch, lambda: serial_steps(w, bufs, inputs, y, warm, steps), args.graph)
-    wall = (timed_run(torch, lambda: overlapped_steps(torch, M, w, bufs, inputs, y, warm, steps, side),
+    wall = (timed_run(torch, lambda: overlapped_steps(torch, w, bufs, inputs, y, warm, steps, side),
                       args.graph) if args.overlap else serial_wall)
 
     # ---- the same steps again with HIP events between the phases (on the

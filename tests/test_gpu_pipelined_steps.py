@@ -79,7 +79,7 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
 
     side = torch.cuda.Stream()
     _poison(bufs)
-    bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side, group)
+    bench.overlapped_steps(torch, w, bufs, inputs, y, 0, steps, side, group)
     torch.cuda.synchronize()
     for i in (steps - 2, steps - 1):
         got = _state(bufs[i % (2 * group)])
@@ -90,7 +90,7 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        bench.overlapped_steps(torch, M, w, bufs, inputs, y, 0, steps, side, group)
+        bench.overlapped_steps(torch, w, bufs, inputs, y, 0, steps, side, group)
     for rep in range(2):
         _poison(bufs)
         torch.cuda.synchronize()
