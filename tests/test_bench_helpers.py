@@ -95,3 +95,108 @@ def test_launch_flags(monkeypatch):
         monkeypatch.setattr(bench.sys, "argv", ["bench.py"] + argv)
         a = bench.parse()
         assert (a.graph, a.overlap) == (graph, overlap), argv
+
+
+class _FakeTorch:
+    """Just enough of torch.cuda for bench.pipelined: streams are queues of
+    operations, events point at the last operation of the stream they were
+    recorded on, and a wait makes the next operation of a stream depend on
+    it. Every enqueued operation records what it must come after."""
+
+    def __init__(self):
+        self.ops = []            # (stream, label, set of op indices it depends on)
+        self.current = "main"
+        torch_self = self
+
+        class Event:
+            def __init__(self):
+                self.op = None   # index of the op the event marks, None = nothing
+
+            def record(self, stream):
+                self.op = torch_self._last(stream.name)
+
+        class Stream:
+            def __init__(self, name="side"):
+                self.name = name
+                self.pending = set()
+
+            def wait_event(self, e):
+                if e.op is not None:
+                    torch_self.waits[self.name].add(e.op)
+
+            def wait_stream(self, other):
+                last = torch_self._last(other.name)
+                if last is not None:
+                    torch_self.waits[self.name].add(last)
+
+        class _Ctx:
+            def __init__(self, s):
+                self.s, self.prev = s, None
+
+            def __enter__(self):
+                self.prev, torch_self.current = torch_self.current, self.s.name
+
+            def __exit__(self, *a):
+                torch_self.current = self.prev
+
+        self.waits = {"main": set(), "side": set()}
+        self.main_stream = Stream("main")
+        cuda = type("cuda", (), {})()
+        cuda.Event = Event
+        cuda.Stream = Stream
+        cuda.current_stream = lambda: self.main_stream if self.current == "main" else self.side_stream
+        cuda.stream = lambda s: _Ctx(s)
+        self.cuda = cuda
+        self.side_stream = Stream("side")
+
+    def _last(self, stream):
+        for j in range(len(self.ops) - 1, -1, -1):
+            if self.ops[j][0] == stream:
+                return j
+        return None
+
+    def op(self, label):
+        s = self.current
+        deps = set(self.waits[s])
+        prev = self._last(s)
+        if prev is not None:
+            deps.add(prev)
+        self.waits[s] = set()
+        self.ops.append((s, label, deps))
+
+    def before(self, a, b):
+        """Op a happens before op b (transitively)."""
+        todo, seen = [b], set()
+        while todo:
+            x = todo.pop()
+            for d in self.ops[x][2]:
+                if d == a:
+                    return True
+                if d not in seen:
+                    seen.add(d)
+                    todo.append(d)
+        return False
+
+
+@pytest.mark.parametrize("group,steps", [(4, 13), (1, 5), (2, 8)])
+def test_pipelined_step_dependencies(group, steps):
+    """bench.pipelined on a fake torch: the side stream runs the fronts, the
+    current stream the backs; every step's back comes after its front, every
+    front after the back of the step that last used its buffer set, and the
+    fronts of a group may run beside the backs of the group before."""
+    ft = _FakeTorch()
+    nsets = 2 * group
+    bench.pipelined(ft, lambda i, s: ft.op(("front", i, s)), lambda i, s: ft.op(("back", i, s)),
+                    nsets, steps, ft.side_stream, group)
+    idx = {op[1]: n for n, op in enumerate(ft.ops)}
+    for i in range(steps):
+        s = i % nsets
+        f, b = idx[("front", i, s)], idx[("back", i, s)]
+        assert ft.ops[f][0] == "side" and ft.ops[b][0] == "main"
+        assert ft.before(f, b), i
+        if i >= nsets:                        # the previous user of set s is done first
+            assert ft.before(idx[("back", i - nsets, s)], f), i
+    # overlap: a front of group q + 1 does not wait for the backs of group q
+    for i in range(group, steps):
+        for j in range(i - i % group - group, i - i % group):
+            assert not ft.before(idx[("back", j, j % nsets)], idx[("front", i, i % nsets)]), (i, j)
