@@ -82,14 +82,37 @@ __device__ __forceinline__ uint64_t candidate(float key, int e) {
   return ((uint64_t)ordered_bits(key) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-// Wave max of a 32-bit value, in every lane.
+// Wave max of a 32-bit value as a wave-uniform (scalar) value: the max of
+// each 16-lane row by DPP, then the gfx9 row broadcasts carry the row maxima
+// to lane 63 (lane 15 of each row into the next row, in rows 1 and 3; then
+// lane 31 into rows 2 and 3), and lane 63 is read into a scalar register.
+// Rows left out of a broadcast receive 0, the identity of an unsigned max.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0xB1>(v));
   v = max(v, dpp_u32<0x4E>(v));
   v = max(v, dpp_u32<0x141>(v));
   v = max(v, dpp_u32<0x140>(v));
-  v = max(v, xor16_u32(v));
-  return max(v, xor32_u32(v));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Max and fp64 sum over the calling lane's 16-lane row, in every lane of the
+// row. With k <= 16 every chosen slot sits in row 0 and the other lanes hold
+// -inf (max) or +0.0 (sum), so the row result equals the wave result bit for
+// bit: the first four steps of wave_max_f32 / wave_sum_f64 are these, and
+// the remaining two only combine it with -inf or add +0.0.
+__device__ __forceinline__ float row_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  return fmaxf(v, dpp_f32<0x140>(v));
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  return v + dpp_f64<0x140>(v);
 }
 
 // Top-2 merge of (largest, second largest) pairs.
@@ -257,14 +280,16 @@ __global__ __launch_bounds__(256) void route_kernel(
     }
   }
 
+  // k is uniform: the branches below do not diverge
   double u;
   if (sigmoid) {
     u = lane < k ? (double)my_score : 0.0;
   } else {
-    const float m = wave_max_f32(lane < k ? my_score : -INFINITY);
+    const float mv = lane < k ? my_score : -INFINITY;
+    const float m = k <= 16 ? row_max_f32(mv) : wave_max_f32(mv);
     u = lane < k ? exp_f64((double)my_score - (double)m) : 0.0;
   }
-  const double total = wave_sum_f64(u);
+  const double total = k <= 16 ? row_sum_f64(u) : wave_sum_f64(u);
   if (lane < k) {
     idx_out[(size_t)t * k + lane] = my_e;
     w_out[(size_t)t * k + lane] = (float)(u / total);
