@@ -16,6 +16,8 @@
 // FMA, so k x 1 KiB per wave are in flight; the fp32 accumulators are
 // rounded once to bf16 (nearest even) and stored with one 16-byte store.
 
+#include <atomic>
+
 #include "kernels.h"
 #include "wave.h"
 
@@ -113,13 +115,36 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // outputs in registers (8 per item) and stores all of them after the last
 // item's rows have been read. The next item's rows and weights are loaded
 // while the current rows are in flight. Launched at kHeldBlocksPerCu, so the
-// grid (at most kHeldWaves waves) is resident at once: the chip reads the
+// grid (at most held_waves() waves) is resident at once: the chip reads the
 // expert rows first and writes the outputs in one burst at the end, instead
 // of mixing the output stores into the read stream. The arithmetic is the
 // combine_kernel's: the same fma chain in slot order and one rounding.
 constexpr int kHeldPart = 2 * MOE_WAVE;              // chunks per item
 constexpr int kHeldBlocksPerCu = 2;                  // ~210 registers per lane
-constexpr int kHeldWaves = 256 * kHeldBlocksPerCu * kWavesPerBlock;   // 256 CUs
+
+// Waves the device holds at once at kHeldBlocksPerCu (2,048 on a whole
+// MI355X, 256 CUs), from its compute-unit count, read once per device; 0 if
+// the count cannot be read. A partition with fewer CUs gets a smaller grid,
+// which the bounds on items per wave below then usually turn away.
+long long held_waves() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return (long long)n * kHeldBlocksPerCu * kWavesPerBlock;
+}
 constexpr int kHeldMinItems = 8, kHeldMaxItems = 16;
 // Rows of at least 7 parts (hidden > 6144): measured against the per-item
 // kernel at k = 8, held outputs were 3-10% faster on rows of 7 parts (hidden
@@ -354,14 +379,16 @@ void launch_held(int waves, hipStream_t stream, int T, int nch, int parts, int n
 }
 
 // k = 8, rows of at least kHeldMinParts parts, 8..16 items per wave over
-// kHeldWaves waves: the held-output kernel (returns false otherwise).
+// held_waves() waves: the held-output kernel (returns false otherwise).
 bool try_launch_held(int T, int nch, int k, int num_rows, const void* y,
                      const int32_t* dst_row, const float* w, void* out, hipStream_t stream) {
   if (k != 8) return false;
   const int parts = (nch + kHeldPart - 1) / kHeldPart;
   if (parts < kHeldMinParts) return false;
+  const long long max_waves = held_waves();
+  if (max_waves <= 0) return false;
   const long long items = (long long)T * parts;
-  const long long ipw = (items + kHeldWaves - 1) / kHeldWaves;
+  const long long ipw = (items + max_waves - 1) / max_waves;
   if (ipw < kHeldMinItems || ipw > kHeldMaxItems) return false;
   const int waves = (int)((items + ipw - 1) / ipw);
 #define MOE_HELD(n) \
