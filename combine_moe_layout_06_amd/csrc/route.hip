@@ -193,14 +193,24 @@ __global__ __launch_bounds__(256) void route_kernel(
       if (lpg >= 32) merge_top2(m1, m2, xor16_f32(m1), xor16_f32(m2));
       if (lpg >= 64) merge_top2(m1, m2, xor32_f32(m1), xor32_f32(m2));
       const float gscore = gs == 1 ? m1 : m1 + m2;
-      // rank of the lane's group (ties to the lower group); group q's score
-      // is in lane q*lpg
+      // rank of the lane's group (ties to the lower group); every lane of
+      // group q holds its score
       const int my_group = lane / lpg;
       const uint32_t mine = ordered_bits(gscore);
       int rank = 0;
-      for (int q = 0; q < G; ++q) {
-        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, q * lpg);
-        rank += (o > mine) || (o == mine && q < my_group);
+      if (G <= lpg) {
+        // lane r of each group compares its group with group r (r < G);
+        // the group's rank is the count of its lanes whose group r beats it
+        const int r = lane & (lpg - 1);
+        const uint32_t o = (uint32_t)__shfl((int)mine, r * lpg);
+        const uint64_t beats = wave_ballot(r < G && (o > mine || (o == mine && r < my_group)));
+        const uint64_t seg = beats >> (my_group * lpg);
+        rank = __popcll(seg & ((1ull << lpg) - 1));  // G >= 2, so lpg <= 32
+      } else {
+        for (int q = 0; q < G; ++q) {
+          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, q * lpg);
+          rank += (o > mine) || (o == mine && q < my_group);
+        }
       }
 #pragma unroll
       for (int i = 0; i < VPL; ++i) ok[i] = ok[i] && rank < kg;
@@ -230,43 +240,38 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
   if (!live) return;  // whole wave; no barrier follows
 
-  // The lane's candidates sorted by key, descending; equal keys keep slot
-  // order (adjacent swaps on strictly greater keys only). 0 = no candidate:
-  // every finite key maps above it.
+  // The lane's candidates as ordered keys; 0 = no candidate (every finite
+  // key maps above it).
   uint32_t sk[VPL];
-  int sj[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    sk[i] = ok[i] ? ordered_bits(key[i]) : 0u;
-    sj[i] = i;
-#pragma unroll
-    for (int p = i; p >= 1; --p) {
-      const bool up = sk[p] > sk[p - 1];
-      const uint32_t a = sk[p - 1], b = sk[p];
-      const int ja = sj[p - 1], jb = sj[p];
-      sk[p - 1] = up ? b : a;
-      sk[p] = up ? a : b;
-      sj[p - 1] = up ? jb : ja;
-      sj[p] = up ? ja : jb;
-    }
-  }
-  // k rounds: the wave max of the lanes' heads wins; among lanes holding
-  // it the lowest lane, which holds the lowest expert; that lane pops.
+  for (int i = 0; i < VPL; ++i) sk[i] = ok[i] ? ordered_bits(key[i]) : 0u;
+  // k rounds. The wave max of the lanes' best remaining keys wins; among the
+  // slots holding it, the lowest lane and in it the lowest slot, i.e. the
+  // lowest expert (lane l holds experts [l*VPL, l*VPL + VPL)). That slot is
+  // cleared, and lane j keeps the winner's expert.
   int my_e = -1;
   for (int j = 0; j < k; ++j) {
-    const uint32_t top = wave_max_u32(sk[0]);
-    const uint64_t holders = wave_ballot(sk[0] == top);
-    const int owner = (int)__builtin_ctzll(holders);
-    const int e_win = owner * VPL + __builtin_amdgcn_readlane(sj[0], owner);
-    if (lane == owner) {
+    uint32_t head = sk[0];
 #pragma unroll
-      for (int p = 0; p + 1 < VPL; ++p) {
-        sk[p] = sk[p + 1];
-        sj[p] = sj[p + 1];
-      }
-      sk[VPL - 1] = 0u;
+    for (int i = 1; i < VPL; ++i) head = max(head, sk[i]);
+    const uint32_t top = wave_max_u32(head);
+    uint64_t hit[VPL];
+    uint64_t any = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      hit[i] = wave_ballot(sk[i] == top);
+      any |= hit[i];
     }
-    if (lane == j) my_e = e_win;
+    const int owner = (int)__builtin_ctzll(any);
+    int slot = 0;
+#pragma unroll
+    for (int i = VPL - 1; i >= 0; --i)
+      if ((hit[i] >> owner) & 1ull) slot = i;
+    const bool in_owner = lane == owner;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (i == slot) sk[i] = in_owner ? 0u : sk[i];
+    if (lane == j) my_e = owner * VPL + slot;
   }
   // score of the chosen expert, from the lane that holds it
   float my_score = 0.0f;
