@@ -59,6 +59,8 @@ def gpu_route(logits, bias, k, score_fn, G, kg):
 def _logits(g, t, e, kind):
     if kind == "int":      # small integers: many exact ties
         return g.integers(-3, 4, size=(t, e)).astype(np.float32)
+    if kind == "const":    # every key equal: the tie order alone decides
+        return np.full((t, e), 0.25, dtype=np.float32)
     return g.standard_normal((t, e), dtype=np.float32)
 
 
@@ -100,6 +102,11 @@ ROUTE_CASES = [
     (250, 256, 8, 0, 1, 1, None, "int"),
     (220, 512, 32, 0, 1, 1, "int", "int"),
     (129, 131, 7, 1, 1, 1, "normal", "normal"),
+    # all logits equal, no bias: the lowest groups, then the lowest experts
+    (64, 256, 8, 1, 8, 4, None, "const"),
+    (33, 512, 32, 1, 16, 8, None, "const"),
+    (40, 256, 8, 0, 1, 1, None, "const"),
+    (70, 128, 8, 1, 4, 2, None, "const"),
 ]
 
 
@@ -120,8 +127,11 @@ def test_route_parity(case):
     idx_o, w_o = O.route(logits, k, fn, G, kg, bias)
     nd = assert_route_close(idx_g, w_g, idx_o, w_o, oracle_keys(logits, bias, fn), str(case))
     say("  tokens with a near-tie difference:", nd)
-    if fn == 0 or lk == "int":
+    if fn == 0 or lk in ("int", "const"):
         assert nd == 0   # no transcendental decides these choices
+    if lk == "const" and bias_kind is None:
+        # keys all equal: groups 0..kg-1 are kept and the experts come in index order
+        assert (idx_g == np.arange(k, dtype=np.int32)[None, :]).all()
     assert idx_g.dtype == np.int32 and ((idx_g >= 0) & (idx_g < e)).all()
 
 

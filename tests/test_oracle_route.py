@@ -145,3 +145,15 @@ def test_qwen3_skew_load_is_about_ten_times_mean():
     c = np.bincount(idx.ravel(), minlength=w.experts)
     ratio = c.max() / (w.tokens * w.top_k / w.experts)
     assert 9.5 <= ratio <= 10.5
+
+
+@pytest.mark.parametrize("t,e,k,fn,G,kg", [(5, 256, 8, 1, 8, 4), (3, 512, 32, 1, 16, 8),
+                                           (4, 256, 8, 0, 1, 1), (6, 128, 8, 1, 4, 2)])
+def test_all_keys_equal_picks_the_lowest_experts(t, e, k, fn, G, kg):
+    """Every key equal: all group scores tie, so groups 0..kg-1 are kept (ties to the lower
+    group), and inside them every key ties, so experts 0..k-1 are chosen in index order (ties
+    to the lower expert). Each weight is s / (k*s) or exp(0) / k, i.e. 1/k to rounding."""
+    logits = np.full((t, e), 0.25, dtype=np.float32)
+    idx, w = O.route(logits, k, fn, G, kg, None)
+    assert (idx == np.arange(k)[None, :]).all()
+    assert np.abs(w.astype(np.float64) - 1.0 / k).max() <= 2.0 ** -23
