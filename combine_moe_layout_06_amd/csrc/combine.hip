@@ -39,12 +39,6 @@ constexpr int kCombineBackwardBlocksPerCu = 4;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ void fma_row(float (&acc)[8], float w, const u32x4& v) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -56,7 +50,7 @@ __device__ __forceinline__ void fma_row(float (&acc)[8], float w, const u32x4& v
 __device__ __forceinline__ u32x4 pack_row(const float (&acc)[8]) {
   u32x4 r;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) r[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+  for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
   return r;
 }
 
@@ -302,7 +296,7 @@ __device__ __forceinline__ u32x4 scale_row(const u32x4& g, float w) {
   u32x4 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    r[q] = bf16_rne(w * bf16_lo(g[q])) | (bf16_rne(w * bf16_hi(g[q])) << 16);
+    r[q] = pack_bf16x2(w * bf16_lo(g[q]), w * bf16_hi(g[q]));
   return r;
 }
 

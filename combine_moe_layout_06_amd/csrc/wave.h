@@ -28,6 +28,18 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 #endif
 }
 
+// Two fp32 values rounded to bf16 (nearest, ties to even) and packed, `lo`
+// in the low half, with gfx950's packed convert (v_cvt_pk_bf16_f32). On the
+// device it gives the integer rounding (b + 0x7FFF + lsb) >> 16 for every
+// non-NaN fp32 pattern, infinities, overflow and subnormals included (all
+// 2^32 patterns compared); a NaN stays a quiet NaN with its payload.
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const moe_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, moe_bf16x2));
+}
+
 __device__ __forceinline__ int lane_id() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }

@@ -397,6 +397,50 @@ def test_combine_parity(case):
     say("  bit-exact fraction %.6f" % frac)
 
 
+def _rounding_weights():
+    """fp32 values whose bf16 rounding covers every exponent (subnormals and the largest
+    binade included), both signs, the low 16 bits below, at and above the halfway point, kept
+    bits even and odd and all ones (a carry into the exponent, up to infinity), and the two
+    infinities. NaN is left out: its bits are not part of the contract."""
+    lows = (0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF)
+    kept = (0x00, 0x01, 0x7E, 0x7F)
+    pats = [(sign << 31) | (e << 23) | (m << 16) | lo
+            for sign in (0, 1) for e in range(255) for m in kept for lo in lows]
+    pats += [0x7F800000, 0xFF800000]
+    return np.array(pats, dtype=np.uint32).view(np.float32)
+
+
+def test_combine_rounds_every_binade_like_the_oracle():
+    """With k = 1 and expert rows of 1.0 the fp32 accumulator is the weight itself, so the
+    output is the weight's bf16 rounding: compared with the oracle on every binade and
+    rounding boundary (the per-item kernel)."""
+    w = _rounding_weights()
+    t, h = len(w), 8
+    y = np.full((t, h), 0x3F80, np.uint16)                   # bf16 1.0
+    dst = np.arange(t, dtype=np.int32).reshape(t, 1)
+    got = gpu_combine(y, dst, w.reshape(t, 1), t, h)
+    want, _ = O.combine(y, dst, w.reshape(t, 1))
+    assert np.array_equal(got, want)
+    # the sum starts from +0.0, so -0.0 comes out as +0.0
+    assert np.array_equal(want[:, 0], O.round_to_bf16(w.astype(np.float64) + 0.0))
+
+
+def test_held_combine_rounds_every_binade_like_the_oracle():
+    """The same rounding cases through the held-output kernel (k = 8, rows of 7 parts,
+    3000 tokens: 11 items per wave): slot 0 carries the weight, the other seven weigh 0."""
+    w = _rounding_weights()
+    t, h, k = 3000, 7168, 8
+    y = np.full((k, h), 0x3F80, np.uint16)
+    dst = np.tile(np.arange(k, dtype=np.int32), (t, 1))
+    for start in range(0, len(w), t):
+        part = np.resize(w[start:start + t], t)               # the last call repeats values
+        wt = np.zeros((t, k), np.float32)
+        wt[:, 0] = part
+        got = gpu_combine(y, dst, wt, t, h)
+        want, _ = O.combine(y, dst, wt)
+        assert np.array_equal(got, want), "calls from weight %d" % start
+
+
 def test_combine_ignores_rows_past_num_rows():
     g = np.random.Generator(np.random.PCG64(6))
     y = W.random_bf16_rows(g, 50, 256)
