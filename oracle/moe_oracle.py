@@ -39,6 +39,11 @@ Readings where the pages are silent (each is also listed in the design notes):
   R6 FP8: OCP e4m3fn, 1x128 blocks along H, scale = amax/448 in fp32, codes
      by round-to-nearest-even of x*(448/amax) with saturation to +-448.
   R7 capacity: pairs beyond `cap` in an expert's stable order are dropped.
+  R14 combine arithmetic: the weighted sum is accumulated in fp32, one fused
+     multiply-add per pair in slot order starting from +0, and rounded once
+     to bf16 (the combine contract: fp32 accumulation in a fixed slot order);
+     the same rule serves the gradient of dispatch and both levels of the
+     hierarchical combine.
   R18 MXFP8: 1x32 blocks, E8M0 scale 2^(floor(log2 amax) - 8), e4m3fn codes
      of x / scale with round-to-nearest-even and saturation.
   R20 deduplicated dispatch: one row per (token, rank) with at least one
@@ -456,26 +461,58 @@ def expert_dequant_mx(codes: np.ndarray, sbytes: np.ndarray) -> np.ndarray:
 # Combine: weighted sum of each token's expert outputs
 # ---------------------------------------------------------------------------
 
+def fma_f32(a, b, c) -> np.ndarray:
+    """fp32 fused multiply-add, elementwise: a*b + c computed exactly and
+    rounded once to fp32 (nearest, ties to even), for fp32 inputs.
+
+    The product of two fp32 values has at most 48 significant bits, so it is
+    exact in fp64. The sum p + c is formed in fp64 together with its exact
+    rounding error (Knuth's two-sum), so that p + c = s + e exactly. Rounding
+    s to fp32 is then the correct rounding of p + c, except in one case: s
+    lies exactly halfway between two fp32 values while e is not zero. The
+    exact sum is then off the midpoint on the side of e, and the result is
+    the fp32 neighbour on that side (fp32 midpoints are fp64 numbers, so the
+    fp64 rounding of p + c can land on one but never step over one)."""
+    a64 = np.asarray(a, dtype=F32).astype(F64)
+    b64 = np.asarray(b, dtype=F32).astype(F64)
+    c64 = np.asarray(c, dtype=F32).astype(F64)
+    p = a64 * b64
+    s = p + c64
+    bv = s - p
+    e = (p - (s - bv)) + (c64 - bv)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = s.astype(F32)
+        r64 = r.astype(F64)
+        side = np.where(s > r64, np.float32(np.inf), np.float32(-np.inf))
+        n = np.nextafter(r, side)
+        tie = (s != r64) & np.isfinite(r64) & (s - r64 == n.astype(F64) - s)
+        fix = tie & (e != 0) & ((e > 0) == (s > r64))
+    return np.where(fix, n, r).astype(F32)
+
+
 def combine(y_bits: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray):
     """out[t] = bf16( sum_j w[t, j] * y[dst_row[t, j]] ) over the pairs that
     have a row (glossary "Expert Parallelism", Phase 2: results return to the
-    token's origin and are summed weighted by the router scores). The sum is
-    taken in fp64 and rounded once to bf16; dropped pairs add nothing and the
-    weights are not renormalised.
+    token's origin and are summed weighted by the router scores).
+
+    The sum is accumulated in fp32 in slot order, one fused multiply-add per
+    pair: acc = +0; for j = 0..k-1 with a row, acc = fma_f32(w[t, j],
+    y[dst_row[t, j]], acc); then acc is rounded to bf16 (nearest even).
+    Dropped pairs add nothing and the weights are not renormalised.
     Returns (out bits [T, H] uint16, abs_sum [T, H] fp64 = sum_j |w y|)."""
     t, k = dst_row.shape
     h = y_bits.shape[1]
-    acc = np.zeros((t, h), dtype=F64)
+    acc = np.zeros((t, h), dtype=F32)
     mag = np.zeros((t, h), dtype=F64)
     for j in range(k):
         d = dst_row[:, j]
         live = d >= 0
         if not live.any():
             continue
-        yj = bf16_to_f32(y_bits[d[live]]).astype(F64)
-        term = topk_w[live, j].astype(F64)[:, None] * yj
-        acc[live] += term
-        mag[live] += np.abs(term)
+        yj = bf16_to_f32(y_bits[d[live]])
+        wj = topk_w[live, j].astype(F32)[:, None]
+        acc[live] = fma_f32(wj, yj, acc[live])
+        mag[live] += np.abs(wj.astype(F64) * yj.astype(F64))
     return round_to_bf16(acc), mag
 
 
@@ -488,7 +525,8 @@ def combine(y_bits: np.ndarray, dst_row: np.ndarray, topk_w: np.ndarray):
 def dispatch_backward(grad_rows_bits: np.ndarray, dst_row: np.ndarray):
     """Gradient of dispatch with respect to x: each token collects the
     gradients of its rows, dx[t] = bf16( sum_j g[dst_row[t, j]] ) (the
-    adjoint of copying x[t] to k rows). It is combine with unit weights.
+    adjoint of copying x[t] to k rows). It is combine with unit weights: an
+    fp32 sum in slot order (fma with weight 1), rounded once to bf16.
     Returns (dx bits [T, H], abs_sum [T, H])."""
     t, k = dst_row.shape
     return combine(grad_rows_bits, dst_row, np.ones((t, k), dtype=F32))
@@ -613,14 +651,15 @@ def combine_local(y_bits: np.ndarray, dst_row: np.ndarray, rank_row: np.ndarray,
         partial[rank_row[t, j]] = bf16( sum over slots j' of t with
             rank_row[t, j'] = rank_row[t, j] and a kept expert row of
             w[t, j'] * y[dst_row[t, j']] )
-    taken in fp64 and rounded once to bf16 (the partial travels as a bf16 row,
-    reading R20). A (token, rank) row whose pairs were all dropped by capacity
-    is still written, as +0.
+    accumulated as combine() does: in fp32, one fused multiply-add per pair,
+    in slot order, starting from +0, then rounded to bf16 (the partial
+    travels as a bf16 row, reading R20). A (token, rank) row whose pairs
+    were all dropped by capacity is still written, as +0.
     Returns (partial bits [num_rank_rows, H], written, abs_sum [num_rank_rows,
     H] = sum of |w y| of the row's terms)."""
     t, k = dst_row.shape
     h = y_bits.shape[1]
-    acc = np.zeros((num_rank_rows, h), dtype=F64)
+    acc = np.zeros((num_rank_rows, h), dtype=F32)
     mag = np.zeros((num_rank_rows, h), dtype=F64)
     written = np.zeros(num_rank_rows, dtype=bool)
     for j in range(k):
@@ -630,20 +669,22 @@ def combine_local(y_bits: np.ndarray, dst_row: np.ndarray, rank_row: np.ndarray,
         keep = has & (dst_row[:, j] >= 0)
         if not keep.any():
             continue
-        term = topk_w[keep, j].astype(F64)[:, None] * \
-            bf16_to_f32(y_bits[dst_row[keep, j]]).astype(F64)
+        wj = topk_w[keep, j].astype(F32)[:, None]
+        yj = bf16_to_f32(y_bits[dst_row[keep, j]])
         # a (token, rank) row appears at most once in one slot column (the
-        # rows of different tokens differ), so the indexed sums add each
-        # term once
-        acc[s[keep]] += term
-        mag[s[keep]] += np.abs(term)
+        # rows of different tokens differ), so each row takes one step here
+        # and its steps run in slot order
+        rows = s[keep]
+        acc[rows] = fma_f32(wj, yj, acc[rows])
+        mag[rows] += np.abs(wj.astype(F64) * yj.astype(F64))
     return round_to_bf16(acc), written, mag
 
 
 def combine_partials(partial_bits: np.ndarray, send_row: np.ndarray):
     """Second level: out[t] = bf16( sum over t's (token, rank) rows of the
-    partial rows ), fp64 sum, one rounding. Each row is named once, at the
-    rank's first slot (send_row). Returns (out bits [T, H], abs_sum)."""
+    partial rows ), accumulated in fp32 in slot order as combine() does with
+    unit weights. Each row is named once, at the rank's first slot
+    (send_row). Returns (out bits [T, H], abs_sum)."""
     t, k = send_row.shape
     return combine(partial_bits, send_row, np.ones((t, k), dtype=F32))
 

@@ -1,7 +1,8 @@
 """Pins of the oracle's dispatch and combine: the round trip with identity
 experts and normalised weights returns x exactly, FP8 payloads are half the
-bf16 bytes and dequantise within the e4m3 error bound, and combine agrees
-with an exactly summed (math.fsum) reference on small inputs."""
+bf16 bytes and dequantise within the e4m3 error bound, and combine (an fp32
+chain in slot order) stays within its rounding bound of an exactly summed
+(math.fsum) reference on small inputs."""
 
 import math
 
@@ -83,7 +84,7 @@ def test_fp8_zero_and_tiny_blocks():
     assert np.all(codes[1, 128:] == 0) and sc[1, 1] == 0 and sc[1, 0] > 0
 
 
-def test_combine_matches_exact_sum():
+def test_combine_within_chain_bound_of_exact_sum():
     g = np.random.Generator(np.random.PCG64(21))
     t, k, rows, h = 40, 3, 90, 16
     y = W.random_bf16_rows(g, rows, h)
@@ -98,9 +99,11 @@ def test_combine_matches_exact_sum():
                      if dst[i, j] >= 0]
             exact = math.fsum(terms)
             got = float(O.bf16_to_f32(out[i:i + 1, c:c + 1])[0, 0])
-            # the oracle's result is the bf16 value nearest the exact sum
-            ulp = 2.0 ** (math.floor(math.log2(abs(exact))) - 7) if exact else 2.0 ** -133
-            assert abs(got - exact) <= ulp / 2 * (1 + 1e-12)
+            # half a bf16 ulp of the output, plus one fp32 rounding per
+            # live slot of the chain
+            big = max(abs(got), abs(exact), 2.0 ** -126)
+            ulp = 2.0 ** (math.floor(math.log2(big)) - 7)
+            assert abs(got - exact) <= (ulp / 2 + k * 2.0 ** -24 * mag[i, c]) * (1 + 1e-12)
             assert mag[i, c] == pytest.approx(math.fsum(abs(v) for v in terms))
 
 

@@ -14,6 +14,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from synth import workloads as W
+from exact_f32 import chain_f32  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -185,7 +186,9 @@ def test_dedup_dispatch_then_fanout_equals_flat_dispatch(fmt, cap):
 
 
 def _loop_partials(y, dst, rank_row, w, nr):
-    """math.fsum over each (token, rank) row's terms, one bf16 rounding."""
+    """Each (token, rank) row's terms in slot order through the Fraction fp32
+    chain of tests/exact_f32.py, one bf16 rounding at the end; math.fsum of
+    the terms' magnitudes."""
     t, k = dst.shape
     h = y.shape[1]
     yf = O.bf16_to_f32(y)
@@ -195,19 +198,21 @@ def _loop_partials(y, dst, rank_row, w, nr):
             s = int(rank_row[i, j])
             if s < 0:
                 continue
-            terms.setdefault(s, [[] for _ in range(h)])
+            terms.setdefault(s, [])
             if dst[i, j] >= 0:
-                for c in range(h):
-                    terms[s][c].append(float(w[i, j]) * float(yf[dst[i, j], c]))
+                terms[s].append((w[i, j], yf[dst[i, j]]))
     out, mag = {}, {}
-    for s, cols in terms.items():
-        out[s] = O.round_to_bf16(np.array([math.fsum(v) for v in cols]))
-        mag[s] = np.array([math.fsum(abs(x) for x in v) for v in cols])
+    for s, pairs in terms.items():
+        ws = [p[0] for p in pairs]
+        out[s] = O.round_to_bf16(np.array(
+            [chain_f32(ws, [p[1][c] for p in pairs]) for c in range(h)], np.float32))
+        mag[s] = np.array([math.fsum(abs(float(p[0]) * float(p[1][c])) for p in pairs)
+                           for c in range(h)])
     return out, mag
 
 
 @pytest.mark.parametrize("seed,cap", [(21, 0), (22, 3)])
-def test_partials_match_fsum_loops(seed, cap):
+def test_partials_match_loop_chains(seed, cap):
     g = W.rng(seed)
     t, e, r, k, h = 30, 12, 3, 4, 24
     idx = W.random_topk_idx(g, t, e, k, mask_frac=0.15)
@@ -222,13 +227,15 @@ def test_partials_match_fsum_loops(seed, cap):
     for s, row in want.items():
         assert np.array_equal(partial[s], row), s
         np.testing.assert_allclose(mag[s], want_mag[s], rtol=1e-12, atol=0)
-    # final level: fsum of the partial values, one rounding
+    # final level: the unit-weight chain of the partials in slot order, one
+    # rounding
     out, _ = O.combine_partials(partial, rl["send_row"])
     pf = O.bf16_to_f32(partial)
     for i in range(t):
         rows = [int(s) for s in rl["send_row"][i] if s >= 0]
-        want_t = O.round_to_bf16(np.array([math.fsum(float(pf[s, c]) for s in rows)
-                                           for c in range(h)]))
+        want_t = O.round_to_bf16(np.array(
+            [chain_f32([1.0] * len(rows), [pf[s, c] for s in rows]) for c in range(h)],
+            np.float32))
         assert np.array_equal(out[i], want_t), i
 
 
