@@ -5,7 +5,9 @@ CPU fallback (CPU only).
   and the standard library; the seeded input generators (synth) import
   neither side.
 - bench.py reaches the oracle only from its cpu_baseline functions, and
-  __graft_entry__.py only from smoke().
+  __graft_entry__.py only from smoke() and, to compile the oracle's C twin
+  (building the checker, not using it), from build().
+- The oracle's C source includes only the C standard library.
 - The HIP sources include only each other and include/.
 - A missing library, or host tensors handed to an entry point, raise
   instead of computing anything on the CPU.
@@ -60,7 +62,7 @@ def test_package_never_imports_the_oracle():
 
 def test_oracle_imports_only_numpy_and_the_standard_library():
     allowed = {"numpy", "__future__", "math", "typing", "dataclasses", "itertools",
-               "functools", "struct"}
+               "functools", "struct", "ctypes", "os", "subprocess"}
     for path in _py_files(os.path.join(ROOT, "oracle")):
         mods = {m for m, _ in _imports(_parse(path))}
         assert mods <= allowed, (path, mods - allowed)
@@ -84,7 +86,20 @@ def test_graft_entry_reaches_the_oracle_only_from_smoke():
             if m == "oracle"]
     assert uses
     for _, func in uses:
-        assert func == "smoke", func
+        assert func in ("smoke", "build"), func
+    src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
+    build_src = src[src.index("def build"):src.index("def smoke")]
+    assert "c_twin.build()" in build_src and "O." not in build_src
+
+
+def test_oracle_c_source_includes_only_the_standard_library():
+    std = {"<math.h>", "<stdint.h>", "<string.h>", "<stdlib.h>", "<stddef.h>"}
+    for name in os.listdir(os.path.join(ROOT, "oracle")):
+        if name.endswith((".c", ".h")):
+            with open(os.path.join(ROOT, "oracle", name)) as f:
+                for line in f:
+                    if line.strip().startswith("#include"):
+                        assert line.split()[1] in std, (name, line)
 
 
 def test_hip_sources_include_only_their_own_headers():
