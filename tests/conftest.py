@@ -9,3 +9,20 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the combine cases checked bit for bit in this session (name and
+    element count) to gpurun_out/combine_exactness.txt when that folder
+    exists."""
+    helpers = sys.modules.get("gpu_helpers")
+    log = getattr(helpers, "EXACT_LOG", None)
+    out_dir = os.path.join(ROOT, "gpurun_out")
+    if not log or not os.path.isdir(out_dir):
+        return
+    total = sum(n for _, n in log)
+    with open(os.path.join(out_dir, "combine_exactness.txt"), "w") as f:
+        f.write("combine cases whose every output equals the oracle's bits: %d cases, "
+                "%d outputs\n" % (len(log), total))
+        for what, n in log:
+            f.write("%s\t%d\n" % (what, n))

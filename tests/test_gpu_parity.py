@@ -3,8 +3,10 @@ by element, on the same seeded inputs.
 
 Bars: bit-exact for expert choices (up to logged near-ties of the fp64
 transcendentals), layout outputs, bf16 rows and FP8 codes/scales; routing
-weights within 1 fp32 ulp; combine within 1 bf16 ulp plus the fp32
-accumulation bound (gpu_helpers). Output buffers are pre-filled with 0xFF and
+weights within 1 fp32 ulp; combine outputs equal to the oracle's bits (the
+oracle runs the combine's fp32 slot-order chain; the contract's bound is one
+bf16 ulp). Full-size layers take the FP8 codes and the combine from the
+oracle's C twin, pinned bit for bit to the numpy oracle. Output buffers are pre-filled with 0xFF and
 followed by guard rows, so unwritten rows and stray writes are caught.
 """
 
@@ -18,8 +20,9 @@ torch = pytest.importorskip("torch")
 
 import combine_moe_layout_06_amd as M  # noqa: E402
 from combine_moe_layout_06_amd import LayerBuffers  # noqa: E402
-from gpu_helpers import (assert_bf16_within_ulp, assert_combine_close,  # noqa: E402
+from gpu_helpers import (assert_bf16_within_ulp, assert_combine_exact,  # noqa: E402
                          assert_route_close, dev, dot_tolerance, host, poison_like)
+from oracle import c_twin as C  # noqa: E402
 from oracle import moe_oracle as O  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
@@ -392,9 +395,8 @@ def test_combine_parity(case):
         dst = np.zeros((0, k), np.int32)
     w = W.random_weights(g, t, k)
     got = gpu_combine(y, dst, w, t, h)
-    want, mag = O.combine(y, dst, w)
-    frac = assert_combine_close(got, want, mag, k, str(case))
-    say("  bit-exact fraction %.6f" % frac)
+    want, _ = O.combine(y, dst, w)
+    assert_combine_exact(got, want, "combine %s" % (case,))
 
 
 def _rounding_weights():
@@ -448,8 +450,8 @@ def test_combine_ignores_rows_past_num_rows():
     dst[::3, 1] = 50 + 1000                     # out of range: skipped like a drop
     w = W.random_weights(g, 40, 2)
     got = gpu_combine(y, dst, w, 40, 256)
-    want, mag = O.combine(y, np.where(dst < 50, dst, -1).astype(np.int32), w)
-    assert_combine_close(got, want, mag, 2)
+    want, _ = O.combine(y, np.where(dst < 50, dst, -1).astype(np.int32), w)
+    assert_combine_exact(got, want)
 
 
 # ------------------------------------------------------------ whole layer
@@ -466,27 +468,34 @@ def run_layer_gpu(w, inp):
     return b
 
 
-def fake_expert(w, L, x, dispatched):
+def fake_expert(w, L, x, dispatched, twin=False):
     """Stand-in expert on the oracle side (harness, not the method)."""
     if w.expert_kind == "identity":
         return dispatched
     if w.expert_kind == "scaled":
         return O.expert_scaled(dispatched, L["expert_offsets"], w.experts)
-    codes, sc = O.quantize_fp8_blocks(x)       # dequantised rows, one per token
+    codes, sc = (C if twin else O).quantize_fp8_blocks(x)   # one row per token
     y_tok = O.expert_dequant(codes, sc)
     y, _ = O.dispatch_bf16(y_tok, L["dst_row"], L["num_rows"])
     return y
 
 
-@pytest.mark.parametrize("name,seed,tokens", [
-    ("tiny", 0, None), ("tiny", 1, None), ("mixtral", 0, None), ("dsv3", 0, None),
-    ("dsv3", 3, 1000), ("qwen3_skew", 0, None), ("decode", 1000, None),
-    ("decode", 1001, None), ("decode", 1002, None)])
+# Full-size layers of every headline shape over seeds 0..4, the reduced
+# dsv3 layer and the tiny and decode layers. Layers of at least 2^22 input
+# elements take the FP8 codes and the combine from the oracle's C twin.
+LAYER_CASES = ([("tiny", 0, None), ("tiny", 1, None)]
+               + [(n, s, None) for n in ("mixtral", "dsv3", "qwen3_skew") for s in range(5)]
+               + [("dsv3", 3, 1000), ("decode", 1000, None), ("decode", 1001, None),
+                  ("decode", 1002, None)])
+
+
+@pytest.mark.parametrize("name,seed,tokens", LAYER_CASES)
 def test_layer_end_to_end(name, seed, tokens):
     w = W.WORKLOADS[name]
     say("layer", name, "seed", seed)
     inp = W.make_inputs(w, seed, tokens=tokens)
     t = inp.x.shape[0]
+    twin = inp.x.size >= 1 << 22
     b = run_layer_gpu(w, inp)
     idx_g, w_g = host(b.topk_idx), host(b.topk_weights)
     idx_o, w_o = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
@@ -504,25 +513,34 @@ def test_layer_end_to_end(name, seed, tokens):
     say("  layout ok; overflow", int(L["overflow"][0]))
     rows = L["num_rows"]
     if b.fp8:
-        q, s, written = O.dispatch_fp8(inp.x, L["dst_row"], rows)
         got_q = host(b.dispatched)[:rows]
         got_s = host(b.scales)[:rows]
-        assert np.array_equal(got_q[written], q[written])
-        assert np.array_equal(got_s[written].view(np.uint32), s[written].view(np.uint32))
-        oracle_out = q
+        if twin:
+            q_tok, s_tok = C.quantize_fp8_blocks(inp.x)
+            d = L["dst_row"].reshape(-1)
+            live = d >= 0
+            tok = np.repeat(np.arange(t), w.top_k)[live]
+            assert np.array_equal(got_q[d[live]], q_tok[tok])
+            assert np.array_equal(got_s[d[live]].view(np.uint32), s_tok[tok].view(np.uint32))
+            oracle_out = None
+        else:
+            q, s, written = O.dispatch_fp8(inp.x, L["dst_row"], rows)
+            assert np.array_equal(got_q[written], q[written])
+            assert np.array_equal(got_s[written].view(np.uint32), s[written].view(np.uint32))
+            oracle_out = q
     else:
         o, written = O.dispatch_bf16(inp.x, L["dst_row"], rows)
         got_o = host(b.dispatched, np.uint16)[:rows]
         assert np.array_equal(got_o[written], o[written])
         oracle_out = o
     say("  dispatch ok")
-    y = fake_expert(w, L, inp.x, oracle_out)
+    y = fake_expert(w, L, inp.x, oracle_out, twin)
     y_dev = dev(np.ascontiguousarray(y))
     b.combine(y_dev)
     got_c = host(b.combined, np.uint16)[:t]
-    want_c, mag = O.combine(y, L["dst_row"], w_g)
-    frac = assert_combine_close(got_c, want_c, mag, w.top_k, name)
-    say("  combine ok; bit-exact fraction %.6f" % frac)
+    want_c = C.combine(y, L["dst_row"], w_g) if twin else O.combine(y, L["dst_row"], w_g)[0]
+    assert_combine_exact(got_c, want_c, "layer %s seed %d T=%d" % (name, seed, t))
+    say("  combine ok: equal to the oracle's bits")
     if w.expert_kind == "identity" and w.capacity == 0:
         # the round trip returns x (as values: a sum that starts at +0 turns
         # an input of -0 into +0)
@@ -619,8 +637,8 @@ def test_mxfp8_layer_end_to_end():
     y, _ = O.dispatch_bf16(O.expert_dequant_mx(codes, sb), L["dst_row"], rows)
     b.combine(dev(y))
     got = host(b.combined, np.uint16)[:t]
-    want, mag = O.combine(y, L["dst_row"], w_g)
-    say("  mxfp8 combine bit-exact fraction %.6f" % assert_combine_close(got, want, mag, w.top_k))
+    want, _ = O.combine(y, L["dst_row"], w_g)
+    assert_combine_exact(got, want, "mxfp8 layer")
 
 
 # --------------------------------------------------------------- backward
@@ -659,8 +677,8 @@ def test_dispatch_backward_parity(case):
                             dev(dst) if t else None, out_full)
     out = host(out_full, np.uint16)
     assert np.all(out[max(t, 1):] == 0xFFFF)
-    want, mag = O.dispatch_backward(grows, dst)
-    say("  bit-exact fraction %.6f" % assert_combine_close(out[:t], want, mag, k))
+    want, _ = O.dispatch_backward(grows, dst)
+    assert_combine_exact(out[:t], want, "dispatch backward")
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "T%d_H%d_k%d_rows%d" % c[:4])
