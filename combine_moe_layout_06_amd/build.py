@@ -89,6 +89,21 @@ def build_abi_check() -> str:
     return ABI_CHECK_BIN
 
 
+SWEEP_SRC = os.path.join(ROOT, "tests", "hip", "convert_sweep.hip")
+SWEEP_LIB = os.path.join(ROOT, "tests", "hip", "libconvert_sweep.so")
+
+
+def build_convert_sweep() -> str:
+    """Compile the test library that compares the hardware converts used by
+    the kernels (their device functions, included from csrc/) with integer
+    rounding references on every fp32 pattern."""
+    tmp = SWEEP_LIB + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, "-I" + CSRC, "-shared", SWEEP_SRC, "-o", tmp])
+    os.replace(tmp, SWEEP_LIB)
+    return SWEEP_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_abi_check())
+    print(build_convert_sweep())

@@ -157,14 +157,21 @@ __device__ __forceinline__ uint32_t quant_pair_sw(uint32_t w, float inv) {
   return quant_one(w & 0xFFFFu, inv) | (quant_one(w >> 16, inv) << 8);
 }
 
-// Two bf16 -> two e4m3 codes with the hardware pack-convert (round to
-// nearest even). Products are clamped to +-448 first; for every fp32 value
-// of magnitude <= 464 this gives the same code as e4m3_from_f32 (checked
-// exhaustively on the device). Needs a finite multiplier: then +-0 stays +-0.
-__device__ __forceinline__ uint32_t quant_pair_hw(uint32_t w, float inv) {
-  const float a = __builtin_amdgcn_fmed3f(__uint_as_float(w << 16) * inv, -448.0f, 448.0f);
-  const float b = __builtin_amdgcn_fmed3f(__uint_as_float(w & 0xFFFF0000u) * inv, -448.0f, 448.0f);
+// Two fp32 values -> two e4m3 codes (low 16 bits, `a` in the low byte) with
+// the hardware pack-convert, which rounds to nearest even; the values are
+// clamped to +-448 first, so larger magnitudes and infinities saturate. For
+// every non-NaN fp32 value this equals e4m3_from_f32 (tests/hip/
+// convert_sweep.hip compares all 2^32 patterns on the device).
+__device__ __forceinline__ uint32_t e4m3_pair_hw(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Two bf16 -> two e4m3 codes of x * inv. Needs a finite multiplier: then
+// +-0 stays +-0.
+__device__ __forceinline__ uint32_t quant_pair_hw(uint32_t w, float inv) {
+  return e4m3_pair_hw(__uint_as_float(w << 16) * inv, __uint_as_float(w & 0xFFFF0000u) * inv);
 }
 
 // 8 bf16 (16 bytes) -> 8 codes (8 bytes)

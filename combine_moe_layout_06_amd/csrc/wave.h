@@ -30,9 +30,9 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 
 // Two fp32 values rounded to bf16 (nearest, ties to even) and packed, `lo`
 // in the low half, with gfx950's packed convert (v_cvt_pk_bf16_f32). On the
-// device it gives the integer rounding (b + 0x7FFF + lsb) >> 16 for every
-// non-NaN fp32 pattern, infinities, overflow and subnormals included (all
-// 2^32 patterns compared); a NaN stays a quiet NaN with its payload.
+// device it gives the integer rounding to nearest even of the fp32 pattern
+// for every non-NaN value, infinities, overflow and subnormals included, and
+// a NaN for a NaN (tests/hip/convert_sweep.hip compares all 2^32 patterns).
 typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
