@@ -28,7 +28,10 @@ Prints one JSON line. Besides the contract fields it carries:
                 between launches, so it matches the profiler's kernel time);
                 `traffic` comes from the committed rocprofv3 counter summary
                 when it was taken on the current kernel source, else null
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  cpu_baseline  the CPU oracle (numpy) timed on this host: all host cores
+                (worker processes over token ranges; the headline value) and
+                one thread on the first 256 tokens, each split into route,
+                layout + dispatch and combine, median of 5 passes
   phases_us     average per-phase times from HIP events, taken in a second
                 pass over the same steps (the timed loop itself has no events)
   cold_us_per_step  the same step with a 1 GiB write between steps, which
@@ -478,47 +481,134 @@ def copy_ceiling_gbps():
     return 2.0 * n * reps / (s.elapsed_time(e) * 1e-3) / 1e9
 
 
-def cpu_baseline(w, seed, budget_s, dtype=None):
-    """The CPU oracle (numpy, one thread) on a bounded sample of the same
-    workload: the first `ts` tokens, the whole path per repeat."""
-    import numpy as np
+CPU_REPS = 5              # repeats of each CPU-baseline leg (median reported)
+CPU_SINGLE_TOKENS = 256   # tokens of the single-thread leg's sample
+CPU_MAX_WORKERS = 16      # the GPU machine's CPU share per GPU
+
+
+def cpu_baseline_phases(w, seed, lo, hi, dtype, reps, barrier=None):
+    """The oracle's route, layout + dispatch and combine over tokens [lo, hi)
+    of the workload, `reps` times; returns per repeat the seconds of each
+    phase. The stand-in expert output is made once, untimed. With a barrier,
+    every phase starts when all workers reach it."""
     from oracle import moe_oracle as O
     from synth import workloads as W
 
-    ts = min(w.tokens, 512)
-    inp = W.make_inputs(w, seed, tokens=ts)
-    idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+    inp = W.make_inputs(w, seed)
+    logits, x = inp.logits[lo:hi], inp.x[lo:hi]
+    idx, wt = O.route(logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
     L = O.layout(idx, w.experts, w.ranks, w.capacity)
-    dtype = w.dispatch_dtype if dtype is None else dtype
     if dtype == 1:
-        codes, sc = O.quantize_fp8_blocks(inp.x)
-        y_tok = O.expert_dequant(codes, sc)
+        y_tok = O.expert_dequant(*O.quantize_fp8_blocks(x))
     elif dtype == 2:
-        codes, sc = O.quantize_mxfp8_blocks(inp.x)
-        y_tok = O.expert_dequant_mx(codes, sc)
+        y_tok = O.expert_dequant_mx(*O.quantize_mxfp8_blocks(x))
     else:
-        y_tok = inp.x
+        y_tok = x
     y, _ = O.dispatch_bf16(y_tok, L["dst_row"], L["num_rows"])
+    disp = {0: O.dispatch_bf16, 1: O.dispatch_fp8, 2: O.dispatch_mxfp8}[dtype]
 
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        idx, wt = O.route(inp.logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+    def sync():
+        if barrier is not None:
+            barrier.wait()
+
+    out = []
+    for _ in range(reps):
+        sync()
+        t0 = time.perf_counter()
+        idx, wt = O.route(logits, w.top_k, w.score_fn, w.groups, w.topk_groups, inp.bias)
+        t1 = time.perf_counter()
+        sync()
+        t1b = time.perf_counter()
         L = O.layout(idx, w.experts, w.ranks, w.capacity)
-        if dtype == 1:
-            O.dispatch_fp8(inp.x, L["dst_row"], L["num_rows"])
-        elif dtype == 2:
-            O.dispatch_mxfp8(inp.x, L["dst_row"], L["num_rows"])
-        else:
-            O.dispatch_bf16(inp.x, L["dst_row"], L["num_rows"])
+        disp(x, L["dst_row"], L["num_rows"])
+        t2 = time.perf_counter()
+        sync()
+        t2b = time.perf_counter()
         O.combine(y, L["dst_row"], wt)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s and reps >= 1:
-            break
-    return {"value": ts * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%s shape, first %d of %d tokens, %d repeats of route+layout+"
-                      "dispatch+combine in %.1f s (numpy, single thread)"
-                      % (w.name, ts, w.tokens, reps, el)}
+        t3 = time.perf_counter()
+        out.append((t1 - t0, t2 - t1b, t3 - t2b))
+    return out
+
+
+def cpu_baseline_worker(name, seed, lo, hi, dtype, reps, barrier, queue):
+    """Process body of the all-cores leg: one token range, phases aligned
+    with the other workers by the barrier."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from synth import workloads as W
+    try:
+        queue.put((lo, cpu_baseline_phases(W.WORKLOADS[name], seed, lo, hi, dtype, reps,
+                                           barrier)))
+    except BaseException as e:  # the parent must not wait forever
+        barrier.abort()
+        queue.put((lo, repr(e)))
+
+
+def cpu_baseline(w, seed, dtype=None):
+    """The CPU oracle (numpy) on this host, two legs, each split into phases
+    (route, layout + dispatch, combine) and timed CPU_REPS times (median):
+      single thread: the first CPU_SINGLE_TOKENS tokens of the workload;
+      all cores:     the whole workload cut into equal token ranges, one
+                     worker process per range, as many as this process may
+                     run on (at most CPU_MAX_WORKERS); each phase starts on
+                     all workers together and lasts until the slowest ends.
+    Must run before anything initialises the GPU in this process: the workers
+    are started as new processes. The headline value is the all-cores leg."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    dtype = w.dispatch_dtype if dtype is None else dtype
+    names = ("route", "layout_dispatch", "combine")
+
+    def summary(per_rep, tokens):
+        ph = np.median(np.asarray(per_rep), axis=0)
+        step = float(np.median(np.asarray(per_rep).sum(axis=1)))
+        return {"value": round(tokens / step, 1), "tokens": tokens,
+                "seconds_per_pass": round(step, 4),
+                "phases_s": {n: round(float(v), 4) for n, v in zip(names, ph)}}
+
+    ts = min(w.tokens, CPU_SINGLE_TOKENS)
+    single = summary(cpu_baseline_phases(w, seed, 0, ts, dtype, CPU_REPS), ts)
+
+    host_cores = len(os.sched_getaffinity(0))
+    n = max(1, min(host_cores, CPU_MAX_WORKERS, w.tokens))
+    cuts = [w.tokens * i // n for i in range(n + 1)]
+    ctx = mp.get_context("spawn")
+    barrier, queue = ctx.Barrier(n, timeout=600), ctx.Queue()
+    procs = [ctx.Process(target=cpu_baseline_worker,
+                         args=(w.name, seed, cuts[i], cuts[i + 1], dtype, CPU_REPS, barrier,
+                               queue)) for i in range(n)]
+    for p in procs:
+        p.start()
+    got = {}
+    while len(got) < n:
+        try:
+            lo, res = queue.get(timeout=5)
+            got[lo] = res
+        except Exception:   # queue.Empty: stop waiting once a worker is gone
+            if any(p.exitcode not in (None, 0) for p in procs):
+                barrier.abort()
+                for p in procs:
+                    p.join(timeout=30)
+                raise RuntimeError("cpu_baseline: a worker process exited with code %s"
+                                   % [p.exitcode for p in procs])
+    for p in procs:
+        p.join()
+    errors = [v for v in got.values() if isinstance(v, str)]
+    if errors:
+        raise RuntimeError("cpu_baseline worker failed: %s" % errors[0])
+    # per repeat and phase: the slowest worker
+    per_rep = np.max(np.stack([np.asarray(got[lo]) for lo in cuts[:-1]]), axis=0)
+    allc = summary(per_rep, w.tokens)
+    allc["workers"] = n
+    return {"value": allc["value"], "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": "%s shape, seed %d: all %d tokens cut into %d token ranges, one numpy "
+                      "oracle process per range (host offers %d cores); route, layout+dispatch "
+                      "and combine each timed from a common start to the slowest worker; "
+                      "median of %d passes" % (w.name, seed, w.tokens, n, host_cores, CPU_REPS),
+            "host_cores": host_cores,
+            "all_cores": allc,
+            "single_thread": dict(single, sample="first %d tokens, one thread" % ts)}
 
 
 def serial_steps(w, bufs, inputs, y, first, steps):
@@ -632,6 +722,13 @@ def main():
         return
 
     w = W.WORKLOADS[args.workload]
+    # the CPU oracle first: its worker processes start while this process
+    # has not touched the GPU yet
+    dtype = {"auto": w.dispatch_dtype, "bf16": M.MOE_DTYPE_BF16, "fp8": M.MOE_DTYPE_FP8_E4M3,
+             "mxfp8": M.MOE_DTYPE_MXFP8_E4M3}[args.dispatch]
+    cpu_base = None
+    if args.pass_ == "forward" and not args.no_cpu_baseline:
+        cpu_base = cpu_baseline(w, args.seed, dtype)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.pass_ == "backward":
@@ -640,8 +737,6 @@ def main():
     if args.pass_ == "hierarchical":
         run_hierarchical(args, w, M, W, torch, np)
         return
-    dtype = {"auto": w.dispatch_dtype, "bf16": M.MOE_DTYPE_BF16, "fp8": M.MOE_DTYPE_FP8_E4M3,
-             "mxfp8": M.MOE_DTYPE_MXFP8_E4M3}[args.dispatch]
     steps, warm = args.steps, args.warmup
 
     # ---- inputs, resident in HBM before timing
@@ -806,10 +901,8 @@ def main():
         "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
         "copy_ceiling_gbps": round(copy_ceiling_gbps(), 1),
         "roofline": roof,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu_base,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds, dtype)
     print(json.dumps(out), flush=True)
 
 

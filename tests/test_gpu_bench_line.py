@@ -44,3 +44,7 @@ def test_bench_line(args, pipelined):
     assert 0 < roof["frac"] <= 1.0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
+    assert 1 <= cpu["cores"] <= cpu["host_cores"] and cpu["all_cores"]["workers"] == cpu["cores"]
+    for leg in ("all_cores", "single_thread"):
+        assert set(cpu[leg]["phases_s"]) == {"route", "layout_dispatch", "combine"}
+        assert cpu[leg]["value"] > 0
