@@ -41,7 +41,7 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
             "moe_dispatch_backward", "moe_combine_backward",
             "moe_rank_layout_workspace_bytes", "moe_rank_layout", "moe_expand",
             "moe_combine_local", "moe_combine_partials", "moe_layout_dispatch",
-            "moe_layout_dispatch_is_fused")
+            "moe_layout_dispatch_is_fused", "moe_layout_no_alloc")
 
 _lib = None
 
@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.moe_layout_dispatch.restype = i32
     L.moe_layout_dispatch_is_fused.argtypes = [i32, i32, i32]
     L.moe_layout_dispatch_is_fused.restype = i32
+    L.moe_layout_no_alloc.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp]
+    L.moe_layout_no_alloc.restype = i32
     _lib = L
     return L
 
@@ -180,6 +183,16 @@ def moe_layout(num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
                             _ptr(rank_counts), _ptr(rank_offsets), _ptr(rank_token_counts),
                             _ptr(dst_row), _ptr(src_pair), _ptr(overflow), _ptr(workspace),
                             workspace_bytes, _stream(stream)))
+
+
+def moe_layout_no_alloc(num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
+                        expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        rank_token_counts, dst_row, src_pair, overflow, stream=None) -> None:
+    _check(lib().moe_layout_no_alloc(num_tokens, num_experts, top_k, num_ranks, capacity,
+                                     _ptr(topk_idx), _ptr(expert_counts), _ptr(expert_offsets),
+                                     _ptr(rank_counts), _ptr(rank_offsets),
+                                     _ptr(rank_token_counts), _ptr(dst_row), _ptr(src_pair),
+                                     _ptr(overflow), _stream(stream)))
 
 
 def moe_layout_dispatch_is_fused(num_tokens, top_k, capacity) -> bool:

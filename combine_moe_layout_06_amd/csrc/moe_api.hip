@@ -9,7 +9,15 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kernels.h"
+
+// Device scratch of moe_layout_no_alloc: the per-tile counts of the layout
+// kernels. Each GPU holds its own copy. Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_LAYOUT_SCRATCH_BYTES];
 
 namespace {
 
@@ -194,6 +202,73 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int ca
                                      topk_idx, expert_counts, expert_offsets, rank_counts,
                                      rank_offsets, rank_token_counts, dst_row, src_pair,
                                      overflow, workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];   // device address of each GPU's scratch
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call with that device current and kept until the process ends.
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, fn);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d with a scratch address", fn,
+                dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(err));
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layout_no_alloc(int num_tokens, int num_experts, int top_k, int num_ranks,
+                        int capacity, const int32_t* topk_idx, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                        int32_t* rank_token_counts, int32_t* dst_row, int32_t* src_pair,
+                        int32_t* overflow, void* stream) {
+  const char* fn = "moe_layout_no_alloc";
+  int st = check_topk(fn, num_tokens, num_experts, top_k);
+  if (st != MOE_OK) return st;
+  const size_t need = moe::layout_workspace_bytes(num_tokens, num_experts, top_k);
+  if (need > MOE_LAYOUT_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "%s: these sizes need %zu bytes of scratch, more than the library's %u "
+                "(call moe_layout with a workspace instead)", fn, need,
+                (unsigned)MOE_LAYOUT_SCRATCH_BYTES);
+  // the remaining checks of moe_layout, with a stand-in for the workspace
+  // (an aligned non-null value of the scratch's size; nothing dereferences it)
+  st = check_layout(fn, num_tokens, num_experts, top_k, num_ranks, capacity, topk_idx,
+                    expert_counts, expert_offsets, rank_counts, rank_offsets, rank_token_counts,
+                    dst_row, src_pair, overflow, reinterpret_cast<void*>(uintptr_t{256}),
+                    MOE_LAYOUT_SCRATCH_BYTES);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(fn, &ws);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_layout(num_tokens, num_experts, top_k, num_ranks, capacity,
+                                     topk_idx, expert_counts, expert_offsets, rank_counts,
+                                     rank_offsets, rank_token_counts, dst_row, src_pair,
+                                     overflow, ws, static_cast<hipStream_t>(stream)),
                   fn);
 }
 

@@ -158,6 +158,36 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_layout_no_alloc -- moe_layout without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments
+ * (minus workspace and workspace_bytes), same results, same kernels.
+ *
+ * The per-tile counts live instead in a static device array of
+ * MOE_LAYOUT_SCRATCH_BYTES bytes that belongs to the library: each GPU the
+ * library runs on holds its own copy from its first call on that GPU until
+ * the process ends (the one exception to "keeps no state" above). The call
+ * allocates and frees nothing; the first call on a device looks up that
+ * device's copy once (hipGetSymbolAddress) with the device current.
+ *   - Sizes whose moe_layout_workspace_bytes() exceeds
+ *     MOE_LAYOUT_SCRATCH_BYTES return MOE_ERR_WORKSPACE and enqueue nothing
+ *     (2 MiB covers up to 130,944 tokens at E = 256, k = 8).
+ *   - The array needs no initialisation: every call writes the parts it
+ *     reads. It keeps the last call's contents.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (other streams, other threads) race and must be ordered by
+ *     the caller. The stream must belong to the calling thread's current
+ *     device.
+ */
+#define MOE_LAYOUT_SCRATCH_BYTES (2u << 20)
+int moe_layout_no_alloc(int num_tokens, int num_experts, int top_k, int num_ranks,
+                        int capacity, const int32_t* topk_idx,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* rank_counts, int32_t* rank_offsets,
+                        int32_t* rank_token_counts, int32_t* dst_row,
+                        int32_t* src_pair, int32_t* overflow, void* stream);
+
+/*
  * moe_dispatch -- copy each token's hidden state to the rows of its
  * experts (glossary "Expert Parallelism", Phase 1; DeepEP article,
  * "Kernels low-latency dispatch et combine").

@@ -114,6 +114,43 @@ def test_layout_rejects(kw, status):
     assert M.moe_last_error().startswith("moe_layout")
 
 
+def _layout_no_alloc(**kw):
+    _no_gpu()
+    a = dict(T=4, E=8, k=2, R=4, cap=0, idx=A16, src=A16, ec=A16, eo=A16, rc=A16, ro=A16,
+             rtc=None, dst=A16, ov=A16)
+    a.update(kw)
+    return M.lib().moe_layout_no_alloc(a["T"], a["E"], a["k"], a["R"], a["cap"], a["idx"],
+                                       a["ec"], a["eo"], a["rc"], a["ro"], a["rtc"], a["dst"],
+                                       a["src"], a["ov"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=3), M.MOE_ERR_INVALID),
+    (dict(cap=-1), M.MOE_ERR_INVALID),
+    (dict(ec=None), M.MOE_ERR_INVALID),
+    (dict(dst=A16 + 2), M.MOE_ERR_INVALID),
+    (dict(k=0), M.MOE_ERR_INVALID),
+    # more scratch than the library holds: refused before any device call
+    (dict(T=1 << 18, E=256, k=8, R=32), M.MOE_ERR_WORKSPACE),
+    (dict(T=1 << 17, E=512, k=8, R=32), M.MOE_ERR_WORKSPACE),
+])
+def test_layout_no_alloc_rejects(kw, status):
+    assert _layout_no_alloc(**kw) == status
+    assert M.moe_last_error().startswith("moe_layout_no_alloc")
+
+
+def test_layout_no_alloc_limit_matches_the_header():
+    """The largest sizes that fit the static scratch, against the header's
+    MOE_LAYOUT_SCRATCH_BYTES."""
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    m = re.search(r"#define MOE_LAYOUT_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == 2 << 20
+    assert M.moe_layout_workspace_bytes(130944, 256, 8) <= limit      # the header's figure
+    assert M.moe_layout_workspace_bytes(130945, 256, 8) > limit
+
+
 def _dispatch(**kw):
     _no_gpu()
     a = dict(T=4, H=256, k=2, rows=8, x=A16, dst=A16, dt=0, out=A16b, sc=None)
