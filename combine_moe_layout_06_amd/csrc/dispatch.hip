@@ -13,11 +13,13 @@ namespace moe {
 namespace {
 
 // Workgroups per CU (occupancy caps, see lds_cap_bytes), measured on the
-// dsv3, mixtral and qwen3_skew shapes: FP8 runs 4-6% faster at 3 than at the
-// 8 its registers allow; bf16 with k <= 2 about 3% faster at 4, while bf16
-// with k = 8 and MXFP8 run best uncapped.
-constexpr int kFp8BlocksPerCu = 3;
+// dsv3, mixtral and qwen3_skew shapes: bf16 with k <= 2 runs about 3% faster
+// at 4, while bf16 with k = 8 and MXFP8 run best uncapped. The row-held FP8
+// kernel: 4 or 5 (53.4, 53.2 us on dsv3), 3: 57.0, 2: 61.0, uncapped: 53.7.
+constexpr int kFp8RowsBlocksPerCu = 4;
 constexpr int kBf16FewBlocksPerCu = 4;
+// Steps (8 blocks of 128 columns) per row-held FP8 wave at most.
+constexpr int kFp8RowMaxSteps = 8;
 
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(
     int T, int k, int nch, int parts, int cpp, int num_rows,
@@ -26,12 +28,24 @@ __global__ __launch_bounds__(256) void dispatch_bf16_kernel(
   dispatch_bf16_body(blockIdx.x, T, k, nch, parts, cpp, num_rows, x, DstRows{dst_row}, out);
 }
 
-__global__ __launch_bounds__(256) void dispatch_fp8_kernel(
+template <int MAXST>
+__global__ __launch_bounds__(256) void dispatch_fp8_rows_kernel(
     int T, int k, int H, int parts, int bpp, int num_rows,
     const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
     uint8_t* __restrict__ out, float* __restrict__ out_scales) {
-  dispatch_fp8_body(blockIdx.x, T, k, H, parts, bpp, num_rows, x, DstRows{dst_row}, out,
-                    out_scales);
+  dispatch_fp8_rows_body<MAXST>(blockIdx.x, T, k, H, parts, bpp, num_rows, x, dst_row, out,
+                                out_scales);
+}
+
+template <int MAXST>
+void launch_fp8_rows(int T, int H, int k, int parts, int bpp, int num_rows, const void* x,
+                     const int32_t* dst_row, void* out, float* out_scales, hipStream_t stream) {
+  const int waves = T * parts;
+  hipLaunchKernelGGL((dispatch_fp8_rows_kernel<MAXST>),
+                     dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(256),
+                     lds_cap_bytes(kFp8RowsBlocksPerCu), stream, T, k, H, parts, bpp, num_rows,
+                     static_cast<const u32x4*>(x), dst_row, static_cast<uint8_t*>(out),
+                     out_scales);
 }
 
 __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(
@@ -76,14 +90,20 @@ hipError_t launch_dispatch_fp8(int T, int H, int k, int num_rows, const void* x,
                                const int32_t* dst_row, void* out, float* out_scales,
                                hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  // parts of at most kFp8RowMaxSteps steps, as even as whole steps allow
   const int nb = H / MOE_FP8_BLOCK;
-  int parts, bpp;
-  split_row(T, nb, kFp8StepBlocks, 64 * kScaleSlots, &parts, &bpp);
-  const int waves = T * parts;
-  hipLaunchKernelGGL(dispatch_fp8_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
-                     dim3(256), lds_cap_bytes(kFp8BlocksPerCu), stream, T, k, H, parts, bpp, num_rows,
-                     static_cast<const u32x4*>(x), dst_row, static_cast<uint8_t*>(out),
-                     out_scales);
+  const int steps = (nb + kFp8StepBlocks - 1) / kFp8StepBlocks;
+  const int parts = (steps + kFp8RowMaxSteps - 1) / kFp8RowMaxSteps;
+  const int per = (steps + parts - 1) / parts;                 // steps per part, <= 8
+  const int bpp = per * kFp8StepBlocks;
+#define MOE_FP8_ROWS(n) \
+  case n: launch_fp8_rows<n>(T, H, k, parts, bpp, num_rows, x, dst_row, out, out_scales, stream); break;
+  switch (per) {
+    MOE_FP8_ROWS(1) MOE_FP8_ROWS(2) MOE_FP8_ROWS(3) MOE_FP8_ROWS(4) MOE_FP8_ROWS(5)
+    MOE_FP8_ROWS(6) MOE_FP8_ROWS(7) MOE_FP8_ROWS(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_FP8_ROWS
   return hipGetLastError();
 }
 

@@ -290,6 +290,94 @@ __device__ __forceinline__ void dispatch_fp8_body(
 }
 
 
+// FP8 with row-held waves: one wave per (token, part of at most MAXST steps),
+// the same step layout and arithmetic as dispatch_fp8_body. The wave issues
+// the loads of all its steps first, keeps the codes of the whole part in
+// registers (4 per step and lane) and then writes each destination row as
+// one contiguous run: MAXST pieces of 1 KiB back to back, then the row's
+// scales. With a part covering the whole row (7 steps at hidden 7168) every
+// destination row is one 7 KiB run from one wave, which the memory writes
+// faster than the same bytes as pieces from seven waves at different times
+// (dsv3: 53.4 against 58.1 us).
+template <int MAXST>
+__device__ __forceinline__ void dispatch_fp8_rows_body(
+    int block, int T, int k, int H, int parts, int bpp, int num_rows,
+    const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
+    uint8_t* __restrict__ out, float* __restrict__ out_scales) {
+  const int lane = threadIdx.x & 63;
+  const int gw = block * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= T * parts) return;
+  const int t = gw / parts;
+  const int nb = H / MOE_FP8_BLOCK;
+  const int nch = H / 8;
+  const int b0 = (gw - t * parts) * bpp;
+  const int nbp = min(bpp, nb - b0);
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const int group = lane >> 4;       // block of A (and of B) inside a step
+  const int sub = lane & 15;         // 16-byte chunk inside the block
+  const bool odd = lane & 1;
+  const u32x4* src = x + (size_t)t * nch;
+
+  u32x4 va[MAXST], vb[MAXST];
+#pragma unroll
+  for (int st = 0; st < MAXST; ++st) {
+    const int ba = st * kFp8StepBlocks + group, bb = ba + kFp8StepBlocks / 2;
+    va[st] = u32x4{0u, 0u, 0u, 0u};
+    vb[st] = u32x4{0u, 0u, 0u, 0u};
+    if (ba < nbp) va[st] = stream_load(src + (b0 + ba) * 16 + sub);
+    if (bb < nbp) vb[st] = stream_load(src + (b0 + bb) * 16 + sub);
+  }
+
+  float sreg[kScaleSlots];
+#pragma unroll
+  for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0.0f;
+  u32x4 q[MAXST];
+#pragma unroll
+  for (int st = 0; st < MAXST; ++st) {
+    const int ba = st * kFp8StepBlocks + group, bb = ba + kFp8StepBlocks / 2;
+    const bool act_a = ba < nbp, act_b = bb < nbp;
+    const float amax_a = block_amax(va[st]), amax_b = block_amax(vb[st]);
+    const float scale_a = amax_a / 448.0f, scale_b = amax_b / 448.0f;
+    const u32x2 qa = quant8(va[st], act_a ? 448.0f / amax_a : 1.0f);
+    const u32x2 qb = quant8(vb[st], act_b ? 448.0f / amax_b : 1.0f);
+    // swap halves inside lane pairs: even lanes keep A, odd lanes keep B
+    const u32x2 send = odd ? qa : qb;
+    u32x2 recv;
+    recv[0] = dpp_u32<0xB1>(send[0]);
+    recv[1] = dpp_u32<0xB1>(send[1]);
+    q[st] = odd ? u32x4{recv[0], recv[1], qb[0], qb[1]} : u32x4{qa[0], qa[1], recv[0], recv[1]};
+    // lane (b & 63), slot (b >> 6) keeps the scale of part-local block b
+#pragma unroll
+    for (int g = 0; g < kFp8StepBlocks; ++g) {
+      const int b = st * kFp8StepBlocks + g;
+      const float sg = read_lane(g < 4 ? scale_a : scale_b, (g & 3) * 16);
+      if (b < nbp && lane == (b & 63)) {
+#pragma unroll
+        for (int s = 0; s < kScaleSlots; ++s)
+          if ((b >> 6) == s) sreg[s] = sg;
+      }
+    }
+  }
+
+  for (int j = 0; j < k; ++j) {
+    const int d = read_lane(my_dst, j);
+    if (d < 0 || d >= num_rows) continue;
+#pragma unroll
+    for (int st = 0; st < MAXST; ++st) {
+      const int ba = st * kFp8StepBlocks + group;
+      const int bq = odd ? ba + kFp8StepBlocks / 2 : ba;   // block this lane writes
+      const int col = (b0 + bq) * MOE_FP8_BLOCK + (sub & ~1) * 8;
+      if (bq < nbp) stream_store(q[st], reinterpret_cast<u32x4*>(out + (size_t)d * H + col));
+    }
+    float* srow = out_scales + (size_t)d * nb + b0;
+#pragma unroll
+    for (int s = 0; s < kScaleSlots; ++s) {
+      const int b = s * 64 + lane;
+      if (b < nbp) srow[b] = sreg[s];
+    }
+  }
+}
+
 // MXFP8: one wave per (token, part); a step covers 512 columns = 16 blocks
 // of 32 columns, 4 lanes per block. The shared exponent comes from the
 // block amax (two DPP steps inside each quad); codes use the hardware

@@ -282,6 +282,9 @@ DISPATCH_CASES = [
     (100, 384, 2, 8, 0, True),          # 3 blocks: partial 512-column step
     (33, 896, 5, 12, 3, True),          # capacity with drops, FP8
     (40, 33280, 2, 4, 0, True),         # 260 blocks: more than one part per row
+    (500, 1152, 4, 16, 0, True),        # 9 blocks: two steps, the second of one block
+    (77, 8320, 3, 8, 0, True),          # 65 blocks, 9 steps: two parts of 5 steps
+    (200, 16384, 8, 64, 0, True),       # 16 steps: two parts of 8
     (9000, 1024, 1, 4, 0, False),
     (0, 256, 2, 8, 0, False),
     (0, 256, 2, 8, 0, True),
