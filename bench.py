@@ -16,9 +16,9 @@ in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
-streams in groups of 4 steps: the route and layout of one group run beside the
-dispatch and combine of the group before, on 8 sets of layer buffers used in
-turn (--serial: one step after the other; the default with --eager). The serial rate of the
+streams in groups of 4 steps (the first group holds one step): the route and
+layout of one group run beside the dispatch and combine of the group before,
+on 8 sets of layer buffers used in turn (--serial: one step after the other; the default with --eager). The serial rate of the
 same steps is measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
@@ -37,6 +37,10 @@ Prints one JSON line. Besides the contract fields it carries:
   cold_us_per_step  the same step with a 1 GiB write between steps, which
                 evicts L2 and the 256 MB Infinity Cache
   serial_ms_per_step  the timed steps run one after the other on one stream
+  ceilings_gbps best GB/s of plain kernels (libmoe_ceilings.so) with the
+                path's access patterns: sequential copy, read and write, and
+                random whole-row gather (combine-like) and scatter
+                (dispatch-like); copy_ceiling_gbps is the sequential copy
 """
 
 from __future__ import annotations
@@ -358,10 +362,10 @@ def run_hierarchical(args, w, M, W, torch, np):
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams in groups of %d: the route, expert layout "
-                   "and (token, rank) layout of one group run beside the send, fan-out and "
-                   "combines of the group before (%d buffer sets in turn)"
-                   % (PIPE_GROUP, 2 * PIPE_GROUP) if overlap
+                  ("; steps pipelined on two streams in groups of %d (the first of %d): the "
+                   "route, expert layout and (token, rank) layout of one group run beside "
+                   "the send, fan-out and combines of the group before (%d buffer sets in "
+                   "turn)" % (PIPE_GROUP, PIPE_LEAD, 2 * PIPE_GROUP) if overlap
                    else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 5),
         "config": {"workload": "%s hierarchical: T=%d H=%d E=%d k=%d R=%d, one row per "
@@ -461,24 +465,102 @@ def calibrate_copy():
                       "bytes_written_per_launch": n, "launches": 5}), flush=True)
 
 
-def copy_ceiling_gbps():
-    """Read+write GB/s of a plain 512 MiB device-to-device copy."""
-    import torch
-    n = 1 << 29
+CEIL_LIB = os.path.join(ROOT, "combine_moe_layout_06_amd", "libmoe_ceilings.so")
+CEIL_BYTES = 1 << 30     # sequential probes: 1 GiB read and/or written
+CEIL_REPS = 10
+
+
+def ceilings(torch, np):
+    """Best GB/s of plain kernels with the path's access patterns on this GPU
+    (libmoe_ceilings.so), each over a small sweep of launch shapes; HIP events
+    on the launch stream around CEIL_REPS back-to-back launches:
+      copy     sequential 16-byte reads + writes (bytes read + written)
+      read     sequential reads only
+      write    sequential writes only
+      gather   random whole-row reads of 14,336-byte rows (bf16 rows of the
+               DeepSeek-V3 shape), sequential writes (read + written)
+      scatter  sequential reads, random whole-row writes of 7,168-byte rows
+               (its FP8 rows) (read + written)
+      fanout   each 7,168-byte row read once and written to 8 random rows
+               (the dispatch's pattern at k = 8) (read + written)"""
+    import ctypes
+
+    if not os.path.exists(CEIL_LIB):
+        raise RuntimeError("%s is missing; run `python -m combine_moe_layout_06_amd.build`"
+                           % CEIL_LIB)
+    L = ctypes.CDLL(CEIL_LIB)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.ceil_copy.argtypes = [vp, vp, sz, i32, i32, i32, vp]
+    L.ceil_read.argtypes = [vp, sz, vp, i32, i32, i32, vp]
+    L.ceil_write.argtypes = [vp, sz, i32, i32, i32, vp]
+    L.ceil_rows.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp]
+    L.ceil_fanout.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    for f in (L.ceil_copy, L.ceil_read, L.ceil_write, L.ceil_rows, L.ceil_fanout):
+        f.restype = i32
+
+    n = CEIL_BYTES
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
-    for _ in range(3):
-        b.copy_(a)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    reps = 20
-    for _ in range(reps):
-        b.copy_(a)
-    e.record()
-    torch.cuda.synchronize()
-    return 2.0 * n * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    b.fill_(2)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def best(moved, configs, launch):
+        top = None
+        for cfg in configs:
+            def go():
+                rc = launch(*cfg)
+                if rc != 0:
+                    raise RuntimeError("ceiling kernel %s failed: %d" % (cfg, rc))
+            go()
+            go()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(CEIL_REPS):
+                go()
+            e.record()
+            torch.cuda.synchronize()
+            gbps = moved * CEIL_REPS / (s.elapsed_time(e) * 1e-3) / 1e9
+            if top is None or gbps > top[0]:
+                top = (gbps, cfg)
+        return top
+
+    seq = [(pc, u) for pc in (1, 2, 4, 8) for u in (1, 4)]
+    out = {}
+    g, c = best(2 * n, seq, lambda pc, u: L.ceil_copy(a.data_ptr(), b.data_ptr(), n, cus * pc,
+                                                         pc, u, stream))
+    out["copy"] = {"gbps": round(g, 1), "per_cu": c[0], "unroll": c[1]}
+    g, c = best(n, seq, lambda pc, u: L.ceil_read(a.data_ptr(), n, sink.data_ptr(), cus * pc,
+                                                     pc, u, stream))
+    out["read"] = {"gbps": round(g, 1), "per_cu": c[0], "unroll": c[1]}
+    g, c = best(n, seq, lambda pc, u: L.ceil_write(b.data_ptr(), n, cus * pc, pc, u, stream))
+    out["write"] = {"gbps": round(g, 1), "per_cu": c[0], "unroll": c[1]}
+    gen = np.random.Generator(np.random.PCG64(12345))
+    for name, gather, row_bytes, pieces in (("gather", 1, 14336, (128, 448, 896)),
+                                            ("scatter", 0, 7168, (64, 128, 448))):
+        rows = n // row_bytes
+        perm = torch.from_numpy(gen.permutation(rows).astype(np.int32)).cuda()
+        cfgs = [(p, pc) for p in pieces for pc in (0, 1, 2, 3, 4)]
+        g, c = best(2 * rows * row_bytes, cfgs,
+                    lambda p, pc: L.ceil_rows(gather, a.data_ptr(), b.data_ptr(),
+                                              perm.data_ptr(), rows, row_bytes, p, pc, stream))
+        out[name] = {"gbps": round(g, 1), "row_bytes": row_bytes, "piece_bytes": 16 * c[0],
+                     "per_cu": c[1]}
+    row_bytes, k = 7168, 8
+    rows = n // (row_bytes * k)
+    perm = torch.from_numpy(gen.permutation(rows * k).astype(np.int32)).cuda()
+    cfgs = [(p, pc) for p in (64, 128, 256, 448) for pc in (0, 1, 2, 3, 4)]
+    g, c = best(rows * row_bytes * (1 + k), cfgs,
+                lambda p, pc: L.ceil_fanout(a.data_ptr(), b.data_ptr(), perm.data_ptr(), rows, k,
+                                            row_bytes, p, pc, stream))
+    out["fanout"] = {"gbps": round(g, 1), "row_bytes": row_bytes, "k": k,
+                     "piece_bytes": 16 * c[0], "per_cu": c[1]}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 CPU_REPS = 5              # repeats of each CPU-baseline leg (median reported)
@@ -624,18 +706,30 @@ def serial_steps(w, bufs, inputs, y, first, steps):
 
 
 PIPE_GROUP = 4   # steps per cross-stream wait of the pipelined mode
+PIPE_LEAD = 1    # steps of the first group, whose fronts nothing can hide
 
 
-def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP):
-    """Steps pipelined on two streams, in groups of `group` steps: `side`
-    runs front(i, s) for the steps of one group while the current stream runs
-    back(i, s) for the group before; then the current stream waits for the
-    side stream once and runs back() for the group. Step i uses buffer set
-    s = i % nsets (nsets = 2 * group), so consecutive groups use the two
-    halves in turn, and the fronts of a group wait, once, until the backs of
-    the group before last (the same sets) are done. One event per group in
-    each direction: each cross-stream edge costs the stream after it a few
-    microseconds."""
+def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
+    """Groups of the pipelined mode: the first `lead` steps, then groups of
+    `group` steps (the last one shorter). The first group's fronts run with
+    nothing beside them, so a short first group exposes one front, not
+    `group` of them; the next group's fronts then hide behind its backs."""
+    first = min(max(lead, 1), group, steps)
+    out = [range(0, first)] if steps else []
+    out += [range(g0, min(g0 + group, steps)) for g0 in range(first, steps, group)]
+    return out
+
+
+def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIPE_LEAD):
+    """Steps pipelined on two streams, in the groups of pipeline_groups():
+    `side` runs front(i, s) for the steps of one group while the current
+    stream runs back(i, s) for the group before; then the current stream
+    waits for the side stream once and runs back() for the group. Step i uses
+    buffer set s = i % nsets (nsets = 2 * group). Two consecutive groups hold
+    at most nsets steps, so the steps that last used the sets of group q are
+    in group q - 2 or earlier: the fronts of group q wait, once, until the
+    backs of group q - 2 are done. One event per group in each direction:
+    each cross-stream edge costs the stream after it a few microseconds."""
     assert nsets == 2 * group
     main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
     released = []
@@ -643,8 +737,7 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP):
         e = torch.cuda.Event()
         e.record(main)
         released.append(e)
-    for q, g0 in enumerate(range(0, steps, group)):
-        grp = range(g0, min(g0 + group, steps))
+    for q, grp in enumerate(pipeline_groups(steps, group, lead)):
         side.wait_event(released[q % 2])
         with torch.cuda.stream(side):
             for i in grp:
@@ -681,15 +774,21 @@ def overlapped_steps(torch, w, bufs, inputs, y, first, steps, side, group=PIPE_G
     pipelined(torch, front, back, len(bufs), steps, side, group)
 
 
+GRAPH_WARM_REPLAYS = 3   # untimed replays of a captured graph before the timed one
+
+
 def timed_run(torch, run, graph):
-    """Wall time of run(): captured into one HIP graph, replayed once to
-    upload it and once timed; or launched from the host."""
+    """Wall time of run(): captured into one HIP graph, replayed
+    GRAPH_WARM_REPLAYS times untimed (the first uploads it; the first few
+    replays of a new graph run 2-5% slower) and once timed; or launched from
+    the host once untimed and once timed."""
     if graph:
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
             run()
-        g.replay()
+        for _ in range(GRAPH_WARM_REPLAYS):
+            g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         g.replay()
@@ -862,6 +961,7 @@ def main():
             "algorithmic_bytes_per_launch": nbytes["combine"],
             "launch_us": round(comb_us, 2), "timing": roofline_timing()}
 
+    ceil = ceilings(torch, np)
     out = {
         "metric": "dispatch+combine tokens/s and HBM GB/s (% of peak), DeepSeek-V3 shape, 1 GPU",
         "value": round(value, 1),
@@ -876,9 +976,10 @@ def main():
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams in groups of %d: the route and layout "
-                   "of one group run beside the dispatch and combine of the group before "
-                   "(%d layer buffers in turn)" % (PIPE_GROUP, 2 * PIPE_GROUP)
+                  ("; steps pipelined on two streams in groups of %d (the first of %d): the "
+                   "route and layout of one group run beside the dispatch and combine of "
+                   "the group before (%d layer buffers in turn)"
+                   % (PIPE_GROUP, PIPE_LEAD, 2 * PIPE_GROUP)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
@@ -899,7 +1000,8 @@ def main():
         "event_us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
         "event_us_per_step_p99": round(float(np.percentile(step_ms, 99)) * 1e3, 2),
         "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
-        "copy_ceiling_gbps": round(copy_ceiling_gbps(), 1),
+        "copy_ceiling_gbps": ceil["copy"]["gbps"],
+        "ceilings_gbps": ceil,
         "roofline": roof,
         "cpu_baseline": cpu_base,
     }

@@ -89,6 +89,20 @@ def build_abi_check() -> str:
     return ABI_CHECK_BIN
 
 
+CEIL_SRC = os.path.join(CSRC, "ceilings.hip")
+CEIL_LIB = os.path.join(PKG, "libmoe_ceilings.so")
+
+
+def build_ceilings() -> str:
+    """Compile the benchmark's access-pattern ceiling kernels (plain copy,
+    read, write, row gather and row scatter) into their own library; the
+    path never calls them."""
+    tmp = CEIL_LIB + ".tmp"
+    _run([hipcc(), *HIPCC_FLAGS, "-shared", CEIL_SRC, "-o", tmp])
+    os.replace(tmp, CEIL_LIB)
+    return CEIL_LIB
+
+
 SWEEP_SRC = os.path.join(ROOT, "tests", "hip", "convert_sweep.hip")
 SWEEP_LIB = os.path.join(ROOT, "tests", "hip", "libconvert_sweep.so")
 
@@ -107,3 +121,4 @@ if __name__ == "__main__":
     print(build(verbose=True))
     print(build_abi_check())
     print(build_convert_sweep())
+    print(build_ceilings())

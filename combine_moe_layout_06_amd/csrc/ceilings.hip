@@ -1,0 +1,239 @@
+// Access-pattern ceilings of this GPU, measured with plain kernels beside the
+// path's own (library libmoe_ceilings.so; the benchmark times them, nothing
+// in the path calls them).
+//
+// The path moves rows between HBM buffers in three patterns, and each kernel
+// is judged against the best a plain kernel reaches with the same pattern on
+// the same chip:
+//   copy     sequential 16-byte reads and writes of one buffer into another
+//            (the plain device-to-device copy);
+//   read     sequential 16-byte reads only;
+//   write    sequential 16-byte writes only;
+//   gather   dst row i = src row perm[i]: random whole-row reads, sequential
+//            writes (the combine reads its expert rows this way);
+//   scatter  dst row perm[i] = src row i: sequential reads, random whole-row
+//            writes;
+//   fanout   each src row read once and written to k rows dst[perm[i*k + j]]
+//            (the dispatch's pattern: one read, k random row writes).
+// Rows are read and written with nontemporal 16-byte accesses, one wave per
+// row piece of `piece` chunks, as the path's kernels do. The sequential
+// kernels loop over the buffer with a grid of `blocks` workgroups of 256
+// threads; the occupancy cap (workgroups per CU) is set, as in the path, by
+// reserving LDS the kernel never touches. Every launch checks its sizes on
+// the host and every thread's loop is bounded.
+
+#include "kernels.h"
+#include "wave.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src,
+                                                       u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * kThreads * U;
+  for (size_t i = (size_t)blockIdx.x * kThreads * U + threadIdx.x; i < n; i += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (size_t)u * kThreads < n) v[u] = stream_load(src + i + (size_t)u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (size_t)u * kThreads < n) stream_store(v[u], dst + i + (size_t)u * kThreads);
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ src, size_t n,
+                                                       uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kThreads * U;
+  uint32_t acc = 0;
+  for (size_t i = (size_t)blockIdx.x * kThreads * U + threadIdx.x; i < n; i += stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (size_t)u * kThreads < n) {
+        const u32x4 v = stream_load(src + i + (size_t)u * kThreads);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+  }
+  // keeps the loads alive; the sink has one word and the pattern never occurs
+  // in the benchmark's buffers, so nothing is written in practice
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * kThreads * U;
+  const u32x4 v = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  for (size_t i = (size_t)blockIdx.x * kThreads * U + threadIdx.x; i < n; i += stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (size_t)u * kThreads < n) stream_store(v, dst + i + (size_t)u * kThreads);
+  }
+}
+
+// One wave per (row, piece); a piece is `piece` 16-byte chunks, one per lane
+// per step of 64. gather: dst[i] = src[perm[i]]; scatter: dst[perm[i]] = src[i].
+template <bool kGather>
+__global__ __launch_bounds__(kThreads) void rows_kernel(const u32x4* __restrict__ src,
+                                                       u32x4* __restrict__ dst,
+                                                       const int32_t* __restrict__ perm,
+                                                       int rows, int nch, int piece) {
+  const int pieces = (nch + piece - 1) / piece;
+  const long long item = (long long)blockIdx.x * (kThreads / MOE_WAVE) + (threadIdx.x >> 6);
+  if (item >= (long long)rows * pieces) return;
+  const int row = (int)(item / pieces);
+  const int c0 = (int)(item - (long long)row * pieces) * piece;
+  const int lane = threadIdx.x & 63;
+  const int other = perm[row];
+  const u32x4* s = src + (size_t)(kGather ? other : row) * nch;
+  u32x4* d = dst + (size_t)(kGather ? row : other) * nch;
+  const int end = min(nch, c0 + piece);
+  for (int c = c0 + lane; c < end; c += MOE_WAVE) stream_store(stream_load(s + c), d + c);
+}
+
+// One wave per (src row, piece of 64 * P chunks): the piece is read once into
+// registers and written to the k destination rows.
+template <int P>
+__global__ __launch_bounds__(kThreads) void fanout_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst,
+                                                         const int32_t* __restrict__ perm,
+                                                         int rows, int k, int nch) {
+  constexpr int kPiece = 64 * P;
+  const int pieces = (nch + kPiece - 1) / kPiece;
+  const long long item = (long long)blockIdx.x * (kThreads / MOE_WAVE) + (threadIdx.x >> 6);
+  if (item >= (long long)rows * pieces) return;
+  const int row = (int)(item / pieces);
+  const int c0 = (int)(item - (long long)row * pieces) * kPiece;
+  const int lane = threadIdx.x & 63;
+  const u32x4* s = src + (size_t)row * nch;
+  u32x4 v[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int c = c0 + p * MOE_WAVE + lane;
+    if (c < nch) v[p] = stream_load(s + c);
+  }
+  for (int j = 0; j < k; ++j) {
+    u32x4* d = dst + (size_t)perm[(size_t)row * k + j] * nch;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + p * MOE_WAVE + lane;
+      if (c < nch) stream_store(v[p], d + c);
+    }
+  }
+}
+
+int finish() { return (int)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+// Sequential kernels over `bytes` (a multiple of 16) with `blocks`
+// workgroups, at most `per_cu` workgroups per CU (0 = no cap) and `unroll`
+// (1, 2 or 4) chunks per thread in flight. Return a hipError_t (0 = success)
+// or -1 for arguments outside these limits.
+int ceil_copy(const void* src, void* dst, size_t bytes, int blocks, int per_cu, int unroll,
+              void* stream) {
+  if (!src || !dst || bytes % 16 || blocks < 1 || per_cu < 0) return -1;
+  const size_t n = bytes / 16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = moe::lds_cap_bytes(per_cu);
+  const auto* a = static_cast<const u32x4*>(src);
+  auto* b = static_cast<u32x4*>(dst);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(copy_kernel<1>, dim3(blocks), dim3(kThreads), lds, s, a, b, n); break;
+    case 2: hipLaunchKernelGGL(copy_kernel<2>, dim3(blocks), dim3(kThreads), lds, s, a, b, n); break;
+    case 4: hipLaunchKernelGGL(copy_kernel<4>, dim3(blocks), dim3(kThreads), lds, s, a, b, n); break;
+    default: return -1;
+  }
+  return finish();
+}
+
+// sink: one uint32 of device memory.
+int ceil_read(const void* src, size_t bytes, void* sink, int blocks, int per_cu, int unroll,
+              void* stream) {
+  if (!src || !sink || bytes % 16 || blocks < 1 || per_cu < 0) return -1;
+  const size_t n = bytes / 16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = moe::lds_cap_bytes(per_cu);
+  const auto* a = static_cast<const u32x4*>(src);
+  auto* k = static_cast<uint32_t*>(sink);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(read_kernel<1>, dim3(blocks), dim3(kThreads), lds, s, a, n, k); break;
+    case 2: hipLaunchKernelGGL(read_kernel<2>, dim3(blocks), dim3(kThreads), lds, s, a, n, k); break;
+    case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(blocks), dim3(kThreads), lds, s, a, n, k); break;
+    default: return -1;
+  }
+  return finish();
+}
+
+int ceil_write(void* dst, size_t bytes, int blocks, int per_cu, int unroll, void* stream) {
+  if (!dst || bytes % 16 || blocks < 1 || per_cu < 0) return -1;
+  const size_t n = bytes / 16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = moe::lds_cap_bytes(per_cu);
+  auto* b = static_cast<u32x4*>(dst);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(write_kernel<1>, dim3(blocks), dim3(kThreads), lds, s, b, n); break;
+    case 2: hipLaunchKernelGGL(write_kernel<2>, dim3(blocks), dim3(kThreads), lds, s, b, n); break;
+    case 4: hipLaunchKernelGGL(write_kernel<4>, dim3(blocks), dim3(kThreads), lds, s, b, n); break;
+    default: return -1;
+  }
+  return finish();
+}
+
+// Row kernels: `rows` rows of `row_bytes` (a multiple of 16) in both
+// buffers; perm holds `rows` values, each in [0, rows) (a permutation for
+// scatter, so that no two waves write one row). piece: 16-byte chunks per
+// wave, a multiple of 64.
+int ceil_rows(int gather, const void* src, void* dst, const int32_t* perm, int rows,
+              int row_bytes, int piece, int per_cu, void* stream) {
+  if (!src || !dst || !perm || rows < 1 || row_bytes < 16 || row_bytes % 16 || piece < 64 ||
+      piece % 64 || per_cu < 0)
+    return -1;
+  const int nch = row_bytes / 16;
+  const long long items = (long long)rows * ((nch + piece - 1) / piece);
+  const long long blocks = (items + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = moe::lds_cap_bytes(per_cu);
+  const auto* a = static_cast<const u32x4*>(src);
+  auto* b = static_cast<u32x4*>(dst);
+  if (gather)
+    hipLaunchKernelGGL(rows_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b,
+                       perm, rows, nch, piece);
+  else
+    hipLaunchKernelGGL(rows_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b,
+                       perm, rows, nch, piece);
+  return finish();
+}
+
+// Fan-out: `rows` src rows, rows * k dst rows of `row_bytes` (a multiple of
+// 16); perm is a permutation of [0, rows * k). piece: 64, 128, 256 or 448
+// chunks (448: a whole 7,168-byte row per wave).
+int ceil_fanout(const void* src, void* dst, const int32_t* perm, int rows, int k,
+                int row_bytes, int piece, int per_cu, void* stream) {
+  if (!src || !dst || !perm || rows < 1 || k < 1 || (long long)rows * k > 0x7FFFFFFF ||
+      row_bytes < 16 || row_bytes % 16 || per_cu < 0)
+    return -1;
+  const int nch = row_bytes / 16;
+  const long long items = (long long)rows * ((nch + piece - 1) / piece);
+  const long long blocks = (items + 3) / 4;
+  if (piece < 64 || blocks > 0x7FFFFFFF) return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = moe::lds_cap_bytes(per_cu);
+  const auto* a = static_cast<const u32x4*>(src);
+  auto* b = static_cast<u32x4*>(dst);
+  switch (piece) {
+    case 64: hipLaunchKernelGGL(fanout_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, k, nch); break;
+    case 128: hipLaunchKernelGGL(fanout_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, k, nch); break;
+    case 256: hipLaunchKernelGGL(fanout_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, k, nch); break;
+    case 448: hipLaunchKernelGGL(fanout_kernel<7>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, k, nch); break;
+    default: return -1;
+  }
+  return finish();
+}
+
+}  // extern "C"

@@ -178,8 +178,24 @@ class _FakeTorch:
         return False
 
 
-@pytest.mark.parametrize("group,steps", [(4, 13), (1, 5), (2, 8)])
-def test_pipelined_step_dependencies(group, steps):
+def test_pipeline_groups():
+    assert [list(g) for g in bench.pipeline_groups(10, 4, 1)] == [[0], [1, 2, 3, 4],
+                                                                  [5, 6, 7, 8], [9]]
+    assert [list(g) for g in bench.pipeline_groups(9, 4, 4)] == [[0, 1, 2, 3], [4, 5, 6, 7],
+                                                                 [8]]
+    assert [list(g) for g in bench.pipeline_groups(1, 4, 1)] == [[0]]
+    assert bench.pipeline_groups(0, 4, 1) == []
+    for steps in range(0, 30):
+        for group in (1, 2, 4, 8):
+            for lead in (1, 2, 3, 4, 9):
+                gs = bench.pipeline_groups(steps, group, lead)
+                assert [i for g in gs for i in g] == list(range(steps))
+                assert all(1 <= len(g) <= group for g in gs)
+
+
+@pytest.mark.parametrize("group,steps,lead", [(4, 13, 4), (1, 5, 1), (2, 8, 2), (4, 13, 1),
+                                              (4, 20, 1), (4, 3, 1), (2, 9, 1), (4, 14, 3)])
+def test_pipelined_step_dependencies(group, steps, lead):
     """bench.pipelined on a fake torch: the side stream runs the fronts, the
     current stream the backs; every step's back comes after its front, every
     front after the back of the step that last used its buffer set, and the
@@ -187,7 +203,7 @@ def test_pipelined_step_dependencies(group, steps):
     ft = _FakeTorch()
     nsets = 2 * group
     bench.pipelined(ft, lambda i, s: ft.op(("front", i, s)), lambda i, s: ft.op(("back", i, s)),
-                    nsets, steps, ft.side_stream, group)
+                    nsets, steps, ft.side_stream, group, lead)
     idx = {op[1]: n for n, op in enumerate(ft.ops)}
     for i in range(steps):
         s = i % nsets
@@ -197,6 +213,9 @@ def test_pipelined_step_dependencies(group, steps):
         if i >= nsets:                        # the previous user of set s is done first
             assert ft.before(idx[("back", i - nsets, s)], f), i
     # overlap: a front of group q + 1 does not wait for the backs of group q
-    for i in range(group, steps):
-        for j in range(i - i % group - group, i - i % group):
-            assert not ft.before(idx[("back", j, j % nsets)], idx[("front", i, i % nsets)]), (i, j)
+    groups = bench.pipeline_groups(steps, group, lead)
+    for q in range(1, len(groups)):
+        for i in groups[q]:
+            for j in groups[q - 1]:
+                assert not ft.before(idx[("back", j, j % nsets)],
+                                     idx[("front", i, i % nsets)]), (i, j)
