@@ -20,6 +20,12 @@ constexpr int kFp8RowsBlocksPerCu = 4;
 constexpr int kBf16FewBlocksPerCu = 4;
 // Steps (8 blocks of 128 columns) per row-held FP8 wave at most.
 constexpr int kFp8RowMaxSteps = 8;
+// Row-held MXFP8: steps of 512 columns per wave at most, and its cap.
+constexpr int kMxRowMaxSteps = 16;
+#ifndef MOE_MX_CAP
+#define MOE_MX_CAP 4
+#endif
+constexpr int kMxRowsBlocksPerCu = MOE_MX_CAP;
 
 __global__ __launch_bounds__(256) void dispatch_bf16_kernel(
     int T, int k, int nch, int parts, int cpp, int num_rows,
@@ -48,12 +54,25 @@ void launch_fp8_rows(int T, int H, int k, int parts, int bpp, int num_rows, cons
                      out_scales);
 }
 
-__global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(
+template <int MAXST>
+__global__ __launch_bounds__(256) void dispatch_mxfp8_rows_kernel(
     int T, int k, int H, int parts, int bpp, int num_rows,
     const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
     uint8_t* __restrict__ out, uint8_t* __restrict__ out_scales) {
-  dispatch_mxfp8_body(blockIdx.x, T, k, H, parts, bpp, num_rows, x, DstRows{dst_row}, out,
-                      out_scales);
+  dispatch_mxfp8_rows_body<MAXST>(blockIdx.x, T, k, H, parts, bpp, num_rows, x, dst_row, out,
+                                  out_scales);
+}
+
+template <int MAXST>
+void launch_mxfp8_rows(int T, int H, int k, int parts, int bpp, int num_rows, const void* x,
+                       const int32_t* dst_row, void* out, uint8_t* out_scales,
+                       hipStream_t stream) {
+  const int waves = T * parts;
+  hipLaunchKernelGGL((dispatch_mxfp8_rows_kernel<MAXST>),
+                     dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock), dim3(256),
+                     lds_cap_bytes(kMxRowsBlocksPerCu), stream, T, k, H, parts, bpp, num_rows,
+                     static_cast<const u32x4*>(x), dst_row, static_cast<uint8_t*>(out),
+                     out_scales);
 }
 
 }  // namespace
@@ -62,14 +81,24 @@ hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* 
                                  const int32_t* dst_row, void* out, uint8_t* out_scales,
                                  hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  // parts of at most kMxRowMaxSteps steps, as even as whole steps allow
   const int nb = H / MOE_MX_BLOCK;
-  int parts, bpp;
-  split_row(T, nb, kMxStepBlocks, 64 * kScaleSlots, &parts, &bpp);
-  const int waves = T * parts;
-  hipLaunchKernelGGL(dispatch_mxfp8_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
-                     dim3(256), 0, stream, T, k, H, parts, bpp, num_rows,
-                     static_cast<const u32x4*>(x), dst_row, static_cast<uint8_t*>(out),
-                     out_scales);
+  const int steps = (nb + kMxStepBlocks - 1) / kMxStepBlocks;
+  const int parts = (steps + kMxRowMaxSteps - 1) / kMxRowMaxSteps;
+  const int per = (steps + parts - 1) / parts;                 // steps per part, <= 16
+  const int bpp = per * kMxStepBlocks;
+  // instantiated for 1, 2, 4, 7, 8, 14 and 16 steps; a part of fewer steps
+  // runs in the next larger instance, its extra steps masked off
+#define MOE_MX_ROWS(n) \
+  launch_mxfp8_rows<n>(T, H, k, parts, bpp, num_rows, x, dst_row, out, out_scales, stream)
+  if (per <= 1) MOE_MX_ROWS(1);
+  else if (per <= 2) MOE_MX_ROWS(2);
+  else if (per <= 4) MOE_MX_ROWS(4);
+  else if (per <= 7) MOE_MX_ROWS(7);
+  else if (per <= 8) MOE_MX_ROWS(8);
+  else if (per <= 14) MOE_MX_ROWS(14);
+  else MOE_MX_ROWS(16);
+#undef MOE_MX_ROWS
   return hipGetLastError();
 }
 

@@ -460,6 +460,86 @@ __device__ __forceinline__ void dispatch_mxfp8_body(
   }
 }
 
+// MXFP8 with row-held waves: one wave per (token, part of at most MAXST
+// steps of 512 columns), the step layout and arithmetic of
+// dispatch_mxfp8_body. All loads of the part are issued first, the codes
+// (2 registers per step and lane) and scale bytes are kept, and each
+// destination row is then written as one contiguous run of 512-byte pieces
+// followed by its scale bytes.
+template <int MAXST>
+__device__ __forceinline__ void dispatch_mxfp8_rows_body(
+    int block, int T, int k, int H, int parts, int bpp, int num_rows,
+    const u32x4* __restrict__ x, const int32_t* __restrict__ dst_row,
+    uint8_t* __restrict__ out, uint8_t* __restrict__ out_scales) {
+  const int lane = threadIdx.x & 63;
+  const int gw = block * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= T * parts) return;
+  const int t = gw / parts;
+  const int nb = H / MOE_MX_BLOCK;
+  const int nch = H / 8;
+  const int b0 = (gw - t * parts) * bpp;
+  const int nbp = min(bpp, nb - b0);
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const int blk = lane >> 2;         // block inside a step
+  const int sub = lane & 3;          // 16-byte chunk inside the block
+  const u32x4* src = x + (size_t)t * nch;
+
+  u32x4 v[MAXST];
+#pragma unroll
+  for (int st = 0; st < MAXST; ++st) {
+    const int bl = st * kMxStepBlocks + blk;
+    v[st] = u32x4{0u, 0u, 0u, 0u};
+    if (bl < nbp) v[st] = stream_load(src + (b0 + bl) * 4 + sub);
+  }
+
+  uint32_t sreg[kScaleSlots];        // E8M0 byte of part-local block (s*64 + lane)
+#pragma unroll
+  for (int s = 0; s < kScaleSlots; ++s) sreg[s] = 0u;
+  u32x2 q[MAXST];
+#pragma unroll
+  for (int st = 0; st < MAXST; ++st) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w = v[st][c] & 0x7FFF7FFFu;
+      m = max(m, max(w & 0xFFFFu, w >> 16));
+    }
+    m = max(m, dpp_u32<0xB1>(m));
+    m = max(m, dpp_u32<0x4E>(m));
+    const float amax = __uint_as_float(m << 16);
+    int e = amax == 0.0f ? -127 : __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+    e = min(max(e, -127), 127);
+    const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
+    q[st][0] = quant_pair_hw(v[st][0], inv) | (quant_pair_hw(v[st][1], inv) << 16);
+    q[st][1] = quant_pair_hw(v[st][2], inv) | (quant_pair_hw(v[st][3], inv) << 16);
+    // lane L keeps the byte of part-local block L + 64*slot: in step st the
+    // lanes of row (st % 4) receive block (st*16 + L % 16) from its first lane
+    const uint32_t sb = (uint32_t)(e + 127);
+    const uint32_t got = (uint32_t)__shfl((int)sb, 4 * (lane & 15));
+#pragma unroll
+    for (int s = 0; s < kScaleSlots; ++s)
+      if (st / 4 == s && (lane >> 4) == (st & 3)) sreg[s] = got;
+  }
+
+  for (int j = 0; j < k; ++j) {
+    const int d = read_lane(my_dst, j);
+    if (d < 0 || d >= num_rows) continue;
+#pragma unroll
+    for (int st = 0; st < MAXST; ++st) {
+      const int bl = st * kMxStepBlocks + blk;
+      if (bl < nbp)
+        stream_store(q[st], reinterpret_cast<u32x2*>(out + (size_t)d * H +
+                                                     (size_t)(b0 + bl) * MOE_MX_BLOCK) + sub);
+    }
+    uint8_t* srow = out_scales + (size_t)d * nb + b0;
+#pragma unroll
+    for (int s = 0; s < kScaleSlots; ++s) {
+      const int b = s * 64 + lane;
+      if (b < nbp) srow[b] = (uint8_t)sreg[s];
+    }
+  }
+}
+
 // Split a row of `units` into parts so that the launch has about
 // kTargetWaves waves, each part a multiple of `align` units (but at least
 // `min_units` and at most `max_units` units).

@@ -582,6 +582,10 @@ MX_CASES = [
     (33, 1056, 5, 12, 3),            # capacity with drops; 33 blocks
     (40, 33280, 2, 4, 0),            # 1040 blocks: several parts per row
     (1500, 4096, 2, 8, 0),
+    (64, 8704, 3, 8, 0),             # 17 steps: two parts of 9 (the 14-step instance)
+    (90, 16384, 4, 16, 0),           # 32 steps: two parts of 16
+    (200, 1536, 8, 32, 0),           # 3 steps (the 4-step instance)
+    (10, 32, 1, 2, 0),               # one block
     (0, 256, 2, 8, 0),
 ]
 
