@@ -482,7 +482,9 @@ def ceilings(torch, np):
       scatter  sequential reads, random whole-row writes of 7,168-byte rows
                (its FP8 rows) (read + written)
       fanout   each 7,168-byte row read once and written to 8 random rows
-               (the dispatch's pattern at k = 8) (read + written)"""
+               (the dispatch's pattern at k = 8) (read + written)
+      shuffle  random whole-row reads and random whole-row writes of 14,336-
+               byte rows (the backward pair's and the partial combine's mix)"""
     import ctypes
 
     if not os.path.exists(CEIL_LIB):
@@ -540,7 +542,8 @@ def ceilings(torch, np):
     out["write"] = {"gbps": round(g, 1), "per_cu": c[0], "unroll": c[1]}
     gen = np.random.Generator(np.random.PCG64(12345))
     for name, gather, row_bytes, pieces in (("gather", 1, 14336, (128, 448, 896)),
-                                            ("scatter", 0, 7168, (64, 128, 448))):
+                                            ("scatter", 0, 7168, (64, 128, 448)),
+                                            ("shuffle", 2, 14336, (128, 256, 896))):
         rows = n // row_bytes
         perm = torch.from_numpy(gen.permutation(rows).astype(np.int32)).cuda()
         cfgs = [(p, pc) for p in pieces for pc in (0, 1, 2, 3, 4)]

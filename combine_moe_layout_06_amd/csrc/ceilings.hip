@@ -13,6 +13,8 @@
 //            writes (the combine reads its expert rows this way);
 //   scatter  dst row perm[i] = src row i: sequential reads, random whole-row
 //            writes;
+//   shuffle  dst row perm[i] = src row perm[rows-1-i]: random whole-row reads
+//            and writes (the backward pair's and the partial combine's mix);
 //   fanout   each src row read once and written to k rows dst[perm[i*k + j]]
 //            (the dispatch's pattern: one read, k random row writes).
 // Rows are read and written with nontemporal 16-byte accesses, one wave per
@@ -74,8 +76,9 @@ __global__ __launch_bounds__(kThreads) void write_kernel(u32x4* __restrict__ dst
 }
 
 // One wave per (row, piece); a piece is `piece` 16-byte chunks, one per lane
-// per step of 64. gather: dst[i] = src[perm[i]]; scatter: dst[perm[i]] = src[i].
-template <bool kGather>
+// per step of 64. Mode 1 (gather): dst[i] = src[perm[i]]; 0 (scatter):
+// dst[perm[i]] = src[i]; 2 (shuffle): dst[perm[i]] = src[perm[rows-1-i]].
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void rows_kernel(const u32x4* __restrict__ src,
                                                        u32x4* __restrict__ dst,
                                                        const int32_t* __restrict__ perm,
@@ -87,8 +90,10 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(const u32x4* __restrict_
   const int c0 = (int)(item - (long long)row * pieces) * piece;
   const int lane = threadIdx.x & 63;
   const int other = perm[row];
-  const u32x4* s = src + (size_t)(kGather ? other : row) * nch;
-  u32x4* d = dst + (size_t)(kGather ? row : other) * nch;
+  const int from = kMode == 1 ? other : kMode == 0 ? row : perm[rows - 1 - row];
+  const int to = kMode == 1 ? row : other;
+  const u32x4* s = src + (size_t)from * nch;
+  u32x4* d = dst + (size_t)to * nch;
   const int end = min(nch, c0 + piece);
   for (int c = c0 + lane; c < end; c += MOE_WAVE) stream_store(stream_load(s + c), d + c);
 }
@@ -186,9 +191,9 @@ int ceil_write(void* dst, size_t bytes, int blocks, int per_cu, int unroll, void
 
 // Row kernels: `rows` rows of `row_bytes` (a multiple of 16) in both
 // buffers; perm holds `rows` values, each in [0, rows) (a permutation for
-// scatter, so that no two waves write one row). piece: 16-byte chunks per
-// wave, a multiple of 64.
-int ceil_rows(int gather, const void* src, void* dst, const int32_t* perm, int rows,
+// scatter and shuffle, so that no two waves write one row). mode: 0 scatter,
+// 1 gather, 2 shuffle. piece: 16-byte chunks per wave, a multiple of 64.
+int ceil_rows(int mode, const void* src, void* dst, const int32_t* perm, int rows,
               int row_bytes, int piece, int per_cu, void* stream) {
   if (!src || !dst || !perm || rows < 1 || row_bytes < 16 || row_bytes % 16 || piece < 64 ||
       piece % 64 || per_cu < 0)
@@ -201,12 +206,12 @@ int ceil_rows(int gather, const void* src, void* dst, const int32_t* perm, int r
   const size_t lds = moe::lds_cap_bytes(per_cu);
   const auto* a = static_cast<const u32x4*>(src);
   auto* b = static_cast<u32x4*>(dst);
-  if (gather)
-    hipLaunchKernelGGL(rows_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b,
-                       perm, rows, nch, piece);
-  else
-    hipLaunchKernelGGL(rows_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b,
-                       perm, rows, nch, piece);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(rows_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, nch, piece); break;
+    case 1: hipLaunchKernelGGL(rows_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, nch, piece); break;
+    case 2: hipLaunchKernelGGL(rows_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, nch, piece); break;
+    default: return -1;
+  }
   return finish();
 }
 

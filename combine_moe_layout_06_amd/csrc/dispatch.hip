@@ -20,6 +20,23 @@ constexpr int kFp8RowsBlocksPerCu = 4;
 constexpr int kBf16FewBlocksPerCu = 4;
 // Steps (8 blocks of 128 columns) per row-held FP8 wave at most.
 constexpr int kFp8RowMaxSteps = 8;
+// Row-held kernels split a row into more parts while T * parts stays below
+// this many waves (one resident round at 4 workgroups per CU on 256 CUs):
+// one part per row at T = 4096, one step per part for decode-sized T.
+constexpr int kRowsMinWaves = 4096;
+
+// Parts of a row of `steps` steps: at least enough for `max_steps` steps per
+// part, more for small T (up to one step per part), as even as whole steps
+// allow; returns the steps per part.
+inline int row_parts(int T, int steps, int max_steps, int* parts) {
+  int p = (steps + max_steps - 1) / max_steps;
+  const int want = T > 0 ? (kRowsMinWaves + T - 1) / T : 1;
+  p = max(p, min(steps, want));
+  const int per = (steps + p - 1) / p;
+  *parts = (steps + per - 1) / per;
+  return per;
+}
+
 // Row-held MXFP8: steps of 512 columns per wave at most, and its cap.
 constexpr int kMxRowMaxSteps = 16;
 #ifndef MOE_MX_CAP
@@ -81,11 +98,10 @@ hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* 
                                  const int32_t* dst_row, void* out, uint8_t* out_scales,
                                  hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  // parts of at most kMxRowMaxSteps steps, as even as whole steps allow
   const int nb = H / MOE_MX_BLOCK;
   const int steps = (nb + kMxStepBlocks - 1) / kMxStepBlocks;
-  const int parts = (steps + kMxRowMaxSteps - 1) / kMxRowMaxSteps;
-  const int per = (steps + parts - 1) / parts;                 // steps per part, <= 16
+  int parts;
+  const int per = row_parts(T, steps, kMxRowMaxSteps, &parts);    // steps per part, <= 16
   const int bpp = per * kMxStepBlocks;
   // instantiated for 1, 2, 4, 7, 8, 14 and 16 steps; a part of fewer steps
   // runs in the next larger instance, its extra steps masked off
@@ -119,11 +135,10 @@ hipError_t launch_dispatch_fp8(int T, int H, int k, int num_rows, const void* x,
                                const int32_t* dst_row, void* out, float* out_scales,
                                hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  // parts of at most kFp8RowMaxSteps steps, as even as whole steps allow
   const int nb = H / MOE_FP8_BLOCK;
   const int steps = (nb + kFp8StepBlocks - 1) / kFp8StepBlocks;
-  const int parts = (steps + kFp8RowMaxSteps - 1) / kFp8RowMaxSteps;
-  const int per = (steps + parts - 1) / parts;                 // steps per part, <= 8
+  int parts;
+  const int per = row_parts(T, steps, kFp8RowMaxSteps, &parts);   // steps per part, <= 8
   const int bpp = per * kFp8StepBlocks;
 #define MOE_FP8_ROWS(n) \
   case n: launch_fp8_rows<n>(T, H, k, parts, bpp, num_rows, x, dst_row, out, out_scales, stream); break;
