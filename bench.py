@@ -37,6 +37,11 @@ Prints one JSON line. Besides the contract fields it carries:
   cold_us_per_step  the same step with a 1 GiB write between steps, which
                 evicts L2 and the 256 MB Infinity Cache
   serial_ms_per_step  the timed steps run one after the other on one stream
+  event_us_per_step_median/_p99  per-step times of the event pass (steps one
+                after the other, an event between phases)
+  pipelined_stamps  latency (route start to combine end) and interval (between
+                combine ends) percentiles of pipelined steps, from wall-clock
+                stamp kernels in a separate replay
   ceilings_gbps best GB/s of plain kernels (libmoe_ceilings.so) with the
                 path's access patterns: sequential copy, read and write, and
                 random whole-row gather (combine-like) and scatter
@@ -470,6 +475,76 @@ CEIL_BYTES = 1 << 30     # sequential probes: 1 GiB read and/or written
 CEIL_REPS = 10
 
 
+_measure_lib = None
+
+
+def measure_lib():
+    """libmoe_ceilings.so with its argument types (ceiling kernels, stamps)."""
+    global _measure_lib
+    if _measure_lib is None:
+        import ctypes
+
+        if not os.path.exists(CEIL_LIB):
+            raise RuntimeError("%s is missing; run `python -m combine_moe_layout_06_amd.build`"
+                               % CEIL_LIB)
+        L = ctypes.CDLL(CEIL_LIB)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.ceil_copy.argtypes = [vp, vp, sz, i32, i32, i32, vp]
+        L.ceil_read.argtypes = [vp, sz, vp, i32, i32, i32, vp]
+        L.ceil_write.argtypes = [vp, sz, i32, i32, i32, vp]
+        L.ceil_rows.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.ceil_fanout.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.bench_stamp.argtypes = [vp, i32, vp]
+        for f in (L.ceil_copy, L.ceil_read, L.ceil_write, L.ceil_rows, L.ceil_fanout,
+                  L.bench_stamp):
+            f.restype = i32
+        L.bench_stamp_hz.argtypes = []
+        L.bench_stamp_hz.restype = ctypes.c_double
+        _measure_lib = L
+    return _measure_lib
+
+
+def stamped_pipeline(torch, np, front, back, nsets, steps, side):
+    """Per-step latency and completion intervals of pipelined steps, from
+    the GPU's wall clock: the pipelined steps are captured again with a
+    one-wave stamp kernel before each step's front (on the side stream) and
+    after each step's back (on the current stream), replayed
+    GRAPH_WARM_REPLAYS times, then once for the stamps. The stamps add two
+    small kernels per step, so this pass is separate from the timed one and
+    reports its own us/step beside the percentiles."""
+    L = measure_lib()
+    hz = L.bench_stamp_hz()
+    if hz <= 0:
+        return None
+    st = torch.zeros((2, steps), dtype=torch.int64, device="cuda")
+
+    def stamp(slot):
+        rc = L.bench_stamp(st.data_ptr(), slot, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError("bench_stamp failed: %d" % rc)
+
+    def f(i, s):
+        stamp(i)
+        front(i, s)
+
+    def b(i, s):
+        back(i, s)
+        stamp(steps + i)
+
+    wall = timed_run(torch, lambda: pipelined(torch, f, b, nsets, steps, side), True)
+    t = st.cpu().numpy().astype(np.float64) * 1e6 / hz       # microseconds
+    lat = t[1] - t[0]
+    gap = np.diff(t[1])
+    pct = lambda a, q: round(float(np.percentile(a, q)), 2)
+    return {"us_per_step": round(wall * 1e6 / steps, 2),
+            "latency_us_p50": pct(lat, 50), "latency_us_p99": pct(lat, 99),
+            "interval_us_p50": pct(gap, 50), "interval_us_p99": pct(gap, 99),
+            "clock_hz": hz,
+            "what": "latency: a step's route start to its combine end; interval: between "
+                    "consecutive combine ends; one replay of the pipelined steps with a stamp "
+                    "kernel before each front and after each back"}
+
+
 def ceilings(torch, np):
     """Best GB/s of plain kernels with the path's access patterns on this GPU
     (libmoe_ceilings.so), each over a small sweep of launch shapes; HIP events
@@ -485,20 +560,7 @@ def ceilings(torch, np):
                (the dispatch's pattern at k = 8) (read + written)
       shuffle  random whole-row reads and random whole-row writes of 14,336-
                byte rows (the backward pair's and the partial combine's mix)"""
-    import ctypes
-
-    if not os.path.exists(CEIL_LIB):
-        raise RuntimeError("%s is missing; run `python -m combine_moe_layout_06_amd.build`"
-                           % CEIL_LIB)
-    L = ctypes.CDLL(CEIL_LIB)
-    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-    L.ceil_copy.argtypes = [vp, vp, sz, i32, i32, i32, vp]
-    L.ceil_read.argtypes = [vp, sz, vp, i32, i32, i32, vp]
-    L.ceil_write.argtypes = [vp, sz, i32, i32, i32, vp]
-    L.ceil_rows.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp]
-    L.ceil_fanout.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
-    for f in (L.ceil_copy, L.ceil_read, L.ceil_write, L.ceil_rows, L.ceil_fanout):
-        f.restype = i32
+    L = measure_lib()
 
     n = CEIL_BYTES
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -755,14 +817,11 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIP
     main.wait_stream(side)
 
 
-def overlapped_steps(torch, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
-    """The steps of serial_steps pipelined on two streams (pipelined()): the
-    route and layout of a group of steps run beside the dispatch and combine
-    of the group before, on the 2 * group layer buffers in `bufs` in turn.
-    Layout and dispatch are separate launches here even where
-    moe_layout_dispatch would fuse them (decode-sized capacity mode): the
-    layout is latency-bound, and on the side stream it is hidden. Every step
-    does all of its work; the results equal those of serial_steps."""
+def step_halves(w, bufs, inputs, y, first):
+    """front(i, s): route and layout of step i on buffer set s; back(i, s):
+    its dispatch and combine. Layout and dispatch are separate launches here
+    even where moe_layout_dispatch would fuse them (decode-sized capacity
+    mode): the layout is latency-bound, and on the side stream it is hidden."""
 
     def front(i, s):
         d = inputs[(first + i) % len(inputs)]
@@ -774,6 +833,16 @@ def overlapped_steps(torch, w, bufs, inputs, y, first, steps, side, group=PIPE_G
         bufs[s].dispatch(d["x"])
         bufs[s].combine(y)
 
+    return front, back
+
+
+def overlapped_steps(torch, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
+    """The steps of serial_steps pipelined on two streams (pipelined()): the
+    route and layout of a group of steps run beside the dispatch and combine
+    of the group before, on the 2 * group layer buffers in `bufs` in turn.
+    Every step does all of its work; the results equal those of
+    serial_steps."""
+    front, back = step_halves(w, bufs, inputs, y, first)
     pipelined(torch, front, back, len(bufs), steps, side, group)
 
 
@@ -940,6 +1009,12 @@ def main():
     ms_per_step = wall * 1e3 / steps
     value = w.tokens / (ms_per_step * 1e-3)
 
+    # ---- pipelined steps again with wall-clock stamps (latency percentiles)
+    stamped = None
+    if args.overlap and args.graph:
+        front_h, back_h = step_halves(w, bufs, inputs, y, warm)
+        stamped = stamped_pipeline(torch, np, front_h, back_h, len(bufs), steps, side)
+
     # ---- cold steps: 1 GiB write between steps (untimed)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
@@ -1002,6 +1077,7 @@ def main():
         "phase_bytes": nbytes,
         "event_us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
         "event_us_per_step_p99": round(float(np.percentile(step_ms, 99)) * 1e3, 2),
+        "pipelined_stamps": stamped,
         "cold_us_per_step": round(float(np.median(cold)) * 1e3, 2) if cold else None,
         "copy_ceiling_gbps": ceil["copy"]["gbps"],
         "ceilings_gbps": ceil,

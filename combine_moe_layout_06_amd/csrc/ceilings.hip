@@ -17,6 +17,9 @@
 //            and writes (the backward pair's and the partial combine's mix);
 //   fanout   each src row read once and written to k rows dst[perm[i*k + j]]
 //            (the dispatch's pattern: one read, k random row writes).
+// Beside them, bench_stamp writes the GPU's wall clock into a slot of a
+// buffer from a one-wave kernel, so that the benchmark can time steps inside
+// a replayed graph without events (latency and interval percentiles).
 // Rows are read and written with nontemporal 16-byte accesses, one wave per
 // row piece of `piece` chunks, as the path's kernels do. The sequential
 // kernels loop over the buffer with a grid of `blocks` workgroups of 256
@@ -129,6 +132,13 @@ __global__ __launch_bounds__(kThreads) void fanout_kernel(const u32x4* __restric
   }
 }
 
+// Lane 0 stores the constant-rate wall clock (s_memrealtime) into stamps[slot].
+__global__ __launch_bounds__(64) void stamp_kernel(unsigned long long* __restrict__ stamps,
+                                                  int slot) {
+  const unsigned long long now = wall_clock64();
+  if (threadIdx.x == 0) stamps[slot] = now;
+}
+
 int finish() { return (int)hipGetLastError(); }
 
 }  // namespace
@@ -239,6 +249,27 @@ int ceil_fanout(const void* src, void* dst, const int32_t* perm, int rows, int k
     default: return -1;
   }
   return finish();
+}
+
+// One-wave kernel that writes the wall clock into stamps[slot] (stamps: a
+// device buffer of uint64 with more than `slot` entries).
+int bench_stamp(void* stamps, int slot, void* stream) {
+  if (!stamps || slot < 0) return -1;
+  hipLaunchKernelGGL(stamp_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<unsigned long long*>(stamps), slot);
+  return finish();
+}
+
+// Ticks per second of the clock bench_stamp reads, on the current device
+// (0 if the attribute cannot be read).
+double bench_stamp_hz() {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0.0;
+  }
+  return 1e3 * (double)khz;
 }
 
 }  // extern "C"

@@ -39,6 +39,12 @@ def test_bench_line(args, pipelined):
     assert ("pipelined" in d["launch"]) == pipelined
     if not pipelined:
         assert d["ms_per_step"] == d["serial_ms_per_step"]
+        assert d["pipelined_stamps"] is None
+    else:
+        st = d["pipelined_stamps"]
+        assert 0 < st["interval_us_p50"] <= st["interval_us_p99"]
+        assert 0 < st["latency_us_p50"] <= st["latency_us_p99"]
+        assert st["latency_us_p50"] >= st["interval_us_p50"] * 0.5
     roof = d["roofline"]
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
     assert 0 < roof["frac"] <= 1.0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
