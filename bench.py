@@ -16,9 +16,9 @@ in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
-streams in groups of 4 steps (the first group holds one step): the route and
-layout of one group run beside the dispatch and combine of the group before,
-on 8 sets of layer buffers used in turn (--serial: one step after the other; the default with --eager). The serial rate of the
+streams in groups of 4 steps: the route and layout of one group run beside the
+dispatch and combine of the group before, on 8 sets of layer buffers used in
+turn (--serial: one step after the other; the default with --eager). The serial rate of the
 same steps is measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
@@ -281,12 +281,12 @@ def run_hierarchical(args, w, M, W, torch, np):
             bias=torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None,
             x=torch.from_numpy(inp.x.view(np.int16)).to(dev)))
     overlap = args.graph if args.overlap is None else args.overlap
-    nsets = 2 * PIPE_GROUP if overlap else 1
-    sets = [(M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev,
-                                     dtype=dtype),
-             M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev))
-            for _ in range(nsets)]
-    lb, rb = sets[0]
+    lb = M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev,
+                                 dtype=dtype)
+    rb = M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev)
+    # pipelined steps: layout buffers of their own per step, row buffers shared
+    nsets = max(args.steps, args.warmup) if overlap else 1
+    sets = [(lb, rb)] + [(lb.sharing_rows(), rb.sharing_rows()) for _ in range(nsets - 1)]
 
     phases = ["route", "layout", "rank_layout", "dispatch", "expand", "combine_local",
               "combine_partials"]
@@ -310,8 +310,7 @@ def run_hierarchical(args, w, M, W, torch, np):
             back(i, 0)
 
     def piped(first, n):
-        pipelined(torch, lambda i, s: front(first + i, s), lambda i, s: back(first + i, s),
-                  nsets, n, side)
+        pipelined(torch, lambda i: front(first + i, i), lambda i: back(first + i, i), n, side)
 
     side = torch.cuda.Stream() if overlap else None
 
@@ -367,10 +366,10 @@ def run_hierarchical(args, w, M, W, torch, np):
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams in groups of %d (the first of %d): the "
-                   "route, expert layout and (token, rank) layout of one group run beside "
-                   "the send, fan-out and combines of the group before (%d buffer sets in "
-                   "turn)" % (PIPE_GROUP, PIPE_LEAD, 2 * PIPE_GROUP) if overlap
+                  ("; steps pipelined on two streams: the route, expert layout and (token, "
+                   "rank) layout of every step run ahead on the second stream (layout buffers "
+                   "of their own per step), the send, fan-out and combines follow in order on "
+                   "the first, which waits once per group of %d steps" % PIPE_GROUP if overlap
                    else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 5),
         "config": {"workload": "%s hierarchical: T=%d H=%d E=%d k=%d R=%d, one row per "
@@ -504,7 +503,7 @@ def measure_lib():
     return _measure_lib
 
 
-def stamped_pipeline(torch, np, front, back, nsets, steps, side):
+def stamped_pipeline(torch, np, front, back, steps, side):
     """Per-step latency and completion intervals of pipelined steps, from
     the GPU's wall clock: the pipelined steps are captured again with a
     one-wave stamp kernel before each step's front (on the side stream) and
@@ -523,15 +522,15 @@ def stamped_pipeline(torch, np, front, back, nsets, steps, side):
         if rc != 0:
             raise RuntimeError("bench_stamp failed: %d" % rc)
 
-    def f(i, s):
+    def f(i):
         stamp(i)
-        front(i, s)
+        front(i)
 
-    def b(i, s):
-        back(i, s)
+    def b(i):
+        back(i)
         stamp(steps + i)
 
-    wall = timed_run(torch, lambda: pipelined(torch, f, b, nsets, steps, side), True)
+    wall = timed_run(torch, lambda: pipelined(torch, f, b, steps, side), True)
     t = st.cpu().numpy().astype(np.float64) * 1e6 / hz       # microseconds
     lat = t[1] - t[0]
     gap = np.diff(t[1])
@@ -771,79 +770,73 @@ def serial_steps(w, bufs, inputs, y, first, steps):
 
 
 PIPE_GROUP = 4   # steps per cross-stream wait of the pipelined mode
-PIPE_LEAD = 1    # steps of the first group, whose fronts nothing can hide
+PIPE_LEAD = 4    # steps of the first group
 
 
 def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
     """Groups of the pipelined mode: the first `lead` steps, then groups of
-    `group` steps (the last one shorter). The first group's fronts run with
-    nothing beside them, so a short first group exposes one front, not
-    `group` of them; the next group's fronts then hide behind its backs."""
+    `group` steps (the last one shorter)."""
     first = min(max(lead, 1), group, steps)
     out = [range(0, first)] if steps else []
     out += [range(g0, min(g0 + group, steps)) for g0 in range(first, steps, group)]
     return out
 
 
-def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIPE_LEAD):
-    """Steps pipelined on two streams, in the groups of pipeline_groups():
-    `side` runs front(i, s) for the steps of one group while the current
-    stream runs back(i, s) for the group before; then the current stream
-    waits for the side stream once and runs back() for the group. Step i uses
-    buffer set s = i % nsets (nsets = 2 * group). Two consecutive groups hold
-    at most nsets steps, so the steps that last used the sets of group q are
-    in group q - 2 or earlier: the fronts of group q wait, once, until the
-    backs of group q - 2 are done. One event per group in each direction:
-    each cross-stream edge costs the stream after it a few microseconds."""
-    assert nsets == 2 * group
+def pipelined(torch, front, back, steps, side, group=PIPE_GROUP, lead=PIPE_LEAD):
+    """Steps pipelined on two streams. `side` runs front(i) (route and layout)
+    of every step in order and as early as it can: each step's front writes
+    buffers of its own, so it waits for nothing but the work queued before
+    the call. The current stream runs back(i) (dispatch and combine) of the
+    steps in order, in the groups of pipeline_groups(), waiting once per
+    group for the side stream to have finished that group's fronts. The
+    backs share one set of row buffers, which the current stream uses one
+    step after the other. Cross-stream order comes from events, which a graph
+    capture turns into edges; each edge costs the stream after it a few
+    microseconds, hence one per group."""
     main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
-    released = []
-    for _ in range(2):
-        e = torch.cuda.Event()
-        e.record(main)
-        released.append(e)
-    for q, grp in enumerate(pipeline_groups(steps, group, lead)):
-        side.wait_event(released[q % 2])
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    for grp in pipeline_groups(steps, group, lead):
         with torch.cuda.stream(side):
             for i in grp:
-                front(i, i % nsets)
+                front(i)
         ready = torch.cuda.Event()
         ready.record(side)
         main.wait_event(ready)
         for i in grp:
-            back(i, i % nsets)
-        released[q % 2] = torch.cuda.Event()
-        released[q % 2].record(main)
+            back(i)
     main.wait_stream(side)
 
 
-def step_halves(w, bufs, inputs, y, first):
-    """front(i, s): route and layout of step i on buffer set s; back(i, s):
-    its dispatch and combine. Layout and dispatch are separate launches here
-    even where moe_layout_dispatch would fuse them (decode-sized capacity
-    mode): the layout is latency-bound, and on the side stream it is hidden."""
+def step_halves(w, sets, inputs, y, first):
+    """front(i): route and layout of step i on sets[i]; back(i): its dispatch
+    and combine. Layout and dispatch are separate launches here even where
+    moe_layout_dispatch would fuse them (decode-sized capacity mode): the
+    layout is latency-bound, and on the side stream it is hidden."""
 
-    def front(i, s):
+    def front(i):
         d = inputs[(first + i) % len(inputs)]
-        bufs[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        bufs[s].layout()
+        sets[i].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        sets[i].layout()
 
-    def back(i, s):
+    def back(i):
         d = inputs[(first + i) % len(inputs)]
-        bufs[s].dispatch(d["x"])
-        bufs[s].combine(y)
+        sets[i].dispatch(d["x"])
+        sets[i].combine(y)
 
     return front, back
 
 
-def overlapped_steps(torch, w, bufs, inputs, y, first, steps, side, group=PIPE_GROUP):
+def overlapped_steps(torch, w, sets, inputs, y, first, steps, side, group=PIPE_GROUP):
     """The steps of serial_steps pipelined on two streams (pipelined()): the
-    route and layout of a group of steps run beside the dispatch and combine
-    of the group before, on the 2 * group layer buffers in `bufs` in turn.
+    route and layout of every step run ahead on the second stream, each on
+    its own routing and layout buffers (sets[i], which share their row
+    buffers); the dispatch and combine follow in order on the current stream.
     Every step does all of its work; the results equal those of
     serial_steps."""
-    front, back = step_halves(w, bufs, inputs, y, first)
-    pipelined(torch, front, back, len(bufs), steps, side, group)
+    front, back = step_halves(w, sets, inputs, y, first)
+    pipelined(torch, front, back, steps, side, group)
 
 
 GRAPH_WARM_REPLAYS = 3   # untimed replays of a captured graph before the timed one
@@ -931,10 +924,10 @@ def main():
     # us/step eager, 18.3 against 20.1 replayed)
     if args.overlap is None:
         args.overlap = args.graph
-    # pipelined steps use 2 * PIPE_GROUP layer buffers in turn
-    bufs = [buf] + ([M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
-                                             w.capacity, device=dev, dtype=dtype)
-                     for _ in range(2 * PIPE_GROUP - 1)] if args.overlap else [])
+    # pipelined steps: routing and layout buffers of their own per step, the
+    # row buffers of `buf` shared (the backs run one after the other)
+    bufs = [buf] + ([buf.sharing_rows() for _ in range(max(steps, warm) - 1)]
+                    if args.overlap else [])
     side = torch.cuda.Stream() if args.overlap else None
 
     def front(i):
@@ -1013,7 +1006,7 @@ def main():
     stamped = None
     if args.overlap and args.graph:
         front_h, back_h = step_halves(w, bufs, inputs, y, warm)
-        stamped = stamped_pipeline(torch, np, front_h, back_h, len(bufs), steps, side)
+        stamped = stamped_pipeline(torch, np, front_h, back_h, steps, side)
 
     # ---- cold steps: 1 GiB write between steps (untimed)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -1054,10 +1047,10 @@ def main():
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams in groups of %d (the first of %d): the "
-                   "route and layout of one group run beside the dispatch and combine of "
-                   "the group before (%d layer buffers in turn)"
-                   % (PIPE_GROUP, PIPE_LEAD, 2 * PIPE_GROUP)
+                  ("; steps pipelined on two streams: the route and layout of every step "
+                   "run ahead on the second stream (routing and layout buffers of their own "
+                   "per step), the dispatch and combine follow in order on the first, which "
+                   "waits once per group of %d steps" % PIPE_GROUP
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"

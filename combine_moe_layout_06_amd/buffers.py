@@ -90,6 +90,20 @@ class LayerBuffers:
         b.combined = torch.empty((max(t, 1), hidden), dtype=torch.int16, device=device)
         return b
 
+    def sharing_rows(self, with_rank_tokens=True) -> "LayerBuffers":
+        """A buffer set of the same shape with its own routing and layout
+        buffers (topk, counts, offsets, dst_row, src_pair, workspace) but this
+        set's dispatched, scales and combined rows: for steps whose route and
+        layout may run ahead while earlier steps still dispatch and combine
+        on another stream, one step after the other."""
+        dev = self.topk_idx.device
+        b = LayerBuffers.allocate(self.tokens, 0, self.experts, self.top_k, self.ranks,
+                                  self.capacity, device=dev, with_rank_tokens=with_rank_tokens,
+                                  dtype=MOE_DTYPE_BF16)
+        b.hidden, b.dtype = self.hidden, self.dtype
+        b.dispatched, b.scales, b.combined = self.dispatched, self.scales, self.combined
+        return b
+
     def route(self, logits, bias, score_fn, num_groups=1, topk_groups=1, stream=None):
         moe_route(self.tokens, self.experts, self.top_k, logits, bias, score_fn, num_groups,
                   topk_groups, self.topk_idx, self.topk_weights, stream)
@@ -172,6 +186,16 @@ class RankBuffers:
         else:
             b.sent = torch.empty((n, hidden), dtype=torch.int16, device=device)
         b.partial = torch.empty((n, hidden), dtype=torch.int16, device=device)
+        return b
+
+    def sharing_rows(self) -> "RankBuffers":
+        """A set of the same shape with its own (token, rank) layout buffers
+        but this set's sent rows, their scales and the partial rows (see
+        LayerBuffers.sharing_rows)."""
+        b = RankBuffers.allocate(self.tokens, 0, self.experts, self.top_k, self.ranks,
+                                 MOE_DTYPE_BF16, device=self.rank_row.device)
+        b.hidden, b.dtype = self.hidden, self.dtype
+        b.sent, b.sent_scales, b.partial = self.sent, self.sent_scales, self.partial
         return b
 
     def rank_layout(self, topk_idx, stream=None):

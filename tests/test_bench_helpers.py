@@ -194,28 +194,31 @@ def test_pipeline_groups():
 
 
 @pytest.mark.parametrize("group,steps,lead", [(4, 13, 4), (1, 5, 1), (2, 8, 2), (4, 13, 1),
-                                              (4, 20, 1), (4, 3, 1), (2, 9, 1), (4, 14, 3)])
+                                              (4, 20, 4), (4, 3, 4), (2, 9, 1), (4, 14, 3)])
 def test_pipelined_step_dependencies(group, steps, lead):
     """bench.pipelined on a fake torch: the side stream runs the fronts, the
-    current stream the backs; every step's back comes after its front, every
-    front after the back of the step that last used its buffer set, and the
-    fronts of a group may run beside the backs of the group before."""
+    current stream the backs, each in step order; every back comes after its
+    own front and after the work queued before the call; no front waits for
+    any back (each step's front has buffers of its own); the backs of a group
+    wait for no front of a later group."""
     ft = _FakeTorch()
-    nsets = 2 * group
-    bench.pipelined(ft, lambda i, s: ft.op(("front", i, s)), lambda i, s: ft.op(("back", i, s)),
-                    nsets, steps, ft.side_stream, group, lead)
+    ft.op(("before",))
+    bench.pipelined(ft, lambda i: ft.op(("front", i)), lambda i: ft.op(("back", i)),
+                    steps, ft.side_stream, group, lead)
     idx = {op[1]: n for n, op in enumerate(ft.ops)}
+    before = idx[("before",)]
     for i in range(steps):
-        s = i % nsets
-        f, b = idx[("front", i, s)], idx[("back", i, s)]
+        f, b = idx[("front", i)], idx[("back", i)]
         assert ft.ops[f][0] == "side" and ft.ops[b][0] == "main"
         assert ft.before(f, b), i
-        if i >= nsets:                        # the previous user of set s is done first
-            assert ft.before(idx[("back", i - nsets, s)], f), i
-    # overlap: a front of group q + 1 does not wait for the backs of group q
+        assert ft.before(before, f), i
+        if i:
+            assert ft.before(idx[("front", i - 1)], f) and ft.before(idx[("back", i - 1)], b)
+        for j in range(steps):
+            assert not ft.before(idx[("back", j)], f), (i, j)
     groups = bench.pipeline_groups(steps, group, lead)
-    for q in range(1, len(groups)):
-        for i in groups[q]:
-            for j in groups[q - 1]:
-                assert not ft.before(idx[("back", j, j % nsets)],
-                                     idx[("front", i, i % nsets)]), (i, j)
+    for q, grp in enumerate(groups):
+        later = [i for g in groups[q + 1:] for i in g]
+        for i in grp:
+            for j in later:
+                assert not ft.before(idx[("front", j)], idx[("back", i)]), (i, j)

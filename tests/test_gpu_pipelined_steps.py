@@ -1,7 +1,10 @@
-"""The benchmark's pipelined steps (the route and layout of a group of steps
-on a side stream beside the dispatch and combine of the group before, 2 *
-group layer buffers in turn) give the same results as the same steps run one
-after the other: eager, and captured in a HIP graph and replayed."""
+"""The benchmark's pipelined steps (the route and layout of every step run
+ahead on a side stream, each on routing and layout buffers of its own; the
+dispatch and combine follow in order on the current stream, sharing one set
+of row buffers) give the same results as the same steps run one after the
+other: eager, and captured in a HIP graph and replayed. Every step has its
+own inputs, so a step that read another step's layout would be caught; the
+shared row buffers end with the last step's rows and output."""
 
 import os
 import sys
@@ -20,8 +23,8 @@ import combine_moe_layout_06_amd as M  # noqa: E402
 from gpu_helpers import dev  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
-NAMES = ("topk_idx", "topk_weights", "dst_row", "src_pair", "expert_counts", "expert_offsets",
-         "rank_counts", "rank_token_counts", "overflow", "combined")
+SMALL = ("topk_idx", "topk_weights", "dst_row", "src_pair", "expert_counts", "expert_offsets",
+         "rank_counts", "rank_token_counts", "overflow")
 
 
 def say(*a):
@@ -37,110 +40,131 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _state(b):
-    out = {n: getattr(b, n).clone() for n in NAMES}
+def _small(b):
+    return {n: getattr(b, n).clone() for n in SMALL}
+
+
+def _rows(b):
     live = b.src_pair >= 0
-    out["rows"] = b.dispatched[live].clone()
+    out = {"rows": b.dispatched[live].clone(), "combined": b.combined.clone()}
     if b.scales is not None:
         out["scales"] = b.scales[live].clone()
     return out
 
 
-def _poison(bufs):
-    for b in bufs:
-        for n in NAMES:
+def _poison(sets):
+    for b in sets:
+        for n in SMALL:
             v = getattr(b, n)
             v.fill_(-7.0 if v.dtype == torch.float32 else -7)
-        b.dispatched.fill_(0x55)
+    sets[0].dispatched.fill_(0x55)
+    sets[0].combined.fill_(-7)
 
 
-@pytest.mark.parametrize("name,steps,group", [("dsv3", 10, 4), ("dsv3", 5, 1), ("decode", 11, 4)])
+def _check(sets, want_small, want_rows, what):
+    for i, b in enumerate(sets):
+        for n, v in want_small[i].items():
+            assert torch.equal(getattr(b, n), v), (what, i, n)
+    last = sets[len(sets) - 1]
+    for n, v in want_rows.items():
+        got = _rows(last)[n]
+        assert torch.equal(got, v), (what, "rows of the last step", n)
+
+
+@pytest.mark.parametrize("name,steps,group", [("dsv3", 6, 4), ("dsv3", 5, 1), ("decode", 11, 4)])
 def test_pipelined_steps_equal_serial_steps(name, steps, group):
     w = W.WORKLOADS[name]
     say("pipelined steps", name, "x", steps, "in groups of", group)
-    seeds = [w.step_seed0 + i for i in range(steps)] if w.steps > 1 else [0]
+    seeds = [w.step_seed0 + i for i in range(steps)] if w.steps > 1 else list(range(steps))
     inputs = []
     for s in seeds:
         inp = W.make_inputs(w, s)
         inputs.append(dict(logits=dev(inp.logits),
                            bias=dev(inp.bias) if inp.bias is not None else None,
                            x=dev(inp.x)))
-    bufs = [M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
-                                    dtype=w.dispatch_dtype) for _ in range(2 * group)]
+    base = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                   dtype=w.dispatch_dtype)
+    sets = [base] + [base.sharing_rows() for _ in range(steps - 1)]
     g = np.random.Generator(np.random.PCG64(3))
-    y = dev(W.random_bf16_rows(g, bufs[0].num_rows, w.hidden))
+    y = dev(W.random_bf16_rows(g, base.num_rows, w.hidden))
 
-    # serial reference of the last two steps, each alone in bufs[0]
-    want = {}
-    for i in (steps - 2, steps - 1):
-        bench.serial_steps(w, bufs, inputs, y, i, 1)
+    # serial reference: every step alone in its own buffers
+    ref = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                  dtype=w.dispatch_dtype)
+    want_small, want_rows = [], None
+    for i in range(steps):
+        bench.serial_steps(w, [ref], inputs, y, i, 1)
         torch.cuda.synchronize()
-        want[i] = _state(bufs[0])
+        want_small.append(_small(ref))
+    want_rows = _rows(ref)
 
     side = torch.cuda.Stream()
-    _poison(bufs)
-    bench.overlapped_steps(torch, w, bufs, inputs, y, 0, steps, side, group)
+    _poison(sets)
+    bench.overlapped_steps(torch, w, sets, inputs, y, 0, steps, side, group)
     torch.cuda.synchronize()
-    for i in (steps - 2, steps - 1):
-        got = _state(bufs[i % (2 * group)])
-        for n, v in want[i].items():
-            assert torch.equal(got[n], v), ("eager", i, n)
+    _check(sets, want_small, want_rows, "eager")
     say("  eager pipelined steps equal the serial ones")
 
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        bench.overlapped_steps(torch, w, bufs, inputs, y, 0, steps, side, group)
+        bench.overlapped_steps(torch, w, sets, inputs, y, 0, steps, side, group)
     for rep in range(2):
-        _poison(bufs)
+        _poison(sets)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for i in (steps - 2, steps - 1):
-            got = _state(bufs[i % (2 * group)])
-            for n, v in want[i].items():
-                assert torch.equal(got[n], v), ("graph", rep, i, n)
+        _check(sets, want_small, want_rows, "graph %d" % rep)
     say("  graph replays equal the serial steps")
 
 
 def test_pipelined_hierarchical_steps_equal_serial_steps():
     """The hierarchical pass pipelined the same way (route, expert layout and
-    (token, rank) layout of a group beside the send, fan-out and combines of
-    the group before), replayed from a graph, against the same steps run one
-    after the other."""
+    (token, rank) layout of every step ahead on the side stream, the send,
+    fan-out and combines in order on the current stream), replayed from a
+    graph, against the same steps run one after the other: every step's
+    (token, rank) layout, and the last step's partials and output."""
     w = W.WORKLOADS["dsv3"]
-    group, steps = 2, 6
-    inp = W.make_inputs(w, 0)
-    inputs = [dict(logits=dev(inp.logits), bias=dev(inp.bias), x=dev(inp.x))]
-    sets = [(M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, 0,
-                                     dtype=w.dispatch_dtype),
-             M.RankBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
-                                    dtype=w.dispatch_dtype))
-            for _ in range(2 * group)]
+    group, steps = 2, 5
+    inputs = []
+    for s in range(steps):
+        inp = W.make_inputs(w, 10 + s)
+        inputs.append(dict(logits=dev(inp.logits), bias=dev(inp.bias), x=dev(inp.x)))
+    lb0 = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, 0,
+                                  dtype=w.dispatch_dtype)
+    rb0 = M.RankBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
+                                 dtype=w.dispatch_dtype)
+    sets = [(lb0, rb0)] + [(lb0.sharing_rows(), rb0.sharing_rows()) for _ in range(steps - 1)]
     g = np.random.Generator(np.random.PCG64(4))
-    y = dev(W.random_bf16_rows(g, sets[0][0].num_rows, w.hidden))
-    bench.hierarchical_front(w, sets, inputs, 0, 0)
-    bench.hierarchical_back(sets, inputs, y, 0, 0)
-    torch.cuda.synchronize()
-    n_sent = int(sets[0][1].rank_token_offsets[-1].item())   # partial rows written
-    want = [sets[0][0].combined.clone(), sets[0][1].send_row.clone(),
-            sets[0][1].partial[:n_sent].clone()]
+    y = dev(W.random_bf16_rows(g, lb0.num_rows, w.hidden))
+    ref = [(M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, 0,
+                                    dtype=w.dispatch_dtype),
+            M.RankBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
+                                   dtype=w.dispatch_dtype))]
+    want_send = []
+    for i in range(steps):
+        bench.hierarchical_front(w, ref, inputs, i, 0)
+        bench.hierarchical_back(ref, inputs, y, i, 0)
+        torch.cuda.synchronize()
+        want_send.append(ref[0][1].send_row.clone())
+    n_sent = int(ref[0][1].rank_token_offsets[-1].item())   # partial rows of the last step
+    want = [ref[0][0].combined.clone(), ref[0][1].partial[:n_sent].clone()]
     side = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        bench.pipelined(torch, lambda i, s: bench.hierarchical_front(w, sets, inputs, i, s),
-                        lambda i, s: bench.hierarchical_back(sets, inputs, y, i, s),
-                        2 * group, steps, side, group)
+        bench.pipelined(torch, lambda i: bench.hierarchical_front(w, sets, inputs, i, i),
+                        lambda i: bench.hierarchical_back(sets, inputs, y, i, i),
+                        steps, side, group)
     for rep in range(2):
         for lb, rb in sets:
-            lb.combined.fill_(-7)
             rb.send_row.fill_(-7)
-            rb.partial.fill_(-7)
+        lb0.combined.fill_(-7)
+        rb0.partial.fill_(-7)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for lb, rb in sets:
-            assert torch.equal(lb.combined, want[0]), rep
-            assert torch.equal(rb.send_row, want[1]), rep
-            assert torch.equal(rb.partial[:n_sent], want[2]), rep
-    say("  pipelined hierarchical graph replays equal the serial step")
+        for i, (lb, rb) in enumerate(sets):
+            assert torch.equal(rb.send_row, want_send[i]), (rep, i)
+        assert torch.equal(lb0.combined, want[0]), rep
+        assert torch.equal(rb0.partial[:n_sent], want[1]), rep
+    say("  pipelined hierarchical graph replays equal the serial steps")
