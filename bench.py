@@ -494,6 +494,8 @@ def measure_lib():
         L.ceil_rows.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp]
         L.ceil_fanout.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.bench_stamp.argtypes = [vp, i32, vp]
+        L.ceil_rows_one_way.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+        L.ceil_rows_one_way.restype = i32
         for f in (L.ceil_copy, L.ceil_read, L.ceil_write, L.ceil_rows, L.ceil_fanout,
                   L.bench_stamp):
             f.restype = i32
@@ -535,13 +537,16 @@ def stamped_pipeline(torch, np, front, back, steps, side):
     lat = t[1] - t[0]
     gap = np.diff(t[1])
     pct = lambda a, q: round(float(np.percentile(a, q)), 2)
+    first = float(lat[0] - (np.median(gap) if len(gap) else 0.0))
     return {"us_per_step": round(wall * 1e6 / steps, 2),
             "latency_us_p50": pct(lat, 50), "latency_us_p99": pct(lat, 99),
             "interval_us_p50": pct(gap, 50), "interval_us_p99": pct(gap, 99),
+            "fill_us": round(first, 2),
             "clock_hz": hz,
             "what": "latency: a step's route start to its combine end; interval: between "
-                    "consecutive combine ends; one replay of the pipelined steps with a stamp "
-                    "kernel before each front and after each back"}
+                    "consecutive combine ends; fill: the first step's latency minus the median "
+                    "interval (the front work nothing hides); one replay of the pipelined steps "
+                    "with a stamp kernel before each front and after each back"}
 
 
 def ceilings(torch, np):
@@ -558,7 +563,9 @@ def ceilings(torch, np):
       fanout   each 7,168-byte row read once and written to 8 random rows
                (the dispatch's pattern at k = 8) (read + written)
       shuffle  random whole-row reads and random whole-row writes of 14,336-
-               byte rows (the backward pair's and the partial combine's mix)"""
+               byte rows (the backward pair's and the partial combine's mix)
+      rread    random whole-row reads of 14,336-byte rows, nothing written
+      rwrite   random whole-row writes of 7,168-byte rows, nothing read"""
     L = measure_lib()
 
     n = CEIL_BYTES
@@ -611,6 +618,17 @@ def ceilings(torch, np):
         g, c = best(2 * rows * row_bytes, cfgs,
                     lambda p, pc: L.ceil_rows(gather, a.data_ptr(), b.data_ptr(),
                                               perm.data_ptr(), rows, row_bytes, p, pc, stream))
+        out[name] = {"gbps": round(g, 1), "row_bytes": row_bytes, "piece_bytes": 16 * c[0],
+                     "per_cu": c[1]}
+    for name, mode, row_bytes, pieces in (("rread", 0, 14336, (128, 448, 896)),
+                                          ("rwrite", 1, 7168, (64, 448))):
+        rows = n // row_bytes
+        perm = torch.from_numpy(gen.permutation(rows).astype(np.int32)).cuda()
+        cfgs = [(p, pc) for p in pieces for pc in (0, 2, 3, 4)]
+        g, c = best(rows * row_bytes, cfgs,
+                    lambda p, pc: L.ceil_rows_one_way(mode, a.data_ptr(), b.data_ptr(),
+                                                      perm.data_ptr(), rows, row_bytes, p, pc,
+                                                      sink.data_ptr(), stream))
         out[name] = {"gbps": round(g, 1), "row_bytes": row_bytes, "piece_bytes": 16 * c[0],
                      "per_cu": c[1]}
     row_bytes, k = 7168, 8

@@ -15,6 +15,8 @@
 //            writes;
 //   shuffle  dst row perm[i] = src row perm[rows-1-i]: random whole-row reads
 //            and writes (the backward pair's and the partial combine's mix);
+//   rread    src row perm[i] read, nothing written: random whole-row reads only;
+//   rwrite   dst row perm[i] written, nothing read: random whole-row writes only;
 //   fanout   each src row read once and written to k rows dst[perm[i*k + j]]
 //            (the dispatch's pattern: one read, k random row writes).
 // Beside them, bench_stamp writes the GPU's wall clock into a slot of a
@@ -139,6 +141,34 @@ __global__ __launch_bounds__(64) void stamp_kernel(unsigned long long* __restric
   if (threadIdx.x == 0) stamps[slot] = now;
 }
 
+// One wave per (row, piece): mode 0 reads src row perm[i] (folding the data
+// into a value that is stored only if it matches a pattern the benchmark's
+// data never holds), mode 1 writes a constant into dst row perm[i].
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void rows_one_way_kernel(
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, const int32_t* __restrict__ perm,
+    int rows, int nch, int piece, uint32_t* __restrict__ sink) {
+  const int pieces = (nch + piece - 1) / piece;
+  const long long item = (long long)blockIdx.x * (kThreads / MOE_WAVE) + (threadIdx.x >> 6);
+  if (item >= (long long)rows * pieces) return;
+  const int row = (int)(item / pieces);
+  const int c0 = (int)(item - (long long)row * pieces) * piece;
+  const int lane = threadIdx.x & 63;
+  const size_t base = (size_t)perm[row] * nch;
+  const int end = min(nch, c0 + piece);
+  if (kMode == 0) {
+    uint32_t acc = 0;
+    for (int c = c0 + lane; c < end; c += MOE_WAVE) {
+      const u32x4 v = stream_load(src + base + c);
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+  } else {
+    const u32x4 v = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    for (int c = c0 + lane; c < end; c += MOE_WAVE) stream_store(v, dst + base + c);
+  }
+}
+
 int finish() { return (int)hipGetLastError(); }
 
 }  // namespace
@@ -222,6 +252,32 @@ int ceil_rows(int mode, const void* src, void* dst, const int32_t* perm, int row
     case 2: hipLaunchKernelGGL(rows_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, nch, piece); break;
     default: return -1;
   }
+  return finish();
+}
+
+// One-way row kernels: mode 0 reads `rows` rows of `row_bytes` of src in the
+// order perm (sink: one uint32 of device memory), mode 1 writes the rows of
+// dst in that order. perm: a permutation of [0, rows); piece: a multiple of
+// 64 chunks.
+int ceil_rows_one_way(int mode, const void* src, void* dst, const int32_t* perm, int rows,
+                      int row_bytes, int piece, int per_cu, void* sink, void* stream) {
+  if (!perm || rows < 1 || row_bytes < 16 || row_bytes % 16 || piece < 64 || piece % 64 ||
+      per_cu < 0 || (mode == 0 && (!src || !sink)) || (mode == 1 && !dst) || mode < 0 ||
+      mode > 1)
+    return -1;
+  const int nch = row_bytes / 16;
+  const long long items = (long long)rows * ((nch + piece - 1) / piece);
+  const long long blocks = (items + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = moe::lds_cap_bytes(per_cu);
+  const auto* a = static_cast<const u32x4*>(src);
+  auto* b = static_cast<u32x4*>(dst);
+  auto* k = static_cast<uint32_t*>(sink);
+  if (mode == 0)
+    hipLaunchKernelGGL(rows_one_way_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, nch, piece, k);
+  else
+    hipLaunchKernelGGL(rows_one_way_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), lds, s, a, b, perm, rows, nch, piece, k);
   return finish();
 }
 
