@@ -284,8 +284,9 @@ def run_hierarchical(args, w, M, W, torch, np):
     lb = M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev,
                                  dtype=dtype)
     rb = M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev)
-    # pipelined steps: layout buffers of their own per step, row buffers shared
-    nsets = max(args.steps, args.warmup) if overlap else 1
+    # pipelined steps: 2 * PIPE_GROUP sets of layout buffers in turn, row
+    # buffers shared
+    nsets = 2 * PIPE_GROUP if overlap else 1
     sets = [(lb, rb)] + [(lb.sharing_rows(), rb.sharing_rows()) for _ in range(nsets - 1)]
 
     phases = ["route", "layout", "rank_layout", "dispatch", "expand", "combine_local",
@@ -310,7 +311,8 @@ def run_hierarchical(args, w, M, W, torch, np):
             back(i, 0)
 
     def piped(first, n):
-        pipelined(torch, lambda i: front(first + i, i), lambda i: back(first + i, i), n, side)
+        pipelined(torch, lambda i, s: front(first + i, s), lambda i, s: back(first + i, s),
+                  nsets, n, side)
 
     side = torch.cuda.Stream() if overlap else None
 
@@ -366,10 +368,11 @@ def run_hierarchical(args, w, M, W, torch, np):
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams: the route, expert layout and (token, "
-                   "rank) layout of every step run ahead on the second stream (layout buffers "
-                   "of their own per step), the send, fan-out and combines follow in order on "
-                   "the first, which waits once per group of %d steps" % PIPE_GROUP if overlap
+                  ("; steps pipelined on two streams in groups of %d (the first of %d): the "
+                   "route, expert layout and (token, rank) layout of one group run beside "
+                   "the send, fan-out and combines of the group before (%d sets of layout "
+                   "buffers in turn, row buffers shared)"
+                   % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP), 2 * PIPE_GROUP) if overlap
                    else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 5),
         "config": {"workload": "%s hierarchical: T=%d H=%d E=%d k=%d R=%d, one row per "
@@ -505,7 +508,7 @@ def measure_lib():
     return _measure_lib
 
 
-def stamped_pipeline(torch, np, front, back, steps, side):
+def stamped_pipeline(torch, np, front, back, nsets, steps, side):
     """Per-step latency and completion intervals of pipelined steps, from
     the GPU's wall clock: the pipelined steps are captured again with a
     one-wave stamp kernel before each step's front (on the side stream) and
@@ -524,15 +527,15 @@ def stamped_pipeline(torch, np, front, back, steps, side):
         if rc != 0:
             raise RuntimeError("bench_stamp failed: %d" % rc)
 
-    def f(i):
+    def f(i, s):
         stamp(i)
-        front(i)
+        front(i, s)
 
-    def b(i):
-        back(i)
+    def b(i, s):
+        back(i, s)
         stamp(steps + i)
 
-    wall = timed_run(torch, lambda: pipelined(torch, f, b, steps, side), True)
+    wall = timed_run(torch, lambda: pipelined(torch, f, b, nsets, steps, side), True)
     t = st.cpu().numpy().astype(np.float64) * 1e6 / hz       # microseconds
     lat = t[1] - t[0]
     gap = np.diff(t[1])
@@ -800,61 +803,70 @@ def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
     return out
 
 
-def pipelined(torch, front, back, steps, side, group=PIPE_GROUP, lead=PIPE_LEAD):
-    """Steps pipelined on two streams. `side` runs front(i) (route and layout)
-    of every step in order and as early as it can: each step's front writes
-    buffers of its own, so it waits for nothing but the work queued before
-    the call. The current stream runs back(i) (dispatch and combine) of the
-    steps in order, in the groups of pipeline_groups(), waiting once per
-    group for the side stream to have finished that group's fronts. The
-    backs share one set of row buffers, which the current stream uses one
-    step after the other. Cross-stream order comes from events, which a graph
-    capture turns into edges; each edge costs the stream after it a few
-    microseconds, hence one per group."""
+def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIPE_LEAD):
+    """Steps pipelined on two streams, in the groups of pipeline_groups():
+    `side` runs front(i, s) (route and layout) for the steps of one group
+    while the current stream runs back(i, s) (dispatch and combine) for the
+    group before; then the current stream waits for the side stream once and
+    runs back() for the group. Step i uses the routing and layout buffers of
+    set s = i % nsets (nsets = 2 * group); the backs share one set of row
+    buffers, used one step after the other on the current stream. Two
+    consecutive groups hold at most nsets steps, so the steps that last used
+    the sets of group q are in group q - 2 or earlier: the fronts of group q
+    wait, once, until the backs of group q - 2 are done. One event per group
+    in each direction: each cross-stream edge costs the stream after it a few
+    microseconds. (Without the release waits, with buffers of its own for
+    every step, the side stream could run all fronts ahead; replayed, that
+    graph ran decode steps 22% slower and dsv3 steps no faster.)"""
+    assert nsets == 2 * group
     main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
-    start = torch.cuda.Event()
-    start.record(main)
-    side.wait_event(start)
-    for grp in pipeline_groups(steps, group, lead):
+    released = []
+    for _ in range(2):
+        e = torch.cuda.Event()
+        e.record(main)
+        released.append(e)
+    for q, grp in enumerate(pipeline_groups(steps, group, lead)):
+        side.wait_event(released[q % 2])
         with torch.cuda.stream(side):
             for i in grp:
-                front(i)
+                front(i, i % nsets)
         ready = torch.cuda.Event()
         ready.record(side)
         main.wait_event(ready)
         for i in grp:
-            back(i)
+            back(i, i % nsets)
+        released[q % 2] = torch.cuda.Event()
+        released[q % 2].record(main)
     main.wait_stream(side)
 
 
 def step_halves(w, sets, inputs, y, first):
-    """front(i): route and layout of step i on sets[i]; back(i): its dispatch
-    and combine. Layout and dispatch are separate launches here even where
-    moe_layout_dispatch would fuse them (decode-sized capacity mode): the
-    layout is latency-bound, and on the side stream it is hidden."""
+    """front(i, s): route and layout of step i on buffer set s; back(i, s):
+    its dispatch and combine. Layout and dispatch are separate launches here
+    even where moe_layout_dispatch would fuse them (decode-sized capacity
+    mode): the layout is latency-bound, and on the side stream it is hidden."""
 
-    def front(i):
+    def front(i, s):
         d = inputs[(first + i) % len(inputs)]
-        sets[i].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        sets[i].layout()
+        sets[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
+        sets[s].layout()
 
-    def back(i):
+    def back(i, s):
         d = inputs[(first + i) % len(inputs)]
-        sets[i].dispatch(d["x"])
-        sets[i].combine(y)
+        sets[s].dispatch(d["x"])
+        sets[s].combine(y)
 
     return front, back
 
 
 def overlapped_steps(torch, w, sets, inputs, y, first, steps, side, group=PIPE_GROUP):
     """The steps of serial_steps pipelined on two streams (pipelined()): the
-    route and layout of every step run ahead on the second stream, each on
-    its own routing and layout buffers (sets[i], which share their row
-    buffers); the dispatch and combine follow in order on the current stream.
-    Every step does all of its work; the results equal those of
-    serial_steps."""
+    route and layout of a group of steps run beside the dispatch and combine
+    of the group before, on the 2 * group buffer sets in `sets` in turn
+    (routing and layout buffers of their own, row buffers shared). Every step
+    does all of its work; the results equal those of serial_steps."""
     front, back = step_halves(w, sets, inputs, y, first)
-    pipelined(torch, front, back, steps, side, group)
+    pipelined(torch, front, back, len(sets), steps, side, group)
 
 
 GRAPH_WARM_REPLAYS = 3   # untimed replays of a captured graph before the timed one
@@ -942,9 +954,9 @@ def main():
     # us/step eager, 18.3 against 20.1 replayed)
     if args.overlap is None:
         args.overlap = args.graph
-    # pipelined steps: routing and layout buffers of their own per step, the
-    # row buffers of `buf` shared (the backs run one after the other)
-    bufs = [buf] + ([buf.sharing_rows() for _ in range(max(steps, warm) - 1)]
+    # pipelined steps: 2 * PIPE_GROUP sets of routing and layout buffers in
+    # turn, the row buffers of `buf` shared (the backs run one after the other)
+    bufs = [buf] + ([buf.sharing_rows() for _ in range(2 * PIPE_GROUP - 1)]
                     if args.overlap else [])
     side = torch.cuda.Stream() if args.overlap else None
 
@@ -1024,7 +1036,7 @@ def main():
     stamped = None
     if args.overlap and args.graph:
         front_h, back_h = step_halves(w, bufs, inputs, y, warm)
-        stamped = stamped_pipeline(torch, np, front_h, back_h, steps, side)
+        stamped = stamped_pipeline(torch, np, front_h, back_h, len(bufs), steps, side)
 
     # ---- cold steps: 1 GiB write between steps (untimed)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -1065,10 +1077,10 @@ def main():
         "dtype": {0: "bf16", 1: "fp8e4m3+bf16", 2: "mxfp8e4m3+bf16"}[dtype],
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
-                  ("; steps pipelined on two streams: the route and layout of every step "
-                   "run ahead on the second stream (routing and layout buffers of their own "
-                   "per step), the dispatch and combine follow in order on the first, which "
-                   "waits once per group of %d steps" % PIPE_GROUP
+                  ("; steps pipelined on two streams in groups of %d (the first of %d): the "
+                   "route and layout of one group run beside the dispatch and combine of the "
+                   "group before (%d sets of routing and layout buffers in turn, row buffers "
+                   "shared)" % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP), 2 * PIPE_GROUP)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"

@@ -198,27 +198,27 @@ def test_pipeline_groups():
 def test_pipelined_step_dependencies(group, steps, lead):
     """bench.pipelined on a fake torch: the side stream runs the fronts, the
     current stream the backs, each in step order; every back comes after its
-    own front and after the work queued before the call; no front waits for
-    any back (each step's front has buffers of its own); the backs of a group
-    wait for no front of a later group."""
+    own front, every front after the work queued before the call and after
+    the back of the step that last used its buffer set; the fronts of a group
+    do not wait for the backs of the group before (they run beside them)."""
     ft = _FakeTorch()
     ft.op(("before",))
-    bench.pipelined(ft, lambda i: ft.op(("front", i)), lambda i: ft.op(("back", i)),
-                    steps, ft.side_stream, group, lead)
+    nsets = 2 * group
+    bench.pipelined(ft, lambda i, s: ft.op(("front", i, s)), lambda i, s: ft.op(("back", i, s)),
+                    nsets, steps, ft.side_stream, group, lead)
     idx = {op[1]: n for n, op in enumerate(ft.ops)}
     before = idx[("before",)]
     for i in range(steps):
-        f, b = idx[("front", i)], idx[("back", i)]
+        s = i % nsets
+        f, b = idx[("front", i, s)], idx[("back", i, s)]
         assert ft.ops[f][0] == "side" and ft.ops[b][0] == "main"
         assert ft.before(f, b), i
         assert ft.before(before, f), i
-        if i:
-            assert ft.before(idx[("front", i - 1)], f) and ft.before(idx[("back", i - 1)], b)
-        for j in range(steps):
-            assert not ft.before(idx[("back", j)], f), (i, j)
+        if i >= nsets:                        # the previous user of set s is done first
+            assert ft.before(idx[("back", i - nsets, s)], f), i
     groups = bench.pipeline_groups(steps, group, lead)
-    for q, grp in enumerate(groups):
-        later = [i for g in groups[q + 1:] for i in g]
-        for i in grp:
-            for j in later:
-                assert not ft.before(idx[("front", j)], idx[("back", i)]), (i, j)
+    for q in range(1, len(groups)):
+        for i in groups[q]:
+            for j in groups[q - 1]:
+                assert not ft.before(idx[("back", j, j % nsets)],
+                                     idx[("front", i, i % nsets)]), (i, j)

@@ -1,10 +1,11 @@
-"""The benchmark's pipelined steps (the route and layout of every step run
-ahead on a side stream, each on routing and layout buffers of its own; the
-dispatch and combine follow in order on the current stream, sharing one set
-of row buffers) give the same results as the same steps run one after the
-other: eager, and captured in a HIP graph and replayed. Every step has its
-own inputs, so a step that read another step's layout would be caught; the
-shared row buffers end with the last step's rows and output."""
+"""The benchmark's pipelined steps (the route and layout of a group of steps
+on a side stream beside the dispatch and combine of the group before, 2 *
+group sets of routing and layout buffers in turn, one shared set of row
+buffers) give the same results as the same steps run one after the other:
+eager, and captured in a HIP graph and replayed. Every step has its own
+inputs, so a step that read another step's layout would be caught; each set
+ends with the layout of the last step that used it, and the shared row
+buffers with the last step's rows and output."""
 
 import os
 import sys
@@ -62,16 +63,17 @@ def _poison(sets):
 
 
 def _check(sets, want_small, want_rows, what):
-    for i, b in enumerate(sets):
+    steps = len(want_small)
+    for i in range(max(0, steps - len(sets)), steps):      # the last user of each set
         for n, v in want_small[i].items():
-            assert torch.equal(getattr(b, n), v), (what, i, n)
-    last = sets[len(sets) - 1]
+            assert torch.equal(getattr(sets[i % len(sets)], n), v), (what, i, n)
+    last = sets[(steps - 1) % len(sets)]
     for n, v in want_rows.items():
         got = _rows(last)[n]
         assert torch.equal(got, v), (what, "rows of the last step", n)
 
 
-@pytest.mark.parametrize("name,steps,group", [("dsv3", 6, 4), ("dsv3", 5, 1), ("decode", 11, 4)])
+@pytest.mark.parametrize("name,steps,group", [("dsv3", 10, 4), ("dsv3", 5, 1), ("decode", 11, 4)])
 def test_pipelined_steps_equal_serial_steps(name, steps, group):
     w = W.WORKLOADS[name]
     say("pipelined steps", name, "x", steps, "in groups of", group)
@@ -84,7 +86,7 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
                            x=dev(inp.x)))
     base = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
                                    dtype=w.dispatch_dtype)
-    sets = [base] + [base.sharing_rows() for _ in range(steps - 1)]
+    sets = [base] + [base.sharing_rows() for _ in range(2 * group - 1)]
     g = np.random.Generator(np.random.PCG64(3))
     y = dev(W.random_bf16_rows(g, base.num_rows, w.hidden))
 
@@ -120,10 +122,10 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
 
 def test_pipelined_hierarchical_steps_equal_serial_steps():
     """The hierarchical pass pipelined the same way (route, expert layout and
-    (token, rank) layout of every step ahead on the side stream, the send,
-    fan-out and combines in order on the current stream), replayed from a
-    graph, against the same steps run one after the other: every step's
-    (token, rank) layout, and the last step's partials and output."""
+    (token, rank) layout of a group beside the send, fan-out and combines of
+    the group before), replayed from a graph, against the same steps run one
+    after the other: each set's (token, rank) layout of the last step that
+    used it, and the last step's partials and output."""
     w = W.WORKLOADS["dsv3"]
     group, steps = 2, 5
     inputs = []
@@ -134,7 +136,7 @@ def test_pipelined_hierarchical_steps_equal_serial_steps():
                                   dtype=w.dispatch_dtype)
     rb0 = M.RankBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                                  dtype=w.dispatch_dtype)
-    sets = [(lb0, rb0)] + [(lb0.sharing_rows(), rb0.sharing_rows()) for _ in range(steps - 1)]
+    sets = [(lb0, rb0)] + [(lb0.sharing_rows(), rb0.sharing_rows()) for _ in range(2 * group - 1)]
     g = np.random.Generator(np.random.PCG64(4))
     y = dev(W.random_bf16_rows(g, lb0.num_rows, w.hidden))
     ref = [(M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, 0,
@@ -152,9 +154,9 @@ def test_pipelined_hierarchical_steps_equal_serial_steps():
     side = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        bench.pipelined(torch, lambda i: bench.hierarchical_front(w, sets, inputs, i, i),
-                        lambda i: bench.hierarchical_back(sets, inputs, y, i, i),
-                        steps, side, group)
+        bench.pipelined(torch, lambda i, s: bench.hierarchical_front(w, sets, inputs, i, s),
+                        lambda i, s: bench.hierarchical_back(sets, inputs, y, i, s),
+                        2 * group, steps, side, group)
     for rep in range(2):
         for lb, rb in sets:
             rb.send_row.fill_(-7)
@@ -163,8 +165,8 @@ def test_pipelined_hierarchical_steps_equal_serial_steps():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for i, (lb, rb) in enumerate(sets):
-            assert torch.equal(rb.send_row, want_send[i]), (rep, i)
+        for i in range(steps - 2 * group, steps):              # the last user of each set
+            assert torch.equal(sets[i % (2 * group)][1].send_row, want_send[i]), (rep, i)
         assert torch.equal(lb0.combined, want[0]), rep
         assert torch.equal(rb0.partial[:n_sent], want[1]), rep
     say("  pipelined hierarchical graph replays equal the serial steps")
