@@ -778,15 +778,22 @@ def cpu_baseline(w, seed, dtype=None):
             "single_thread": dict(single, sample="first %d tokens, one thread" % ts)}
 
 
-def serial_steps(w, bufs, inputs, y, first, steps):
+def serial_steps(w, bufs, inputs, y, first, steps, fuse=True):
     """`steps` steps one after the other on the current stream: route,
-    layout + dispatch (moe_layout_dispatch), combine; step i uses the inputs
-    of step first + i."""
+    layout + dispatch, combine; step i uses the inputs of step first + i.
+    fuse: layout and dispatch through moe_layout_dispatch (one launch for
+    decode-sized inputs in capacity mode: the fewest launches for steps
+    launched from the host), else moe_layout then moe_dispatch (faster from a
+    graph, where a launch costs little: decode 17.9 against 19.7 us/step)."""
     b = bufs[0]
     for i in range(steps):
         d = inputs[(first + i) % len(inputs)]
         b.route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        b.layout_dispatch(d["x"])
+        if fuse:
+            b.layout_dispatch(d["x"])
+        else:
+            b.layout()
+            b.dispatch(d["x"])
         b.combine(y)
 
 
@@ -990,13 +997,14 @@ def main():
     total_bytes = sum(nbytes.values())
 
     # ---- warmup
-    serial_steps(w, bufs, inputs, y, 0, warm)
+    serial_steps(w, bufs, inputs, y, 0, warm, fuse=not args.graph)
     if args.overlap:
         overlapped_steps(torch, w, bufs, inputs, y, 0, warm, side)
     torch.cuda.synchronize()
 
     # ---- timed steps: back to back, nothing but the path on the stream(s)
-    serial_wall = timed_run(torch, lambda: serial_steps(w, bufs, inputs, y, warm, steps), args.graph)
+    serial_wall = timed_run(torch, lambda: serial_steps(w, bufs, inputs, y, warm, steps,
+                                                        fuse=not args.graph), args.graph)
     wall = (timed_run(torch, lambda: overlapped_steps(torch, w, bufs, inputs, y, warm, steps, side),
                       args.graph) if args.overlap else serial_wall)
 

@@ -9,8 +9,8 @@
 // sections "Megatron-LM (NVIDIA)" and "Défis et optimisations" (capacity
 // and token dropping).
 //
-// Two launches (one when all pairs fit in one tile, three for many tiles), no
-// global atomics, deterministic:
+// Two launches (one when all pairs fit in one tile: layout_one_tile_kernel,
+// three for many tiles), no global atomics, deterministic:
 //   1. count: one block per tile of whole tokens builds the tile's expert
 //      histogram (and per-rank distinct-token counts) in LDS and writes it
 //      to the workspace.
@@ -242,9 +242,11 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
   }
 }
 
-// self_count: all pairs form one tile (T*k <= kTilePairs) and no count pass
-// ran. Every block loads all pairs and builds the histogram itself (block 0
-// also the distinct-token counts), so the layout takes a single launch; the
+// self_count (the layout blocks of the fused layout + dispatch launch, whose
+// blocks have 256 threads): all pairs form one tile (T*k <= kTilePairs) and
+// no count pass ran. Every block loads all pairs and builds the histogram
+// itself (block 0 also the distinct-token counts), so the layout needs no
+// launch before it; the
 // pairs are then loaded chunk-major (chunk c of wave w = pairs
 // [(4c + w)*64, +64)), and block b places chunk b only, after the pairs of
 // the chunks before it, so up to four blocks share the placement.
@@ -509,6 +511,181 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
                     self_count, num_rows, idx, ws_hist, ws_rhist, ws_tot, ws_rtot,
                     expert_counts, expert_offsets, rank_counts, rank_offsets, rank_token_counts,
                     dst_row, src_pair, overflow);
+}
+
+// ---------------------------------------------------------------------------
+// One tile (T*k <= 1024 pairs) in one launch of 1024-thread blocks. Wave w of
+// every block holds pairs [64w, 64w + 64), one per lane, so the per-wave
+// counts of all pairs take a single ballot round per expert-id bit and each
+// wave has one chunk to place: the chain of dependent steps is a quarter of
+// the 256-thread form's. Every block builds the same counts; block 0 writes
+// the counts and offsets and places the pairs, and every wave of the grid
+// marks the unused rows of about one expert (capacity mode) or the rows past
+// the last pair (packed mode).
+// ---------------------------------------------------------------------------
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / MOE_WAVE;
+static_assert(kOneThreads == kTilePairs, "one pair per thread");
+
+// Exclusive scan of s[0..n) in place (n <= kOneThreads) by a 1024-thread
+// block; returns the total to every thread.
+__device__ int block_exclusive_scan_one(int* s, int n, int* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v = tid < n ? s[tid] : 0;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int run = incl - v, total = 0;
+#pragma unroll
+  for (int w = 0; w < kOneWaves; ++w) {
+    const int x = s_wave[w];
+    if (w < wave) run += x;
+    total += x;
+  }
+  if (tid < n) s[tid] = run;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
+    int T, int E, int k, int R, int epr, int epr_shift, int cap, int num_rows,
+    const int32_t* __restrict__ idx, int32_t* __restrict__ expert_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ rank_token_counts,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_pair,
+    int32_t* __restrict__ overflow) {
+  __shared__ int s_cnt[kOneWaves][MOE_MAX_EXPERTS];
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_rtc[MOE_MAX_EXPERTS];
+  __shared__ int s_rank[kTilePairs];
+  __shared__ uint32_t s_rmask[kRankMaskWords];
+  __shared__ int s_wave[kOneWaves];
+  __shared__ int s_overflow;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool lead = blockIdx.x == 0;
+  const int np = T * k;
+  const int raw = tid < np ? idx[tid] : -1;
+  if (tid < E)
+    for (int w = 0; w < kOneWaves; ++w) s_cnt[w][tid] = 0;
+  const int mask_words = (T + 31) / 32;
+  const bool rtc = lead && rank_token_counts != nullptr;
+  const bool masks = rtc && R * mask_words <= kRankMaskWords;
+  if (rtc && tid < R) s_rtc[tid] = 0;
+  if (masks)
+    for (int i = tid; i < R * mask_words; i += kOneThreads) s_rmask[i] = 0u;
+  if (tid == 0) s_overflow = 0;
+  __syncthreads();
+
+  // the wave's pairs of one expert (one ballot per expert-id bit); the
+  // lowest of them stores their number
+  const int e = clean_expert(raw, E);
+  const uint64_t peers = peer_mask((uint32_t)e, e >= 0, ceil_log2(E));
+  const int below = count_below(peers);
+  if (e >= 0 && below == 0) s_cnt[wave][e] = __popcll(peers);
+  if (rtc) {
+    const int r = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+    if (tid < np) s_rank[tid] = r;
+    if (masks && r >= 0) {
+      const int t = tid / k;
+      atomicOr(&s_rmask[r * mask_words + (t >> 5)], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+
+  // chain the waves: s_cnt[w][e] becomes the first position of wave w's
+  // pairs of expert e; totals and (capacity mode) fixed offsets
+  if (tid < E) {
+    int c[kOneWaves];
+#pragma unroll
+    for (int w = 0; w < kOneWaves; ++w) c[w] = s_cnt[w][tid];
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kOneWaves; ++w) {
+      s_cnt[w][tid] = run;
+      run += c[w];
+    }
+    s_tot[tid] = run;
+    s_off[tid] = cap > 0 ? tid * cap : run;
+  }
+  if (cap > 0 && tid == 0) s_off[E] = E * cap;
+  if (masks) {
+    if (tid < R) {
+      int n = 0;
+      for (int i = 0; i < mask_words; ++i) n += __popc(s_rmask[tid * mask_words + i]);
+      s_rtc[tid] = n;
+    }
+  } else if (rtc) {
+    // one thread per token: a rank counts once, at its first slot
+    for (int t = tid; t < T; t += kOneThreads) {
+      const int* rk = s_rank + t * k;
+      for (int j = 0; j < k; ++j) {
+        const int x = rk[j];
+        bool first = x >= 0;
+        for (int o = 0; o < j; ++o) first = first && rk[o] != x;
+        if (first) atomicAdd(&s_rtc[x], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (cap == 0) {
+    const int total = block_exclusive_scan_one(s_off, E, s_wave);
+    if (tid == 0) s_off[E] = total;
+  }
+  __syncthreads();
+
+  if (lead) {
+    if (tid < E) {
+      expert_counts[tid] = s_tot[tid];
+      expert_offsets[tid] = s_off[tid];
+      if (cap > 0 && s_tot[tid] > cap) atomicAdd(&s_overflow, s_tot[tid] - cap);
+    }
+    if (tid < R) {
+      int rows = 0;
+      for (int x = tid * epr; x < (tid + 1) * epr; ++x) rows += cap > 0 ? min(s_tot[x], cap) : s_tot[x];
+      rank_counts[tid] = rows;
+      rank_offsets[tid] = s_off[tid * epr];
+      if (rtc) rank_token_counts[tid] = s_rtc[tid];
+    }
+    if (tid == 0) {
+      expert_offsets[E] = s_off[E];
+      rank_offsets[R] = s_off[E];
+    }
+    // stable row: the pairs of e in the waves before, then lane order
+    int dst = -1;
+    if (e >= 0) {
+      const int pos = s_cnt[wave][e] + below;
+      if (cap == 0) dst = s_off[e] + pos;
+      else if (pos < cap) dst = e * cap + pos;
+    }
+    if (tid < np) {
+      dst_row[tid] = dst;
+      if (dst >= 0 && dst < num_rows) src_pair[dst] = tid;
+    }
+  }
+
+  // rows that receive no pair are marked -1; all waves of the grid share it
+  const int gwave = blockIdx.x * kOneWaves + wave, nwaves = gridDim.x * kOneWaves;
+  if (cap == 0) {
+    for (int row = s_off[E] + gwave * MOE_WAVE + lane; row < num_rows; row += nwaves * MOE_WAVE)
+      src_pair[row] = -1;
+  } else {
+    for (int x = gwave; x < E; x += nwaves) {
+      const int end = (x + 1) * cap;
+      for (int row = x * cap + min(s_tot[x], cap) + lane; row < end; row += MOE_WAVE)
+        src_pair[row] = -1;
+    }
+  }
+  if (lead) {
+    __syncthreads();
+    if (tid == 0) overflow[0] = s_overflow;
+  }
 }
 
 // Fused layout + dispatch for one tile in capacity mode (decode-sized
@@ -784,11 +961,20 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   int32_t* ws_hist = static_cast<int32_t*>(workspace);
   int32_t* ws_rhist = rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
-  const int self_count = T * k <= kTilePairs ? 1 : 0;
+  const bool self_count = T * k <= kTilePairs;
   const bool scan = !self_count && layout_scans(ntiles, E);
   int32_t* ws_tot = scan ? ws_hist + (size_t)2 * ntiles * E : nullptr;
   int32_t* ws_rtot = scan && ws_rhist != nullptr ? ws_tot + E : nullptr;
-  if (ntiles > 0 && !self_count) {
+  if (self_count) {
+    // capacity mode: enough waves that each marks the unused rows of about
+    // one expert
+    const int blocks = cap > 0 ? (E + kOneWaves - 1) / kOneWaves : 1;
+    hipLaunchKernelGGL(layout_one_tile_kernel, dim3(blocks), dim3(kOneThreads), 0, stream, T, E,
+                       k, R, epr, epr_shift, cap, num_rows, idx, expert_counts, expert_offsets,
+                       rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
+    return hipGetLastError();
+  }
+  if (ntiles > 0) {
     hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
                        T, E, k, R, epr, epr_shift, tt, idx, ws_hist, ws_rhist);
     hipError_t err = hipGetLastError();
@@ -805,11 +991,9 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   // padded buffers: enough waves that each fills the unused rows of about
   // one expert
   const int fill_blocks = cap > 0 ? (E + kWaves - 1) / kWaves : 1;
-  // one tile: one block per 256-pair chunk places it
-  const int place_blocks = self_count ? (T * k + kThreads - 1) / kThreads : ntiles;
-  const int blocks = place_blocks > fill_blocks ? place_blocks : fill_blocks;
+  const int blocks = ntiles > fill_blocks ? ntiles : fill_blocks;
   hipLaunchKernelGGL(layout_place_kernel, dim3(blocks), dim3(kThreads), 0,
-                     stream, T, E, k, R, epr, epr_shift, cap, tt, ntiles, self_count, num_rows,
+                     stream, T, E, k, R, epr, epr_shift, cap, tt, ntiles, 0, num_rows,
                      idx, ws_hist, ws_rhist, ws_tot, ws_rtot, expert_counts, expert_offsets,
                      rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
   return hipGetLastError();

@@ -27,6 +27,7 @@ from oracle import moe_oracle as O  # noqa: E402
 from synth import workloads as W  # noqa: E402
 
 GUARD = 8  # guard rows after every row buffer
+LAYOUT_POISON = 0x7B7B7B7B   # no row, pair index or count takes this value
 
 
 def say(*a):
@@ -149,8 +150,10 @@ def gpu_layout(idx, E, R, cap, with_rtc=True):
     b.rank_counts = poison_like(R, torch.int32)
     b.rank_offsets = poison_like(R + 1, torch.int32)
     b.rank_token_counts = poison_like(R, torch.int32) if with_rtc else None
-    b.dst_row = poison_like((max(t, 1), k), torch.int32)
-    src_full = poison_like(rows + GUARD, torch.int32)
+    # dst_row and src_pair hold -1 for masked pairs and empty rows: poisoned
+    # with another value, so that an entry the layout fails to write shows
+    b.dst_row = torch.full((max(t, 1), k), LAYOUT_POISON, dtype=torch.int32, device="cuda")
+    src_full = torch.full((rows + GUARD,), LAYOUT_POISON, dtype=torch.int32, device="cuda")
     b.src_pair = src_full
     b.overflow = poison_like(1, torch.int32)
     b.workspace_bytes = M.moe_layout_workspace_bytes(t, E, k)
@@ -158,7 +161,7 @@ def gpu_layout(idx, E, R, cap, with_rtc=True):
     b.topk_idx = dev(idx) if t else None
     b.layout()
     src = host(src_full)
-    assert np.all(src[rows:] == -1), "stray write after src_pair"   # 0xFFFFFFFF == -1
+    assert np.all(src[rows:] == LAYOUT_POISON), "stray write after src_pair"
     out = dict(expert_counts=host(b.expert_counts), expert_offsets=host(b.expert_offsets),
                rank_counts=host(b.rank_counts), rank_offsets=host(b.rank_offsets),
                dst_row=host(b.dst_row)[:t], src_pair=src[:rows], overflow=host(b.overflow))
@@ -195,6 +198,14 @@ LAYOUT_CASES = [
     (70000, 64, 4, 8, 4300, False, 0.1),    # 274 tiles, capacity with drops
     (2100, 512, 32, 512, 0, True, 0.05),    # 66 tiles, 512 ranks
     (2100, 512, 32, 16, 5, True, 0.0),      # more fill blocks than tiles
+    # one tile, 1024-thread blocks: every wave holds one 64-pair chunk
+    (1024, 16, 1, 4, 0, True, 0.0),         # a full tile, k = 1
+    (512, 128, 2, 64, 0, True, 0.0),        # rank token counts per token (no bitmasks)
+    (100, 6, 4, 3, 0, False, 0.1),          # duplicates, masked slots
+    (200, 64, 5, 8, 3, False, 0.2),         # 1000 pairs, drops
+    (8, 512, 8, 64, 64, True, 0.0),         # 32 blocks mark unused rows
+    (7, 8, 3, 2, 0, True, 0.0),             # 21 pairs
+    (64, 512, 16, 1, 0, True, 0.0),         # one rank owns all 512 experts
 ]
 
 
@@ -237,7 +248,7 @@ def test_layout_ignores_out_of_range_ids():
         assert np.array_equal(val, want[name].reshape(val.shape)), name
 
 
-@pytest.mark.parametrize("t,k", [(900, 4), (33000, 8)], ids=["staged", "scanned"])
+@pytest.mark.parametrize("t,k", [(200, 4), (900, 4), (33000, 8)], ids=["one_tile", "staged", "scanned"])
 def test_layout_without_rank_token_counts(t, k):
     g = np.random.Generator(np.random.PCG64(5))
     idx = W.random_topk_idx(g, t, 32, k)

@@ -99,6 +99,15 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
         torch.cuda.synchronize()
         want_small.append(_small(ref))
     want_rows = _rows(ref)
+    # the serial form with separate layout and dispatch launches gives the same
+    alt = M.LayerBuffers.allocate(w.tokens, w.hidden, w.experts, w.top_k, w.ranks, w.capacity,
+                                  dtype=w.dispatch_dtype)
+    bench.serial_steps(w, [alt], inputs, y, 0, steps, fuse=False)
+    torch.cuda.synchronize()
+    for n, v in want_small[-1].items():
+        assert torch.equal(getattr(alt, n), v), ("unfused serial", n)
+    for n, v in _rows(alt).items():
+        assert torch.equal(v, want_rows[n]), ("unfused serial rows", n)
 
     side = torch.cuda.Stream()
     _poison(sets)
