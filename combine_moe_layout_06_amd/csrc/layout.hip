@@ -242,16 +242,17 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
   }
 }
 
-// self_count (the layout blocks of the fused layout + dispatch launch, whose
-// blocks have 256 threads): all pairs form one tile (T*k <= kTilePairs) and
-// no count pass ran. Every block loads all pairs and builds the histogram
-// itself (block 0 also the distinct-token counts), so the layout needs no
-// launch before it; the
-// pairs are then loaded chunk-major (chunk c of wave w = pairs
-// [(4c + w)*64, +64)), and block b places chunk b only, after the pairs of
-// the chunks before it, so up to four blocks share the placement.
-// ws_tot != nullptr: the scan pass has run, ws_hist holds the base of every
-// tile and ws_tot / ws_rtot the totals, so the block reads its own row only.
+// The 256-thread place pass, in two modes:
+//   - self_count (the layout blocks of the fused layout + dispatch launch):
+//     all pairs form one tile (T*k <= kTilePairs) and no count pass ran.
+//     Every block loads all pairs and builds the histogram itself (block 0
+//     also the distinct-token counts), so the layout needs no launch before
+//     it; the pairs are loaded chunk-major (chunk c of wave w = pairs
+//     [(4c + w)*64, +64)), and block b places chunk b only, after the pairs
+//     of the chunks before it, so up to four blocks share the placement.
+//   - otherwise the scan pass has run (many tiles): ws_hist holds the base of
+//     every tile and ws_tot / ws_rtot the totals, so the block reads its own
+//     row only.
 // Block `tile` of `nblocks` (the place kernel's blockIdx.x and gridDim.x, or
 // the layout blocks of the fused layout + dispatch launch).
 __device__ __forceinline__ void layout_place_body(
@@ -273,7 +274,7 @@ __device__ __forceinline__ void layout_place_body(
   __shared__ int s_base[kWaves][MOE_MAX_EXPERTS];
   __shared__ int s_wave[kWaves];
   __shared__ int s_overflow;
-  __shared__ int s_stage[kStage];
+  __shared__ int s_rank[kTilePairs];   // rank of each pair (self_count)
   __shared__ uint32_t s_rmask[kRankMaskWords];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -295,17 +296,10 @@ __device__ __forceinline__ void layout_place_body(
     const int p = pair_of(c);
     v[c] = p < np_load ? idx[base + p] : -1;
   }
-  const bool scanned = ws_tot != nullptr;
-  const int hist_n = self_count || scanned ? 0 : ntiles * E;
-  int h[kStage / kThreads];
-  stage_load(h, ws_hist, min(kStage, hist_n));
-  // block 0 also sums the per-tile distinct-token counts: its first chunk
-  // is loaded now, with everything else
+  const bool scanned = !self_count;
+  // block 0 also takes the distinct-token counts of each rank
   const bool sum_rtc = !self_count && tile == 0 && rank_token_counts != nullptr;
-  const int rn = sum_rtc && !scanned ? ntiles * R : 0;
-  int hr[kStage / kThreads];
-  stage_load(hr, ws_rhist, min(kStage, rn));
-  // after a scan pass: this tile's bases and the totals, also loaded now
+  // after the scan pass: this tile's bases and the totals, loaded now
   constexpr int kPerThread = MOE_MAX_EXPERTS / kThreads;
   int pre0[kPerThread], tot0[kPerThread], rtc0[kPerThread];
 #pragma unroll
@@ -350,7 +344,7 @@ __device__ __forceinline__ void layout_place_body(
           atomicOr(&s_rmask[rank_of(e, epr, epr_shift) * mask_words + (t >> 5)], 1u << (t & 31));
         }
       }
-      if (p < np_load) s_stage[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+      if (p < np_load) s_rank[p] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
       if (c != tile) v[c] = -1;   // this block places chunk `tile` only
     }
     __syncthreads();
@@ -362,7 +356,7 @@ __device__ __forceinline__ void layout_place_body(
       }
     } else if (tile == 0 && rank_token_counts != nullptr) {
       for (int tl = tid; tl < T; tl += kThreads) {
-        const int* r = s_stage + tl * k;
+        const int* r = s_rank + tl * k;
         if (R <= 64) {
           uint64_t seen = 0;
           for (int j = 0; j < k; ++j) {
@@ -398,27 +392,6 @@ __device__ __forceinline__ void layout_place_body(
     if (v[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][v[c]], __popcll(peers[c]));
   }
 
-  // per-expert totals and the base of this tile (sum over earlier tiles)
-  for (int c0 = 0; c0 < hist_n; c0 += kStage) {
-    const int n = min(kStage, hist_n - c0);
-    if (c0 > 0) stage_load(h, ws_hist + c0, n);
-    __syncthreads();   // the previous chunk has been consumed
-    stage_store(h, s_stage);
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) column_sums(s_stage, c0, n, E, e, tile, &s_tot[e], &s_pre[e]);
-  }
-  // block 0 also sums the per-tile distinct-token counts of each rank
-  if (sum_rtc) {
-    for (int c0 = 0; c0 < rn; c0 += kStage) {
-      const int n = min(kStage, rn - c0);
-      if (c0 > 0) stage_load(hr, ws_rhist + c0, n);
-      __syncthreads();
-      stage_store(hr, s_stage);
-      __syncthreads();
-      int unused = 0;
-      for (int r = tid; r < R; r += kThreads) column_sums(s_stage, c0, n, R, r, 0, &s_rtc[r], &unused);
-    }
-  }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) s_off[e] = cap > 0 ? 0 : s_tot[e];
   __syncthreads();
@@ -514,22 +487,35 @@ __global__ __launch_bounds__(kThreads) void layout_place_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// One tile (T*k <= 1024 pairs) in one launch of 1024-thread blocks. Wave w of
-// every block holds pairs [64w, 64w + 64), one per lane, so the per-wave
-// counts of all pairs take a single ballot round per expert-id bit and each
-// wave has one chunk to place: the chain of dependent steps is a quarter of
-// the 256-thread form's. Every block builds the same counts; block 0 writes
-// the counts and offsets and places the pairs, and every wave of the grid
-// marks the unused rows of about one expert (capacity mode) or the rows past
-// the last pair (packed mode).
+// Place pass in 1024-thread blocks, one per tile of at most 1024 pairs: wave w
+// holds pairs [64w, 64w + 64) of the tile, one per lane, so the wave's pairs
+// of one expert take a single ballot round per expert-id bit and each wave
+// has one chunk to place (a quarter of the dependent steps of the 256-thread
+// place pass).
+//   - SELF (all pairs form one tile and no count pass ran; ws_hist and
+//     ws_rhist are not read): every block counts the tile itself, from the per-wave
+//     counts; block 0 places it. The layout is then a single launch.
+//   - otherwise the count pass has written the per-tile histograms
+//     ([ntiles, E] in ws_hist, [ntiles, R] distinct-token counts in
+//     ws_rhist) and block b places tile b: every block adds all histogram
+//     rows (its totals) and the rows before its tile (its base), one LDS
+//     atomic per nonzero entry, with all loads in flight at once; block 0
+//     also adds the distinct-token counts. Used while ntiles * E fits
+//     kWideHistLoads loads per thread.
+// Block 0 writes the counts and offsets; every wave of the grid marks the
+// unused rows of about one expert (capacity mode) or the rows past the last
+// pair (packed mode).
 // ---------------------------------------------------------------------------
-constexpr int kOneThreads = 1024;
-constexpr int kOneWaves = kOneThreads / MOE_WAVE;
-static_assert(kOneThreads == kTilePairs, "one pair per thread");
+constexpr int kWideThreads = 1024;
+constexpr int kWideWaves = kWideThreads / MOE_WAVE;
+constexpr int kWideHistLoads = 16;   // histogram entries per thread (max)
+static_assert(kWideThreads == kTilePairs, "one pair per thread");
+// the wide place pass covers every histogram that needs no scan pass
+static_assert(kWideHistLoads * kWideThreads >= 2 * kStage, "histogram loads per thread");
 
-// Exclusive scan of s[0..n) in place (n <= kOneThreads) by a 1024-thread
+// Exclusive scan of s[0..n) in place (n <= kWideThreads) by a 1024-thread
 // block; returns the total to every thread.
-__device__ int block_exclusive_scan_one(int* s, int n, int* s_wave) {
+__device__ int block_exclusive_scan_wide(int* s, int n, int* s_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v = tid < n ? s[tid] : 0;
   int incl = v;
@@ -542,7 +528,7 @@ __device__ int block_exclusive_scan_one(int* s, int n, int* s_wave) {
   __syncthreads();
   int run = incl - v, total = 0;
 #pragma unroll
-  for (int w = 0; w < kOneWaves; ++w) {
+  for (int w = 0; w < kWideWaves; ++w) {
     const int x = s_wave[w];
     if (w < wave) run += x;
     total += x;
@@ -552,44 +538,82 @@ __device__ int block_exclusive_scan_one(int* s, int n, int* s_wave) {
   return total;
 }
 
-__global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
-    int T, int E, int k, int R, int epr, int epr_shift, int cap, int num_rows,
-    const int32_t* __restrict__ idx, int32_t* __restrict__ expert_counts,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ rank_counts,
-    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ rank_token_counts,
-    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_pair,
-    int32_t* __restrict__ overflow) {
-  __shared__ int s_cnt[kOneWaves][MOE_MAX_EXPERTS];
+// Row of flat index i of a row-major matrix with n columns (a shift when n
+// is a power of two).
+__device__ __forceinline__ int row_of(int i, int n, int shift) {
+  return shift >= 0 ? (i >> shift) : i / n;
+}
+
+template <bool SELF>
+__global__ __launch_bounds__(kWideThreads) void layout_wide_kernel(
+    int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
+    int num_rows, int e_shift, int r_shift, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ ws_hist, const int32_t* __restrict__ ws_rhist,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ rank_token_counts, int32_t* __restrict__ dst_row,
+    int32_t* __restrict__ src_pair, int32_t* __restrict__ overflow) {
+  __shared__ int s_cnt[kWideWaves][MOE_MAX_EXPERTS];
   __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_pre[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_rtc[MOE_MAX_EXPERTS];
   __shared__ int s_rank[kTilePairs];
   __shared__ uint32_t s_rmask[kRankMaskWords];
-  __shared__ int s_wave[kOneWaves];
+  __shared__ int s_wave[kWideWaves];
   __shared__ int s_overflow;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool lead = blockIdx.x == 0;
-  const int np = T * k;
-  const int raw = tid < np ? idx[tid] : -1;
-  if (tid < E)
-    for (int w = 0; w < kOneWaves; ++w) s_cnt[w][tid] = 0;
-  const int mask_words = (T + 31) / 32;
+  const int tile = blockIdx.x;
+  const bool lead = tile == 0;
+  constexpr bool self = SELF;
+  // the tile this block reads: all blocks read the only tile in self mode
+  const int mine = self ? 0 : tile;
+  const int np = mine < ntiles ? min(tt, T - mine * tt) * k : 0;
+  const size_t pair0 = (size_t)mine * tt * k;
+  const bool places = self ? lead : tile < ntiles;
+  const int raw = tid < np ? idx[pair0 + tid] : -1;
   const bool rtc = lead && rank_token_counts != nullptr;
-  const bool masks = rtc && R * mask_words <= kRankMaskWords;
+  // histogram rows (and block 0's distinct-token rows), all loads in flight
+  const int hist_n = self ? 0 : ntiles * E;
+  const int rhist_n = self || !rtc ? 0 : ntiles * R;
+  int h[kWideHistLoads], hr[kWideHistLoads];
+#pragma unroll
+  for (int j = 0; j < kWideHistLoads; ++j) {
+    const int i = j * kWideThreads + tid;
+    h[j] = i < hist_n ? ws_hist[i] : 0;
+    hr[j] = i < rhist_n ? ws_rhist[i] : 0;
+  }
+  if (tid < E) {
+    for (int w = 0; w < kWideWaves; ++w) s_cnt[w][tid] = 0;
+    s_tot[tid] = 0;
+    s_pre[tid] = 0;
+  }
+  const int mask_words = (T + 31) / 32;
+  const bool masks = self && rtc && R * mask_words <= kRankMaskWords;
   if (rtc && tid < R) s_rtc[tid] = 0;
   if (masks)
-    for (int i = tid; i < R * mask_words; i += kOneThreads) s_rmask[i] = 0u;
+    for (int i = tid; i < R * mask_words; i += kWideThreads) s_rmask[i] = 0u;
   if (tid == 0) s_overflow = 0;
   __syncthreads();
 
+#pragma unroll
+  for (int j = 0; j < kWideHistLoads; ++j) {
+    const int i = j * kWideThreads + tid;
+    if (h[j] != 0) {
+      const int row = row_of(i, E, e_shift), col = i - row * E;
+      atomicAdd(&s_tot[col], h[j]);
+      if (row < tile) atomicAdd(&s_pre[col], h[j]);
+    }
+    if (hr[j] != 0) atomicAdd(&s_rtc[i - row_of(i, R, r_shift) * R], hr[j]);
+  }
   // the wave's pairs of one expert (one ballot per expert-id bit); the
   // lowest of them stores their number
   const int e = clean_expert(raw, E);
   const uint64_t peers = peer_mask((uint32_t)e, e >= 0, ceil_log2(E));
   const int below = count_below(peers);
   if (e >= 0 && below == 0) s_cnt[wave][e] = __popcll(peers);
-  if (rtc) {
+  if (self && rtc) {
     const int r = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
     if (tid < np) s_rank[tid] = r;
     if (masks && r >= 0) {
@@ -600,19 +624,20 @@ __global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
   __syncthreads();
 
   // chain the waves: s_cnt[w][e] becomes the first position of wave w's
-  // pairs of expert e; totals and (capacity mode) fixed offsets
+  // pairs of expert e (after the tiles before); totals and (capacity mode)
+  // fixed offsets
   if (tid < E) {
-    int c[kOneWaves];
+    int c[kWideWaves];
 #pragma unroll
-    for (int w = 0; w < kOneWaves; ++w) c[w] = s_cnt[w][tid];
-    int run = 0;
+    for (int w = 0; w < kWideWaves; ++w) c[w] = s_cnt[w][tid];
+    int run = s_pre[tid];
 #pragma unroll
-    for (int w = 0; w < kOneWaves; ++w) {
+    for (int w = 0; w < kWideWaves; ++w) {
       s_cnt[w][tid] = run;
       run += c[w];
     }
-    s_tot[tid] = run;
-    s_off[tid] = cap > 0 ? tid * cap : run;
+    if (self) s_tot[tid] = run;
+    s_off[tid] = cap > 0 ? tid * cap : (self ? run : s_tot[tid]);
   }
   if (cap > 0 && tid == 0) s_off[E] = E * cap;
   if (masks) {
@@ -621,9 +646,9 @@ __global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
       for (int i = 0; i < mask_words; ++i) n += __popc(s_rmask[tid * mask_words + i]);
       s_rtc[tid] = n;
     }
-  } else if (rtc) {
+  } else if (self && rtc) {
     // one thread per token: a rank counts once, at its first slot
-    for (int t = tid; t < T; t += kOneThreads) {
+    for (int t = tid; t < T; t += kWideThreads) {
       const int* rk = s_rank + t * k;
       for (int j = 0; j < k; ++j) {
         const int x = rk[j];
@@ -635,7 +660,7 @@ __global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
   }
   __syncthreads();
   if (cap == 0) {
-    const int total = block_exclusive_scan_one(s_off, E, s_wave);
+    const int total = block_exclusive_scan_wide(s_off, E, s_wave);
     if (tid == 0) s_off[E] = total;
   }
   __syncthreads();
@@ -657,7 +682,10 @@ __global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
       expert_offsets[E] = s_off[E];
       rank_offsets[R] = s_off[E];
     }
-    // stable row: the pairs of e in the waves before, then lane order
+  }
+  if (places) {
+    // stable row: the pairs of e before the tile and in the waves before,
+    // then lane order
     int dst = -1;
     if (e >= 0) {
       const int pos = s_cnt[wave][e] + below;
@@ -665,13 +693,13 @@ __global__ __launch_bounds__(kOneThreads) void layout_one_tile_kernel(
       else if (pos < cap) dst = e * cap + pos;
     }
     if (tid < np) {
-      dst_row[tid] = dst;
-      if (dst >= 0 && dst < num_rows) src_pair[dst] = tid;
+      dst_row[pair0 + tid] = dst;
+      if (dst >= 0 && dst < num_rows) src_pair[dst] = (int32_t)(pair0 + tid);
     }
   }
 
   // rows that receive no pair are marked -1; all waves of the grid share it
-  const int gwave = blockIdx.x * kOneWaves + wave, nwaves = gridDim.x * kOneWaves;
+  const int gwave = blockIdx.x * kWideWaves + wave, nwaves = gridDim.x * kWideWaves;
   if (cap == 0) {
     for (int row = s_off[E] + gwave * MOE_WAVE + lane; row < num_rows; row += nwaves * MOE_WAVE)
       src_pair[row] = -1;
@@ -965,28 +993,37 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
   const bool scan = !self_count && layout_scans(ntiles, E);
   int32_t* ws_tot = scan ? ws_hist + (size_t)2 * ntiles * E : nullptr;
   int32_t* ws_rtot = scan && ws_rhist != nullptr ? ws_tot + E : nullptr;
-  if (self_count) {
-    // capacity mode: enough waves that each marks the unused rows of about
-    // one expert
-    const int blocks = cap > 0 ? (E + kOneWaves - 1) / kOneWaves : 1;
-    hipLaunchKernelGGL(layout_one_tile_kernel, dim3(blocks), dim3(kOneThreads), 0, stream, T, E,
-                       k, R, epr, epr_shift, cap, num_rows, idx, expert_counts, expert_offsets,
-                       rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
-    return hipGetLastError();
-  }
-  if (ntiles > 0) {
+  if (ntiles > 0 && !self_count) {
     hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
                        T, E, k, R, epr, epr_shift, tt, idx, ws_hist, ws_rhist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (scan) {
-      const int ga = (E + kScanCols - 1) / kScanCols;
-      const int gb = ws_rhist != nullptr ? (R + kScanCols - 1) / kScanCols : 0;
-      hipLaunchKernelGGL(layout_scan_kernel, dim3(ga + gb), dim3(kScanThreads), 0, stream,
-                         ntiles, E, ga, ws_hist, ws_tot, R, ws_rhist, ws_rtot);
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
-    }
+  }
+  if (!scan) {
+    // one block per tile; capacity mode: enough waves that each marks the
+    // unused rows of about one expert
+    const int fill = cap > 0 ? (E + kWideWaves - 1) / kWideWaves : 1;
+    const int blocks = ntiles > fill ? ntiles : fill;
+    const auto shift = [](int n) { return (n & (n - 1)) == 0 ? __builtin_ctz(n) : -1; };
+#define MOE_WIDE_ARGS T, E, k, R, epr, epr_shift, cap, tt, self_count ? 1 : ntiles, num_rows, \
+    shift(E), shift(R), idx, ws_hist, ws_rhist, expert_counts, expert_offsets, rank_counts, \
+    rank_offsets, rank_token_counts, dst_row, src_pair, overflow
+    if (self_count)
+      hipLaunchKernelGGL(layout_wide_kernel<true>, dim3(blocks), dim3(kWideThreads), 0, stream,
+                         MOE_WIDE_ARGS);
+    else
+      hipLaunchKernelGGL(layout_wide_kernel<false>, dim3(blocks), dim3(kWideThreads), 0, stream,
+                         MOE_WIDE_ARGS);
+#undef MOE_WIDE_ARGS
+    return hipGetLastError();
+  }
+  {
+    const int ga = (E + kScanCols - 1) / kScanCols;
+    const int gb = ws_rhist != nullptr ? (R + kScanCols - 1) / kScanCols : 0;
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(ga + gb), dim3(kScanThreads), 0, stream,
+                       ntiles, E, ga, ws_hist, ws_tot, R, ws_rhist, ws_rtot);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
   // padded buffers: enough waves that each fills the unused rows of about
   // one expert
