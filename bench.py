@@ -252,6 +252,26 @@ def hierarchical_front(w, sets, inputs, i, s):
     rb.rank_layout(lb.topk_idx)
 
 
+def _moe():
+    import combine_moe_layout_06_amd as M
+    return M
+
+
+def hierarchical_fronts(w, sets, inputs, pairs):
+    """hierarchical_front of steps (i, s) in `pairs`: their routes in one
+    launch and their expert layouts in one launch per pass (the batched
+    entry points), then each (token, rank) layout."""
+    M = _moe()
+    lbs = [sets[s][0] for _, s in pairs]
+    ds = [inputs[i % len(inputs)] for i, _ in pairs]
+    M.route_batches(lbs, [d["logits"] for d in ds], [d["bias"] for d in ds], w.score_fn,
+                    w.groups, w.topk_groups)
+    M.layout_batches(lbs)
+    for _, s in pairs:
+        lb, rb = sets[s]
+        rb.rank_layout(lb.topk_idx)
+
+
 def hierarchical_back(sets, inputs, y, i, s):
     """The rest of hierarchical step i: one copy per (token, rank), fan-out
     to the expert rows, per-(token, rank) partial sums of the expert outputs
@@ -311,8 +331,9 @@ def run_hierarchical(args, w, M, W, torch, np):
             back(i, 0)
 
     def piped(first, n):
-        pipelined(torch, lambda i, s: front(first + i, s), lambda i, s: back(first + i, s),
-                  nsets, n, side)
+        pipelined(torch, lambda pairs: hierarchical_fronts(w, sets, inputs,
+                                                           [(first + i, s) for i, s in pairs]),
+                  lambda i, s: back(first + i, s), nsets, n, side)
 
     side = torch.cuda.Stream() if overlap else None
 
@@ -527,9 +548,10 @@ def stamped_pipeline(torch, np, front, back, nsets, steps, side):
         if rc != 0:
             raise RuntimeError("bench_stamp failed: %d" % rc)
 
-    def f(i, s):
-        stamp(i)
-        front(i, s)
+    def f(pairs):
+        for i, _ in pairs:
+            stamp(i)
+        front(pairs)
 
     def b(i, s):
         back(i, s)
@@ -812,19 +834,20 @@ def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
 
 def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIPE_LEAD):
     """Steps pipelined on two streams, in the groups of pipeline_groups():
-    `side` runs front(i, s) (route and layout) for the steps of one group
-    while the current stream runs back(i, s) (dispatch and combine) for the
-    group before; then the current stream waits for the side stream once and
-    runs back() for the group. Step i uses the routing and layout buffers of
-    set s = i % nsets (nsets = 2 * group); the backs share one set of row
-    buffers, used one step after the other on the current stream. Two
-    consecutive groups hold at most nsets steps, so the steps that last used
-    the sets of group q are in group q - 2 or earlier: the fronts of group q
-    wait, once, until the backs of group q - 2 are done. One event per group
-    in each direction: each cross-stream edge costs the stream after it a few
-    microseconds. (Without the release waits, with buffers of its own for
-    every step, the side stream could run all fronts ahead; replayed, that
-    graph ran decode steps 22% slower and dsv3 steps no faster.)"""
+    `side` runs front(pairs) (route and layout of the group's steps, pairs =
+    [(i, s), ...]) while the current stream runs back(i, s) (dispatch and
+    combine) for the steps of the group before; then the current stream
+    waits for the side stream once and runs back() for the group. Step i
+    uses the routing and layout buffers of set s = i % nsets (nsets = 2 *
+    group); the backs share one set of row buffers, used one step after the
+    other on the current stream. Two consecutive groups hold at most nsets
+    steps, so the steps that last used the sets of group q are in group q - 2
+    or earlier: the fronts of group q wait, once, until the backs of group
+    q - 2 are done. One event per group in each direction: each cross-stream
+    edge costs the stream after it a few microseconds. (Without the release
+    waits, with buffers of its own for every step, the side stream could run
+    all fronts ahead; replayed, that graph ran decode steps 22% slower and
+    dsv3 steps no faster.)"""
     assert nsets == 2 * group
     main = torch.cuda.current_stream()   # the capturing stream inside a graph capture
     released = []
@@ -835,8 +858,7 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIP
     for q, grp in enumerate(pipeline_groups(steps, group, lead)):
         side.wait_event(released[q % 2])
         with torch.cuda.stream(side):
-            for i in grp:
-                front(i, i % nsets)
+            front([(i, i % nsets) for i in grp])
         ready = torch.cuda.Event()
         ready.record(side)
         main.wait_event(ready)
@@ -848,15 +870,22 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIP
 
 
 def step_halves(w, sets, inputs, y, first):
-    """front(i, s): route and layout of step i on buffer set s; back(i, s):
-    its dispatch and combine. Layout and dispatch are separate launches here
-    even where moe_layout_dispatch would fuse them (decode-sized capacity
-    mode): the layout is latency-bound, and on the side stream it is hidden."""
+    """front(pairs): route and layout of the steps (i, s) in `pairs`, step i
+    on buffer set s, as batches of one routing launch and one launch per
+    layout pass (moe_route_batched, moe_layout_batched: a group's fronts then
+    cost about one step's launches, which shortens the pipeline's fill and
+    leaves fewer launches beside the backs); back(i, s): dispatch and combine
+    of step i. Layout and dispatch are separate launches here even where
+    moe_layout_dispatch would fuse them (decode-sized capacity mode): the
+    layout is latency-bound, and on the side stream it is hidden."""
+    M = _moe()
 
-    def front(i, s):
-        d = inputs[(first + i) % len(inputs)]
-        sets[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-        sets[s].layout()
+    def front(pairs):
+        bufs = [sets[s] for _, s in pairs]
+        ds = [inputs[(first + i) % len(inputs)] for i, _ in pairs]
+        M.route_batches(bufs, [d["logits"] for d in ds], [d["bias"] for d in ds], w.score_fn,
+                        w.groups, w.topk_groups)
+        M.layout_batches(bufs)
 
     def back(i, s):
         d = inputs[(first + i) % len(inputs)]

@@ -33,6 +33,7 @@ MOE_MAX_TOPK = 32
 MOE_MAX_GROUPS = 64
 MOE_FP8_BLOCK = 128
 MOE_MX_BLOCK = 32
+MOE_MAX_BATCHES = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_layout.so")
 
@@ -41,7 +42,8 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
             "moe_dispatch_backward", "moe_combine_backward",
             "moe_rank_layout_workspace_bytes", "moe_rank_layout", "moe_expand",
             "moe_combine_local", "moe_combine_partials", "moe_layout_dispatch",
-            "moe_layout_dispatch_is_fused", "moe_layout_no_alloc")
+            "moe_layout_dispatch_is_fused", "moe_layout_no_alloc", "moe_route_batched",
+            "moe_layout_batched")
 
 _lib = None
 
@@ -99,6 +101,10 @@ def lib() -> ctypes.CDLL:
     L.moe_layout_no_alloc.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp]
     L.moe_layout_no_alloc.restype = i32
+    L.moe_route_batched.argtypes = [i32, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.moe_route_batched.restype = i32
+    L.moe_layout_batched.argtypes = [i32, vp, i32, i32, i32, i32, i32, vp]
+    L.moe_layout_batched.restype = i32
     _lib = L
     return L
 
@@ -195,6 +201,44 @@ def moe_layout_no_alloc(num_tokens, num_experts, top_k, num_ranks, capacity, top
                                      _ptr(overflow), _stream(stream)))
 
 
+class RouteIO(ctypes.Structure):
+    """moe_route_io: one batch of moe_route_batched."""
+    _fields_ = [("logits", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("topk_idx", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p)]
+
+
+class LayoutIO(ctypes.Structure):
+    """moe_layout_io: one batch of moe_layout_batched."""
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("rank_counts", ctypes.c_void_p),
+                ("rank_offsets", ctypes.c_void_p), ("rank_token_counts", ctypes.c_void_p),
+                ("dst_row", ctypes.c_void_p), ("src_pair", ctypes.c_void_p),
+                ("overflow", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+def moe_route_batched(num_tokens, num_experts, top_k, batches, score_fn, num_groups,
+                      topk_groups, stream=None) -> None:
+    """batches: sequence of (logits, bias or None, topk_idx, topk_weights)
+    device tensors."""
+    arr = (RouteIO * max(len(batches), 1))(
+        *[RouteIO(_ptr(lg), _ptr(bs), _ptr(ix), _ptr(wt)) for lg, bs, ix, wt in batches])
+    _check(lib().moe_route_batched(len(batches), ctypes.cast(arr, ctypes.c_void_p), num_tokens,
+                                   num_experts, top_k, score_fn, num_groups, topk_groups,
+                                   _stream(stream)))
+
+
+def moe_layout_batched(num_tokens, num_experts, top_k, num_ranks, capacity, batches,
+                       stream=None) -> None:
+    """batches: sequence of dicts with the keys of LayoutIO (device tensors;
+    workspace_bytes an int)."""
+    arr = (LayoutIO * max(len(batches), 1))(
+        *[LayoutIO(*[_ptr(b.get(f)) for f, _ in LayoutIO._fields_[:-1]],
+                   int(b["workspace_bytes"])) for b in batches])
+    _check(lib().moe_layout_batched(len(batches), ctypes.cast(arr, ctypes.c_void_p), num_tokens,
+                                    num_experts, top_k, num_ranks, capacity, _stream(stream)))
+
+
 def moe_layout_dispatch_is_fused(num_tokens, top_k, capacity) -> bool:
     return bool(lib().moe_layout_dispatch_is_fused(num_tokens, top_k, capacity))
 
@@ -277,4 +321,5 @@ def moe_combine_partials(num_tokens, hidden, top_k, num_rank_rows, partial_bf16,
                                       _stream(stream)))
 
 
-from .buffers import LayerBuffers, RankBuffers, run_layer  # noqa: E402,F401
+from .buffers import (LayerBuffers, RankBuffers, layout_batches, route_batches,  # noqa: E402,F401
+                      run_layer)

@@ -15,7 +15,8 @@ from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_FP8
                MOE_MX_BLOCK, moe_combine, moe_combine_local, moe_combine_partials,
                moe_dispatch, moe_expand, moe_layout, moe_layout_dispatch,
                moe_layout_workspace_bytes,
-               moe_rank_layout, moe_rank_layout_workspace_bytes, moe_route)
+               moe_layout_batched, moe_rank_layout, moe_rank_layout_workspace_bytes, moe_route,
+               moe_route_batched)
 
 
 @dataclasses.dataclass
@@ -223,6 +224,29 @@ class RankBuffers:
     def combine_partials(self, out, stream=None):
         moe_combine_partials(self.tokens, self.hidden, self.top_k, self.num_rank_rows,
                              self.partial, self.send_row, out, stream)
+
+
+def route_batches(bufs, logits, biases, score_fn, num_groups=1, topk_groups=1, stream=None):
+    """route() of every LayerBuffers in `bufs` (same sizes) on its own logits
+    and bias (entries may be None), in one launch (moe_route_batched)."""
+    b0 = bufs[0]
+    moe_route_batched(b0.tokens, b0.experts, b0.top_k,
+                      [(lg, bs, b.topk_idx, b.topk_weights)
+                       for b, lg, bs in zip(bufs, logits, biases)],
+                      score_fn, num_groups, topk_groups, stream)
+
+
+def layout_batches(bufs, stream=None):
+    """layout() of every LayerBuffers in `bufs` (same sizes), one launch per
+    pass for all of them (moe_layout_batched)."""
+    b0 = bufs[0]
+    moe_layout_batched(b0.tokens, b0.experts, b0.top_k, b0.ranks, b0.capacity,
+                       [dict(topk_idx=b.topk_idx, expert_counts=b.expert_counts,
+                             expert_offsets=b.expert_offsets, rank_counts=b.rank_counts,
+                             rank_offsets=b.rank_offsets, rank_token_counts=b.rank_token_counts,
+                             dst_row=b.dst_row, src_pair=b.src_pair, overflow=b.overflow,
+                             workspace=b.workspace, workspace_bytes=b.workspace_bytes)
+                        for b in bufs], stream)
 
 
 def run_layer(buf: LayerBuffers, logits, bias, x, score_fn, num_groups=1, topk_groups=1,

@@ -10,9 +10,23 @@
 
 namespace moe {
 
+// Several independent batches of the same sizes in one launch: the grid's
+// y dimension is the batch, and the per-batch pointers travel in the kernel
+// arguments.
+constexpr int kMaxBatches = MOE_MAX_BATCHES;
+
+struct RouteBatches {
+  const float* logits[kMaxBatches];
+  const float* bias[kMaxBatches];   // entries may be null
+  int32_t* idx[kMaxBatches];
+  float* w[kMaxBatches];
+};
+
 hipError_t launch_route(int T, int E, int k, const float* logits, const float* bias,
                         int sigmoid, int G, int kg, int32_t* idx_out, float* w_out,
                         hipStream_t stream);
+hipError_t launch_route_batches(int nb, const RouteBatches& rb, int T, int E, int k,
+                                int sigmoid, int G, int kg, hipStream_t stream);
 
 // Layout: pairs are cut into tiles of whole tokens; one block per tile.
 int layout_tile_tokens(int k);
@@ -25,6 +39,25 @@ hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx
                          int32_t* rank_token_counts, int32_t* dst_row,
                          int32_t* src_pair, int32_t* overflow, void* workspace,
                          hipStream_t stream);
+
+// Per-batch pointers of a batched layout (the arguments of launch_layout).
+struct LayoutBatch {
+  const int32_t* idx;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* rank_counts;
+  int32_t* rank_offsets;
+  int32_t* rank_token_counts;   // may be null
+  int32_t* dst_row;
+  int32_t* src_pair;
+  int32_t* overflow;
+  void* workspace;
+};
+struct LayoutBatches {
+  LayoutBatch b[kMaxBatches];
+};
+hipError_t launch_layout_batches(int nb, const LayoutBatches& lb, int T, int E, int k, int R,
+                                 int cap, hipStream_t stream);
 
 // Layout followed by dispatch; one launch when all pairs fit one tile in
 // capacity mode (layout_dispatch_fused), else the two launches above.

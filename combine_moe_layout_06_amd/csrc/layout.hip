@@ -61,10 +61,16 @@ __device__ __forceinline__ int rank_of(int e, int epr, int epr_shift) {
   return epr_shift >= 0 ? (e >> epr_shift) : e / epr;
 }
 
+// Batch blockIdx.y of `lb`; its workspace receives [ntiles, E] expert
+// counts, then (with rank_token_counts) [ntiles, R] distinct-token counts.
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(
-    int T, int E, int k, int R, int epr, int epr_shift, int tt,
-    const int32_t* __restrict__ idx, int32_t* __restrict__ ws_hist,
-    int32_t* __restrict__ ws_rhist) {
+    int T, int E, int k, int R, int epr, int epr_shift, int tt, int ntiles,
+    const LayoutBatches lb) {
+  const LayoutBatch& bt = lb.b[blockIdx.y];
+  const int32_t* __restrict__ idx = bt.idx;
+  int32_t* __restrict__ ws_hist = static_cast<int32_t*>(bt.workspace);
+  int32_t* __restrict__ ws_rhist =
+      bt.rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
   __shared__ int s_hist[MOE_MAX_EXPERTS];
   __shared__ int s_rhist[MOE_MAX_EXPERTS];
   __shared__ int s_rank[kTilePairs];     // rank of each pair, -1 if masked
@@ -544,15 +550,24 @@ __device__ __forceinline__ int row_of(int i, int n, int shift) {
   return shift >= 0 ? (i >> shift) : i / n;
 }
 
+// Batch blockIdx.y of `lb` (its workspace as layout_count_kernel wrote it).
 template <bool SELF>
 __global__ __launch_bounds__(kWideThreads) void layout_wide_kernel(
     int T, int E, int k, int R, int epr, int epr_shift, int cap, int tt, int ntiles,
-    int num_rows, int e_shift, int r_shift, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ ws_hist, const int32_t* __restrict__ ws_rhist,
-    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ rank_token_counts, int32_t* __restrict__ dst_row,
-    int32_t* __restrict__ src_pair, int32_t* __restrict__ overflow) {
+    int num_rows, int e_shift, int r_shift, const LayoutBatches lb) {
+  const LayoutBatch& bt = lb.b[blockIdx.y];
+  const int32_t* __restrict__ idx = bt.idx;
+  const int32_t* __restrict__ ws_hist = static_cast<const int32_t*>(bt.workspace);
+  const int32_t* __restrict__ ws_rhist =
+      bt.rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
+  int32_t* __restrict__ expert_counts = bt.expert_counts;
+  int32_t* __restrict__ expert_offsets = bt.expert_offsets;
+  int32_t* __restrict__ rank_counts = bt.rank_counts;
+  int32_t* __restrict__ rank_offsets = bt.rank_offsets;
+  int32_t* __restrict__ rank_token_counts = bt.rank_token_counts;
+  int32_t* __restrict__ dst_row = bt.dst_row;
+  int32_t* __restrict__ src_pair = bt.src_pair;
+  int32_t* __restrict__ overflow = bt.overflow;
   __shared__ int s_cnt[kWideWaves][MOE_MAX_EXPERTS];
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
@@ -976,64 +991,89 @@ size_t layout_workspace_bytes(int T, int E, int k) {
   return (tiles + (layout_scans((int)tiles, E) ? 1 : 0)) * (size_t)(2 * E) * sizeof(int32_t);
 }
 
-hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx,
-                         int32_t* expert_counts, int32_t* expert_offsets,
-                         int32_t* rank_counts, int32_t* rank_offsets,
-                         int32_t* rank_token_counts, int32_t* dst_row,
-                         int32_t* src_pair, int32_t* overflow, void* workspace,
-                         hipStream_t stream) {
+// Many tiles: count, scan and place passes for one batch.
+static hipError_t launch_layout_scanned(int T, int E, int k, int R, int cap,
+                                        const LayoutBatch& bt, hipStream_t stream) {
   const int tt = layout_tile_tokens(k);
   const int ntiles = layout_num_tiles(T, k);
   const int epr = E / R;
-  const int num_rows = cap > 0 ? E * cap : T * k;
-  int32_t* ws_hist = static_cast<int32_t*>(workspace);
-  int32_t* ws_rhist = rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
-  const bool self_count = T * k <= kTilePairs;
-  const bool scan = !self_count && layout_scans(ntiles, E);
-  int32_t* ws_tot = scan ? ws_hist + (size_t)2 * ntiles * E : nullptr;
-  int32_t* ws_rtot = scan && ws_rhist != nullptr ? ws_tot + E : nullptr;
-  if (ntiles > 0 && !self_count) {
-    hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
-                       T, E, k, R, epr, epr_shift, tt, idx, ws_hist, ws_rhist);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  if (!scan) {
-    // one block per tile; capacity mode: enough waves that each marks the
-    // unused rows of about one expert
-    const int fill = cap > 0 ? (E + kWideWaves - 1) / kWideWaves : 1;
-    const int blocks = ntiles > fill ? ntiles : fill;
-    const auto shift = [](int n) { return (n & (n - 1)) == 0 ? __builtin_ctz(n) : -1; };
-#define MOE_WIDE_ARGS T, E, k, R, epr, epr_shift, cap, tt, self_count ? 1 : ntiles, num_rows, \
-    shift(E), shift(R), idx, ws_hist, ws_rhist, expert_counts, expert_offsets, rank_counts, \
-    rank_offsets, rank_token_counts, dst_row, src_pair, overflow
-    if (self_count)
-      hipLaunchKernelGGL(layout_wide_kernel<true>, dim3(blocks), dim3(kWideThreads), 0, stream,
-                         MOE_WIDE_ARGS);
-    else
-      hipLaunchKernelGGL(layout_wide_kernel<false>, dim3(blocks), dim3(kWideThreads), 0, stream,
-                         MOE_WIDE_ARGS);
-#undef MOE_WIDE_ARGS
-    return hipGetLastError();
-  }
-  {
-    const int ga = (E + kScanCols - 1) / kScanCols;
-    const int gb = ws_rhist != nullptr ? (R + kScanCols - 1) / kScanCols : 0;
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(ga + gb), dim3(kScanThreads), 0, stream,
-                       ntiles, E, ga, ws_hist, ws_tot, R, ws_rhist, ws_rtot);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
+  const int num_rows = cap > 0 ? E * cap : T * k;
+  int32_t* ws_hist = static_cast<int32_t*>(bt.workspace);
+  int32_t* ws_rhist = bt.rank_token_counts != nullptr ? ws_hist + (size_t)ntiles * E : nullptr;
+  int32_t* ws_tot = ws_hist + (size_t)2 * ntiles * E;
+  int32_t* ws_rtot = ws_rhist != nullptr ? ws_tot + E : nullptr;
+  LayoutBatches one{};
+  one.b[0] = bt;
+  hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
+                     T, E, k, R, epr, epr_shift, tt, ntiles, one);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int ga = (E + kScanCols - 1) / kScanCols;
+  const int gb = ws_rhist != nullptr ? (R + kScanCols - 1) / kScanCols : 0;
+  hipLaunchKernelGGL(layout_scan_kernel, dim3(ga + gb), dim3(kScanThreads), 0, stream,
+                     ntiles, E, ga, ws_hist, ws_tot, R, ws_rhist, ws_rtot);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   // padded buffers: enough waves that each fills the unused rows of about
   // one expert
   const int fill_blocks = cap > 0 ? (E + kWaves - 1) / kWaves : 1;
   const int blocks = ntiles > fill_blocks ? ntiles : fill_blocks;
   hipLaunchKernelGGL(layout_place_kernel, dim3(blocks), dim3(kThreads), 0,
                      stream, T, E, k, R, epr, epr_shift, cap, tt, ntiles, 0, num_rows,
-                     idx, ws_hist, ws_rhist, ws_tot, ws_rtot, expert_counts, expert_offsets,
-                     rank_counts, rank_offsets, rank_token_counts, dst_row, src_pair, overflow);
+                     bt.idx, ws_hist, ws_rhist, ws_tot, ws_rtot, bt.expert_counts,
+                     bt.expert_offsets, bt.rank_counts, bt.rank_offsets, bt.rank_token_counts,
+                     bt.dst_row, bt.src_pair, bt.overflow);
   return hipGetLastError();
+}
+
+hipError_t launch_layout_batches(int nb, const LayoutBatches& lb, int T, int E, int k, int R,
+                                 int cap, hipStream_t stream) {
+  const int tt = layout_tile_tokens(k);
+  const int ntiles = layout_num_tiles(T, k);
+  const int epr = E / R;
+  const int num_rows = cap > 0 ? E * cap : T * k;
+  const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
+  const bool self_count = T * k <= kTilePairs;
+  if (!self_count && layout_scans(ntiles, E)) {
+    for (int b = 0; b < nb; ++b) {
+      const hipError_t err = launch_layout_scanned(T, E, k, R, cap, lb.b[b], stream);
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+  }
+  if (nb == 0) return hipSuccess;
+  if (!self_count) {
+    hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles, nb), dim3(kThreads), 0, stream,
+                       T, E, k, R, epr, epr_shift, tt, ntiles, lb);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // one block per tile; capacity mode: enough waves that each marks the
+  // unused rows of about one expert
+  const int fill = cap > 0 ? (E + kWideWaves - 1) / kWideWaves : 1;
+  const int blocks = ntiles > fill ? ntiles : fill;
+  const auto shift = [](int n) { return (n & (n - 1)) == 0 ? __builtin_ctz(n) : -1; };
+  const dim3 grid(blocks, nb);
+  if (self_count)
+    hipLaunchKernelGGL(layout_wide_kernel<true>, grid, dim3(kWideThreads), 0, stream, T, E, k,
+                       R, epr, epr_shift, cap, tt, 1, num_rows, shift(E), shift(R), lb);
+  else
+    hipLaunchKernelGGL(layout_wide_kernel<false>, grid, dim3(kWideThreads), 0, stream, T, E, k,
+                       R, epr, epr_shift, cap, tt, ntiles, num_rows, shift(E), shift(R), lb);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout(int T, int E, int k, int R, int cap, const int32_t* idx,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* rank_counts, int32_t* rank_offsets,
+                         int32_t* rank_token_counts, int32_t* dst_row,
+                         int32_t* src_pair, int32_t* overflow, void* workspace,
+                         hipStream_t stream) {
+  LayoutBatches lb{};
+  lb.b[0] = LayoutBatch{idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        rank_token_counts, dst_row, src_pair, overflow, workspace};
+  return launch_layout_batches(1, lb, T, E, k, R, cap, stream);
 }
 
 

@@ -69,6 +69,29 @@ int check_rows(const char* fn, int T, int H, int k, int num_rows) {
   return MOE_OK;
 }
 
+int check_route(const char* fn, int num_tokens, int num_experts, int top_k, const float* logits,
+                const float* bias, int score_fn, int num_groups, int topk_groups,
+                const int32_t* topk_idx, const float* topk_weights) {
+  int st = check_topk(fn, num_tokens, num_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID, "%s: score_fn=%d", fn, score_fn);
+  if (num_groups < 1 || num_groups > MOE_MAX_GROUPS || num_experts % num_groups != 0)
+    return fail(MOE_ERR_INVALID, "%s: num_groups=%d must divide num_experts=%d and be <= %d", fn,
+                num_groups, num_experts, MOE_MAX_GROUPS);
+  if (score_fn == MOE_SCORE_SOFTMAX && num_groups != 1)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: softmax routing takes no groups", fn);
+  if (topk_groups < 1 || topk_groups > num_groups)
+    return fail(MOE_ERR_INVALID, "%s: topk_groups=%d not in [1, %d]", fn, topk_groups, num_groups);
+  if ((long long)topk_groups * (num_experts / num_groups) < top_k)
+    return fail(MOE_ERR_INVALID, "%s: the kept groups hold fewer than top_k experts", fn);
+  if (num_tokens > 0 && (!logits || !topk_idx || !topk_weights))
+    return fail(MOE_ERR_INVALID, "%s: NULL logits/topk_idx/topk_weights", fn);
+  if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
+    return fail(MOE_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,26 +113,36 @@ int moe_route(int num_tokens, int num_experts, int top_k, const float* logits,
               const float* bias, int score_fn, int num_groups, int topk_groups,
               int32_t* topk_idx, float* topk_weights, void* stream) {
   const char* fn = "moe_route";
-  int st = check_topk(fn, num_tokens, num_experts, top_k);
+  const int st = check_route(fn, num_tokens, num_experts, top_k, logits, bias, score_fn,
+                             num_groups, topk_groups, topk_idx, topk_weights);
   if (st != MOE_OK) return st;
-  if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID)
-    return fail(MOE_ERR_INVALID, "%s: score_fn=%d", fn, score_fn);
-  if (num_groups < 1 || num_groups > MOE_MAX_GROUPS || num_experts % num_groups != 0)
-    return fail(MOE_ERR_INVALID, "%s: num_groups=%d must divide num_experts=%d and be <= %d", fn,
-                num_groups, num_experts, MOE_MAX_GROUPS);
-  if (score_fn == MOE_SCORE_SOFTMAX && num_groups != 1)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: softmax routing takes no groups", fn);
-  if (topk_groups < 1 || topk_groups > num_groups)
-    return fail(MOE_ERR_INVALID, "%s: topk_groups=%d not in [1, %d]", fn, topk_groups, num_groups);
-  if ((long long)topk_groups * (num_experts / num_groups) < top_k)
-    return fail(MOE_ERR_INVALID, "%s: the kept groups hold fewer than top_k experts", fn);
-  if (num_tokens > 0 && (!logits || !topk_idx || !topk_weights))
-    return fail(MOE_ERR_INVALID, "%s: NULL logits/topk_idx/topk_weights", fn);
-  if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
-    return fail(MOE_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
   return from_hip(moe::launch_route(num_tokens, num_experts, top_k, logits, bias,
                                     score_fn == MOE_SCORE_SIGMOID, num_groups, topk_groups,
                                     topk_idx, topk_weights, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_route_batched(int num_batches, const moe_route_io* batches, int num_tokens,
+                      int num_experts, int top_k, int score_fn, int num_groups,
+                      int topk_groups, void* stream) {
+  const char* fn = "moe_route_batched";
+  if (num_batches < 1 || num_batches > MOE_MAX_BATCHES || !batches)
+    return fail(MOE_ERR_INVALID, "%s: num_batches=%d not in [1, %d] (or NULL batches)", fn,
+                num_batches, MOE_MAX_BATCHES);
+  moe::RouteBatches rb{};
+  for (int b = 0; b < num_batches; ++b) {
+    const int st = check_route(fn, num_tokens, num_experts, top_k, batches[b].logits,
+                               batches[b].bias, score_fn, num_groups, topk_groups,
+                               batches[b].topk_idx, batches[b].topk_weights);
+    if (st != MOE_OK) return st;
+    rb.logits[b] = batches[b].logits;
+    rb.bias[b] = batches[b].bias;
+    rb.idx[b] = batches[b].topk_idx;
+    rb.w[b] = batches[b].topk_weights;
+  }
+  return from_hip(moe::launch_route_batches(num_batches, rb, num_tokens, num_experts, top_k,
+                                            score_fn == MOE_SCORE_SIGMOID, num_groups,
+                                            topk_groups, static_cast<hipStream_t>(stream)),
                   fn);
 }
 
@@ -202,6 +235,34 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks, int ca
                                      topk_idx, expert_counts, expert_offsets, rank_counts,
                                      rank_offsets, rank_token_counts, dst_row, src_pair,
                                      overflow, workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_layout_batched(int num_batches, const moe_layout_io* batches, int num_tokens,
+                       int num_experts, int top_k, int num_ranks, int capacity, void* stream) {
+  const char* fn = "moe_layout_batched";
+  if (num_batches < 1 || num_batches > MOE_MAX_BATCHES || !batches)
+    return fail(MOE_ERR_INVALID, "%s: num_batches=%d not in [1, %d] (or NULL batches)", fn,
+                num_batches, MOE_MAX_BATCHES);
+  moe::LayoutBatches lb{};
+  for (int b = 0; b < num_batches; ++b) {
+    const moe_layout_io& io = batches[b];
+    const int st = check_layout(fn, num_tokens, num_experts, top_k, num_ranks, capacity,
+                                io.topk_idx, io.expert_counts, io.expert_offsets,
+                                io.rank_counts, io.rank_offsets, io.rank_token_counts,
+                                io.dst_row, io.src_pair, io.overflow, io.workspace,
+                                io.workspace_bytes);
+    if (st != MOE_OK) return st;
+    if ((io.rank_token_counts == nullptr) != (batches[0].rank_token_counts == nullptr))
+      return fail(MOE_ERR_INVALID, "%s: rank_token_counts must be given for all batches or none",
+                  fn);
+    lb.b[b] = moe::LayoutBatch{io.topk_idx, io.expert_counts, io.expert_offsets, io.rank_counts,
+                               io.rank_offsets, io.rank_token_counts, io.dst_row, io.src_pair,
+                               io.overflow, io.workspace};
+  }
+  return from_hip(moe::launch_layout_batches(num_batches, lb, num_tokens, num_experts, top_k,
+                                             num_ranks, capacity,
+                                             static_cast<hipStream_t>(stream)),
                   fn);
 }
 

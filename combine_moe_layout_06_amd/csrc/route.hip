@@ -150,12 +150,15 @@ __device__ __forceinline__ void load_slots(float (&v)[VPL], const float* __restr
 // One wave per token; lane l holds the VPL consecutive experts
 // [l*VPL, l*VPL + VPL), so a group of gs experts spans gs/VPL neighbouring
 // lanes and, among equal keys, a lower lane always holds the lower expert.
+// Batch blockIdx.y of `rb`.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(
-    int T, int E, int k, const float* __restrict__ logits,
-    const float* __restrict__ bias, int sigmoid, int G, int kg, int vec,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+    int T, int E, int k, const RouteBatches rb, int sigmoid, int G, int kg, int vec) {
   __shared__ float s_key[kRouteWaves][MOE_MAX_EXPERTS];
+  const float* __restrict__ logits = rb.logits[blockIdx.y];
+  const float* __restrict__ bias = rb.bias[blockIdx.y];
+  int32_t* __restrict__ idx_out = rb.idx[blockIdx.y];
+  float* __restrict__ w_out = rb.w[blockIdx.y];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -354,9 +357,11 @@ __device__ __forceinline__ double team_sum_f64(double v) {
 // SPG: slots per expert group (a group is SPG*L experts), 0 = no groups.
 template <int L, int VPL, int SPG>
 __global__ __launch_bounds__(256) void route_team_kernel(
-    int T, int E, int k, const float* __restrict__ logits,
-    const float* __restrict__ bias, int sigmoid, int G, int kg,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+    int T, int E, int k, const RouteBatches rb, int sigmoid, int G, int kg) {
+  const float* __restrict__ logits = rb.logits[blockIdx.y];
+  const float* __restrict__ bias = rb.bias[blockIdx.y];
+  int32_t* __restrict__ idx_out = rb.idx[blockIdx.y];
+  float* __restrict__ w_out = rb.w[blockIdx.y];
   constexpr int kTeams = MOE_WAVE / L;
   const int lane = threadIdx.x & 63;
   const int tl = lane % L;
@@ -434,35 +439,41 @@ __global__ __launch_bounds__(256) void route_team_kernel(
   }
 }
 
+// Arguments of one routing launch over nb batches.
+struct RouteLaunch {
+  int nb, T, E, k;
+  const RouteBatches* rb;
+  int sigmoid, G, kg;
+  hipStream_t stream;
+};
+
 template <int L, int VPL, int SPG>
-void launch_team_spg(int T, int E, int k, const float* logits, const float* bias, int sigmoid,
-                     int G, int kg, int32_t* idx_out, float* w_out, hipStream_t stream) {
+void launch_team_spg(const RouteLaunch& a) {
   constexpr int per_block = kRouteWaves * (MOE_WAVE / L);
-  hipLaunchKernelGGL((route_team_kernel<L, VPL, SPG>), dim3((T + per_block - 1) / per_block),
-                     dim3(256), 0, stream, T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out);
+  hipLaunchKernelGGL((route_team_kernel<L, VPL, SPG>), dim3((a.T + per_block - 1) / per_block, a.nb),
+                     dim3(256), 0, a.stream, a.T, a.E, a.k, *a.rb, a.sigmoid, a.G, a.kg);
 }
 
 // Returns false when no instance covers the group size.
 template <int L, int VPL>
-bool launch_team(int T, int E, int k, const float* logits, const float* bias, int sigmoid,
-                 int G, int kg, int32_t* idx_out, float* w_out, hipStream_t stream) {
-  const int spg = G > 1 ? E / G / L : 0;
+bool launch_team(const RouteLaunch& a) {
+  const int spg = a.G > 1 ? a.E / a.G / L : 0;
   switch (spg) {
-    case 0: launch_team_spg<L, VPL, 0>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream); return true;
-    case 1: launch_team_spg<L, VPL, 1>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream); return true;
-    case 2: if (VPL >= 2) { launch_team_spg<L, VPL, (VPL >= 2 ? 2 : 1)>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream); return true; } return false;
-    case 4: if (VPL >= 4) { launch_team_spg<L, VPL, (VPL >= 4 ? 4 : 1)>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream); return true; } return false;
-    case 8: if (VPL >= 8) { launch_team_spg<L, VPL, (VPL >= 8 ? 8 : 1)>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream); return true; } return false;
+    case 0: launch_team_spg<L, VPL, 0>(a); return true;
+    case 1: launch_team_spg<L, VPL, 1>(a); return true;
+    case 2: if (VPL >= 2) { launch_team_spg<L, VPL, (VPL >= 2 ? 2 : 1)>(a); return true; } return false;
+    case 4: if (VPL >= 4) { launch_team_spg<L, VPL, (VPL >= 4 ? 4 : 1)>(a); return true; } return false;
+    case 8: if (VPL >= 8) { launch_team_spg<L, VPL, (VPL >= 8 ? 8 : 1)>(a); return true; } return false;
     default: return false;
   }
 }
 
 }  // namespace
 
-hipError_t launch_route(int T, int E, int k, const float* logits, const float* bias,
-                        int sigmoid, int G, int kg, int32_t* idx_out, float* w_out,
-                        hipStream_t stream) {
-  if (T == 0) return hipSuccess;
+hipError_t launch_route_batches(int nb, const RouteBatches& rb, int T, int E, int k,
+                                int sigmoid, int G, int kg, hipStream_t stream) {
+  if (T == 0 || nb == 0) return hipSuccess;
+  const RouteLaunch a{nb, T, E, k, &rb, sigmoid, G, kg, stream};
   // Team kernels (8 lanes per token up to 64 experts, 16 up to 128) cut the
   // reduction cost per token; with more experts one wave per token is
   // faster, because the longer per-lane fp64 sigmoid chains of a team then
@@ -471,27 +482,41 @@ hipError_t launch_route(int T, int E, int k, const float* logits, const float* b
   const bool team = E <= 128 && k <= L && (G == 1 || (E / G) % L == 0);
   if (team) {
     bool done;
-    if (E <= 8) done = launch_team<8, 1>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream);
-    else if (E <= 16) done = launch_team<8, 2>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream);
-    else if (E <= 32) done = launch_team<8, 4>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream);
-    else if (E <= 64) done = launch_team<8, 8>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream);
-    else done = launch_team<16, 8>(T, E, k, logits, bias, sigmoid, G, kg, idx_out, w_out, stream);
+    if (E <= 8) done = launch_team<8, 1>(a);
+    else if (E <= 16) done = launch_team<8, 2>(a);
+    else if (E <= 32) done = launch_team<8, 4>(a);
+    else if (E <= 64) done = launch_team<8, 8>(a);
+    else done = launch_team<16, 8>(a);
     if (done) return hipGetLastError();
   }
-  const dim3 grid((T + kRouteWaves - 1) / kRouteWaves), block(256);
+  const dim3 grid((T + kRouteWaves - 1) / kRouteWaves, nb), block(256);
   const int vpl = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8;
   // 16-byte loads of a lane's slots: rows of whole 16-byte units, aligned
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  const int vec = vpl >= 4 && E % vpl == 0 && a16(logits) && (bias == nullptr || a16(bias));
+  bool aligned = true;
+  for (int b = 0; b < nb; ++b)
+    aligned = aligned && a16(rb.logits[b]) && (rb.bias[b] == nullptr || a16(rb.bias[b]));
+  const int vec = vpl >= 4 && E % vpl == 0 && aligned;
   if (vpl == 1)
-    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
+    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, stream, T, E, k, rb, sigmoid, G, kg, vec);
   else if (vpl == 2)
-    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
+    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, stream, T, E, k, rb, sigmoid, G, kg, vec);
   else if (vpl == 4)
-    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
+    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, stream, T, E, k, rb, sigmoid, G, kg, vec);
   else
-    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, T, E, k, logits, bias, sigmoid, G, kg, vec, idx_out, w_out);
+    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, stream, T, E, k, rb, sigmoid, G, kg, vec);
   return hipGetLastError();
+}
+
+hipError_t launch_route(int T, int E, int k, const float* logits, const float* bias,
+                        int sigmoid, int G, int kg, int32_t* idx_out, float* w_out,
+                        hipStream_t stream) {
+  RouteBatches rb{};
+  rb.logits[0] = logits;
+  rb.bias[0] = bias;
+  rb.idx[0] = idx_out;
+  rb.w[0] = w_out;
+  return launch_route_batches(1, rb, T, E, k, sigmoid, G, kg, stream);
 }
 
 }  // namespace moe

@@ -64,6 +64,7 @@ enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3 = 1, MOE_DTYPE_MXFP8_E4M3 = 2 };
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_GROUPS 64
+#define MOE_MAX_BATCHES 8
 #define MOE_FP8_BLOCK 128
 #define MOE_MX_BLOCK 32
 
@@ -107,6 +108,34 @@ int moe_route(int num_tokens, int num_experts, int top_k,
               const float* logits, const float* bias,
               int score_fn, int num_groups, int topk_groups,
               int32_t* topk_idx, float* topk_weights, void* stream);
+
+/*
+ * moe_route_batched -- moe_route on num_batches independent batches of the
+ * same sizes (each batch has its own logits, bias and outputs; the routing
+ * settings are shared), in one launch instead of num_batches: the
+ * batches are, for example, the micro-batches or consecutive steps whose
+ * routing a caller prepares ahead of their dispatch. Each batch's results
+ * equal those of moe_route on it alone (same definition: hyper.ai story on
+ * Hybrid-EP for top-k routing, DeepEP article "Group-limited gating
+ * algorithm" for the groups).
+ *
+ *   batches   HOST array of num_batches moe_route_io, read during the call
+ *             only; 1 <= num_batches <= MOE_MAX_BATCHES
+ * Every batch is validated as moe_route validates its arguments before
+ * anything is enqueued. No output of one batch may overlap another batch's
+ * inputs or outputs.
+ */
+typedef struct {
+  const float* logits;   /* [num_tokens, num_experts] fp32 */
+  const float* bias;     /* [num_experts] fp32 or NULL */
+  int32_t* topk_idx;     /* [num_tokens, top_k] int32 output */
+  float* topk_weights;   /* [num_tokens, top_k] fp32 output */
+} moe_route_io;
+
+int moe_route_batched(int num_batches, const moe_route_io* batches,
+                      int num_tokens, int num_experts, int top_k,
+                      int score_fn, int num_groups, int topk_groups,
+                      void* stream);
 
 /* Bytes of device workspace moe_layout needs for these sizes. */
 size_t moe_layout_workspace_bytes(int num_tokens, int num_experts, int top_k);
@@ -156,6 +185,39 @@ int moe_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
                int32_t* rank_token_counts, int32_t* dst_row,
                int32_t* src_pair, int32_t* overflow,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_layout_batched -- moe_layout on num_batches independent batches of
+ * the same sizes (each with its own routing, outputs and workspace), with
+ * one launch per pass for all of them instead of one per batch and pass.
+ * Each batch's results equal those of moe_layout on it alone (same
+ * definitions: glossary "Expert Parallelism", "Le principe de base" and
+ * "Megatron-LM (NVIDIA)"). Sizes that need the scan pass (many tiles) run
+ * the batches one after the other.
+ *
+ *   batches   HOST array of num_batches moe_layout_io, read during the call
+ *             only; 1 <= num_batches <= MOE_MAX_BATCHES; rank_token_counts
+ *             must be given for every batch or for none
+ * Every batch is validated as moe_layout validates its arguments before
+ * anything is enqueued. Batches must not share outputs or workspaces.
+ */
+typedef struct {
+  const int32_t* topk_idx;      /* the arrays of moe_layout, per batch */
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* rank_counts;
+  int32_t* rank_offsets;
+  int32_t* rank_token_counts;   /* may be NULL */
+  int32_t* dst_row;
+  int32_t* src_pair;
+  int32_t* overflow;
+  void* workspace;
+  size_t workspace_bytes;
+} moe_layout_io;
+
+int moe_layout_batched(int num_batches, const moe_layout_io* batches,
+                       int num_tokens, int num_experts, int top_k,
+                       int num_ranks, int capacity, void* stream);
 
 /*
  * moe_layout_no_alloc -- moe_layout without a workspace argument, for

@@ -382,3 +382,51 @@ def test_layout_dispatch_rejects(kw, status):
                                        a["src"], a["ov"], a["ws"], a["wsb"], a["H"], a["x"],
                                        a["dt"], a["out"], a["sc"], None) == status
     assert M.moe_last_error().startswith("moe_layout_dispatch")
+
+
+def test_batched_calls_reject():
+    """Batch counts outside [1, MOE_MAX_BATCHES], a NULL batch array, a bad
+    pointer in any batch, and rank token counts given for some batches only:
+    all refused before anything is enqueued."""
+    _no_gpu()
+    L = M.lib()
+    ok = M.RouteIO(A16, None, A16b, A16b + 4096)
+    arr = (M.RouteIO * 3)(ok, ok, ok)
+    args = (16, 64, 4, 0, 1, 1, None)
+    assert L.moe_route_batched(0, ctypes.cast(arr, ctypes.c_void_p), *args) == M.MOE_ERR_INVALID
+    assert L.moe_route_batched(M.MOE_MAX_BATCHES + 1, ctypes.cast(arr, ctypes.c_void_p),
+                               *args) == M.MOE_ERR_INVALID
+    assert L.moe_route_batched(2, None, *args) == M.MOE_ERR_INVALID
+    arr[2] = M.RouteIO(None, None, A16b, A16b)
+    assert L.moe_route_batched(3, ctypes.cast(arr, ctypes.c_void_p), *args) == M.MOE_ERR_INVALID
+    assert M.moe_last_error().startswith("moe_route_batched")
+    arr[2] = M.RouteIO(A16 + 2, None, A16b, A16b)
+    assert L.moe_route_batched(3, ctypes.cast(arr, ctypes.c_void_p), *args) == M.MOE_ERR_INVALID
+    arr[2] = M.RouteIO(A16, A16 + 1, A16b, A16b)      # a misaligned bias
+    assert L.moe_route_batched(3, ctypes.cast(arr, ctypes.c_void_p), *args) == M.MOE_ERR_INVALID
+
+    def lio(**kw):
+        d = dict(topk_idx=A16, expert_counts=A16, expert_offsets=A16, rank_counts=A16,
+                 rank_offsets=A16, rank_token_counts=A16, dst_row=A16, src_pair=A16,
+                 overflow=A16, workspace=A16b, workspace_bytes=1 << 20)
+        d.update(kw)
+        return M.LayoutIO(*[d[f] for f, _ in M.LayoutIO._fields_])
+
+    la = (M.LayoutIO * 2)(lio(), lio(rank_token_counts=None))
+    largs = (16, 64, 4, 8, 0, None)
+    assert L.moe_layout_batched(2, ctypes.cast(la, ctypes.c_void_p), *largs) == M.MOE_ERR_INVALID
+    assert "rank_token_counts" in M.moe_last_error()
+    la[1] = lio(workspace_bytes=0)
+    assert L.moe_layout_batched(2, ctypes.cast(la, ctypes.c_void_p),
+                                5000, 64, 4, 8, 0, None) == M.MOE_ERR_WORKSPACE
+    la[1] = lio(dst_row=A16 + 2)
+    assert L.moe_layout_batched(2, ctypes.cast(la, ctypes.c_void_p), *largs) == M.MOE_ERR_INVALID
+    assert L.moe_layout_batched(0, ctypes.cast(la, ctypes.c_void_p), *largs) == M.MOE_ERR_INVALID
+    assert L.moe_layout_batched(2, None, *largs) == M.MOE_ERR_INVALID
+    assert M.moe_last_error().startswith("moe_layout_batched")
+
+
+def test_batch_limit_matches_the_header():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    assert re.search(r"#define MOE_MAX_BATCHES (\d+)", text).group(1) == str(M.MOE_MAX_BATCHES)

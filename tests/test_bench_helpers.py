@@ -204,8 +204,8 @@ def test_pipelined_step_dependencies(group, steps, lead):
     ft = _FakeTorch()
     ft.op(("before",))
     nsets = 2 * group
-    bench.pipelined(ft, lambda i, s: ft.op(("front", i, s)), lambda i, s: ft.op(("back", i, s)),
-                    nsets, steps, ft.side_stream, group, lead)
+    bench.pipelined(ft, lambda pairs: [ft.op(("front", i, s)) for i, s in pairs],
+                    lambda i, s: ft.op(("back", i, s)), nsets, steps, ft.side_stream, group, lead)
     idx = {op[1]: n for n, op in enumerate(ft.ops)}
     before = idx[("before",)]
     for i in range(steps):

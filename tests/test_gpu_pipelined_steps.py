@@ -1,5 +1,5 @@
-"""The benchmark's pipelined steps (the route and layout of a group of steps
-on a side stream beside the dispatch and combine of the group before, 2 *
+"""The benchmark's pipelined steps (the route and layout of a group of steps,
+batched, on a side stream beside the dispatch and combine of the group before, 2 *
 group sets of routing and layout buffers in turn, one shared set of row
 buffers) give the same results as the same steps run one after the other:
 eager, and captured in a HIP graph and replayed. Every step has its own
@@ -163,7 +163,7 @@ def test_pipelined_hierarchical_steps_equal_serial_steps():
     side = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        bench.pipelined(torch, lambda i, s: bench.hierarchical_front(w, sets, inputs, i, s),
+        bench.pipelined(torch, lambda pairs: bench.hierarchical_fronts(w, sets, inputs, pairs),
                         lambda i, s: bench.hierarchical_back(sets, inputs, y, i, s),
                         2 * group, steps, side, group)
     for rep in range(2):
