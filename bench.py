@@ -1125,9 +1125,12 @@ def main():
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
                   ("; steps pipelined on two streams in groups of %d (the first of %d): the "
-                   "route and layout of one group run beside the dispatch and combine of the "
-                   "group before (%d sets of routing and layout buffers in turn, row buffers "
-                   "shared)" % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP), 2 * PIPE_GROUP)
+                   "routes and layouts of one group (batched launches%s) run beside the "
+                   "dispatch and combine of the group before (%d sets of routing and layout "
+                   "buffers in turn, row buffers shared)"
+                   % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP),
+                      "" if w.tokens * w.top_k > 1024 else " for the first group",
+                      2 * PIPE_GROUP)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
