@@ -178,6 +178,7 @@ def run_backward(args, w, M, W, torch, np):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    evict_caches(torch)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -212,6 +213,7 @@ def run_backward(args, w, M, W, torch, np):
         "hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total, "phase_bytes": nb,
         "phases_us": {"combine_backward": round(cb * 1e6, 2), "dispatch_backward": round(db * 1e6, 2)},
+        "cache_eviction": EVICTION,
         "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -396,6 +398,7 @@ def run_hierarchical(args, w, M, W, torch, np):
                    % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP), 2 * PIPE_GROUP) if overlap
                    else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 5),
+        "cache_eviction": EVICTION,
         "config": {"workload": "%s hierarchical: T=%d H=%d E=%d k=%d R=%d, one row per "
                    "(token, rank), bf16 partials" % (w.name, T, H, w.experts, k, w.ranks),
                    "tokens": T, "hidden": H, "experts": w.experts, "top_k": k,
@@ -916,13 +919,32 @@ def overlapped_steps(torch, w, sets, inputs, y, first, steps, side, group=PIPE_G
 
 
 GRAPH_WARM_REPLAYS = 3   # untimed replays of a captured graph before the timed one
+EVICT_BYTES = 1 << 30    # read before each timed window: more than L2 and the 256 MB MALL
+EVICTION = ("a 1 GiB device read before each timed window (evicts L2 and the Infinity Cache "
+            "and leaves no dirty lines to write back inside the window)")
+_evict_buf = []
+
+
+def evict_caches(torch):
+    """Untimed: read EVICT_BYTES of device memory (a torch reduction, with
+    loads that allocate in the caches) and wait, so that the timed window
+    that follows starts from HBM, not from cached inputs. A read rather than
+    a write: a 1 GiB write left hundreds of MB of dirty lines whose write-back
+    then ran inside the window."""
+    if not _evict_buf:
+        b = torch.empty(EVICT_BYTES // 8, dtype=torch.int64, device="cuda")
+        b.fill_(1)
+        _evict_buf.append(b)
+    torch.amax(_evict_buf[0])
+    torch.cuda.synchronize()
 
 
 def timed_run(torch, run, graph):
     """Wall time of run(): captured into one HIP graph, replayed
     GRAPH_WARM_REPLAYS times untimed (the first uploads it; the first few
     replays of a new graph run 2-5% slower) and once timed; or launched from
-    the host once untimed and once timed."""
+    the host once timed (the caller has warmed it up). The caches are evicted
+    before the timed window."""
     if graph:
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
@@ -931,11 +953,13 @@ def timed_run(torch, run, graph):
         for _ in range(GRAPH_WARM_REPLAYS):
             g.replay()
         torch.cuda.synchronize()
+        evict_caches(torch)
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
         return time.perf_counter() - t0
     torch.cuda.synchronize()
+    evict_caches(torch)
     t0 = time.perf_counter()
     run()
     torch.cuda.synchronize()
@@ -1133,6 +1157,7 @@ def main():
                       2 * PIPE_GROUP)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
+        "cache_eviction": EVICTION,
         "config": {"workload": "%s: T=%d H=%d E=%d k=%d R=%d %s%s, %s dispatch, bf16 combine%s"
                    % (w.name, w.tokens, w.hidden, w.experts, w.top_k, w.ranks,
                       "group-limited sigmoid G=%d kg=%d" % (w.groups, w.topk_groups)

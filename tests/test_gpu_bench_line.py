@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FIELDS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
           "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "launch",
-          "serial_ms_per_step", "roofline", "cpu_baseline", "phases_us")
+          "serial_ms_per_step", "roofline", "cpu_baseline", "phases_us", "cache_eviction")
 
 
 def _run(*args):
