@@ -136,3 +136,58 @@ def test_layout_batched_equals_single_calls(case):
             got = outs[b].result()
             for name in got:
                 assert np.array_equal(got[name], L[name].reshape(got[name].shape)), (case, b, name)
+
+
+N_RANDOM = 40
+
+
+def _draw(seed):
+    g = W.rng(70000 + seed)
+    nb = int(g.integers(1, M.MOE_MAX_BATCHES + 1))
+    R = int(g.choice([1, 2, 4, 8, 16, 32]))
+    E = R * int(g.choice([1, 2, 4, 8]))
+    k = int(g.integers(1, min(E, 16) + 1))
+    T = int(g.choice([1, 63, 64, 65, 127, 128, 129, int(g.integers(1, max(2, 20000 // k)))]))
+    cap = 0 if g.random() < 0.5 else int(g.integers(1, max(2, 2 * T * k // E + 2)))
+    # routing settings: softmax, or group-limited sigmoid when the experts split into groups
+    G = int(g.choice([d for d in (1, 2, 4, 8) if E % d == 0 and E // d * d == E]))
+    fn = 1 if G > 1 or g.random() < 0.5 else 0
+    kg = int(g.integers(1, G + 1))
+    while kg * (E // G) < k:
+        kg += 1
+    return dict(nb=nb, T=T, E=E, k=k, R=R, cap=cap, G=G, fn=fn, kg=kg,
+                rtc=bool(g.random() < 0.7), seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(N_RANDOM))
+def test_batched_random_shapes(seed):
+    """Seeded random shapes through both batched calls, each batch against
+    the single calls on the same inputs, bit for bit."""
+    c = _draw(seed)
+    say("batched random case", c)
+    nb, t, e, k, r, cap = c["nb"], c["T"], c["E"], c["k"], c["R"], c["cap"]
+    g = W.rng(80000 + seed)
+    logits = [dev(g.standard_normal((t, e), dtype=np.float32)) for _ in range(nb)]
+    bias = [dev((g.standard_normal(e, dtype=np.float32) * np.float32(0.1)).astype(np.float32))
+            if g.random() < 0.5 else None for _ in range(nb)]
+    idx = [_ints(t * k) for _ in range(nb)]
+    wts = [torch.full((t * k + GUARD,), float("nan"), device="cuda") for _ in range(nb)]
+    M.moe_route_batched(t, e, k, [(logits[b], bias[b], idx[b], wts[b]) for b in range(nb)],
+                        c["fn"], c["G"], c["kg"])
+    outs = [LayoutOut(t, e, k, r, cap, c["rtc"]) for _ in range(nb)]
+    M.moe_layout_batched(t, e, k, r, cap, [outs[b].io(idx[b]) for b in range(nb)])
+    for b in range(nb):
+        i1 = _ints(t * k)
+        w1 = torch.full((t * k + GUARD,), float("nan"), device="cuda")
+        M.moe_route(t, e, k, logits[b], bias[b], c["fn"], c["G"], c["kg"], i1, w1)
+        assert torch.equal(idx[b], i1), (c, b, "topk_idx")
+        assert torch.equal(wts[b][:t * k], w1[:t * k]), (c, b, "topk_weights")
+        got = outs[b].result()
+        one = LayoutOut(t, e, k, r, cap, c["rtc"])
+        o = one.io(i1)
+        M.moe_layout(t, e, k, r, cap, i1, o["expert_counts"], o["expert_offsets"],
+                     o["rank_counts"], o["rank_offsets"], o["rank_token_counts"], o["dst_row"],
+                     o["src_pair"], o["overflow"], o["workspace"], o["workspace_bytes"])
+        want = one.result()
+        for name in want:
+            assert np.array_equal(got[name], want[name]), (c, b, name)

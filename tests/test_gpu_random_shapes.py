@@ -11,13 +11,14 @@ experts per token, and a fraction of masked slots. It then checks:
   - moe_layout_dispatch (the one-launch path when capacity > 0 and
     T*k <= 1024, else layout then dispatch): every layout output and every
     written row bit for bit; rows no pair reaches keep their poison;
-  - moe_combine on random rows and weights, within the combine bound;
+  - moe_combine on random rows and weights: equal bits with the oracle's
+    fp32 slot-order chain;
   - the hierarchical pass (rank layout, send, fan-out, per-rank partials,
-    their sum): rows bit for bit, partials within the combine bound, the
-    final sum within the two-level bound;
+    their sum): rows, partials and the final sum bit for bit with the
+    oracle's two-level chains;
   - the backward pair on the draw's layout: row gradients within one bf16
-    ulp, weight gradients within the dot-product bound, dx within the
-    combine bound (computed by the oracle from the GPU's row gradients).
+    ulp, weight gradients within the dot-product bound, dx bit for bit
+    (computed by the oracle from the GPU's row gradients).
 """
 
 import sys
