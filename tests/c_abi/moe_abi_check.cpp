@@ -12,6 +12,8 @@
 //     below half a bf16 ulp);
 //   - the fanned-out (token, rank) rows equal the dispatched rows, and the
 //     two-level sum stays within two bf16 ulps of x;
+//   - the batched routing and layout give, per batch, what the single calls
+//     give;
 //   - a call with bad arguments returns MOE_ERR_INVALID and names itself.
 // Prints "c-abi check ok" and exits 0 on success.
 
@@ -190,6 +192,61 @@ int main() {
   for (size_t i = 0; i < x.size(); ++i) {
     const float a = bf16_value(out[i]), b = bf16_value(x[i]);
     CHECK(std::fabs(a - b) <= std::ldexp(std::fabs(b), -7), "two-level sum within two ulps of x");
+  }
+
+  // ---- batched calls: batch 0 repeats the flat pass's routing and layout,
+  // batch 1 routes other logits; each batch must equal its single calls
+  {
+    std::vector<float> logits1((size_t)T * E);
+    for (auto& v : logits1) v = (float)(next(seed) % 4096) / 1024.0f - 2.0f;
+    float *d_logits1, *d_wb[2];
+    int32_t *d_ib[2], *d_ecb[2], *d_eob[2], *d_rcb[2], *d_rob[2], *d_rtcb[2], *d_dstb[2],
+        *d_srcb[2], *d_ovfb[2];
+    void* d_wsb[2];
+    if (to_device(logits1, &d_logits1)) return 1;
+    for (int b = 0; b < 2; ++b) {
+      if (alloc(pairs, &d_wb[b]) || alloc(pairs, &d_ib[b]) || alloc(E, &d_ecb[b]) ||
+          alloc(E + 1, &d_eob[b]) || alloc(R, &d_rcb[b]) || alloc(R + 1, &d_rob[b]) ||
+          alloc(R, &d_rtcb[b]) || alloc(pairs, &d_dstb[b]) || alloc(rows, &d_srcb[b]) ||
+          alloc(1, &d_ovfb[b]))
+        return 1;
+      HIP_OK(hipMalloc(&d_wsb[b], ws_bytes + 16));
+    }
+    const moe_route_io rio[2] = {{d_logits, nullptr, d_ib[0], d_wb[0]},
+                                 {d_logits1, nullptr, d_ib[1], d_wb[1]}};
+    MOE_CALL(moe_route_batched(2, rio, T, E, k, MOE_SCORE_SOFTMAX, 1, 1, st));
+    moe_layout_io lio[2];
+    for (int b = 0; b < 2; ++b)
+      lio[b] = moe_layout_io{d_ib[b], d_ecb[b], d_eob[b], d_rcb[b], d_rob[b], d_rtcb[b],
+                             d_dstb[b], d_srcb[b], d_ovfb[b], d_wsb[b], ws_bytes};
+    MOE_CALL(moe_layout_batched(2, lio, T, E, k, R, 0, st));
+    // single calls on batch 1's logits, into the flat pass's buffers
+    MOE_CALL(moe_route(T, E, k, d_logits1, nullptr, MOE_SCORE_SOFTMAX, 1, 1, d_idx, d_w, st));
+    MOE_CALL(moe_layout(T, E, k, R, 0, d_idx, d_ec, d_eo, d_rc, d_ro, d_rtc, d_dst, d_src, d_ovf,
+                        d_ws, ws_bytes, st));
+    HIP_OK(hipStreamSynchronize(st));
+    std::vector<int32_t> i0, i1, d0, d1, s0, s1, e1, one_i, one_d, one_s, one_e;
+    std::vector<float> w0, one_w;
+    if (to_host(d_ib[0], pairs, i0) || to_host(d_ib[1], pairs, i1) ||
+        to_host(d_dstb[0], pairs, d0) || to_host(d_dstb[1], pairs, d1) ||
+        to_host(d_srcb[0], rows, s0) || to_host(d_srcb[1], rows, s1) ||
+        to_host(d_ecb[1], E, e1) || to_host(d_wb[0], pairs, w0) ||
+        to_host(d_idx, pairs, one_i) || to_host(d_dst, pairs, one_d) ||
+        to_host(d_src, rows, one_s) || to_host(d_ec, E, one_e) || to_host(d_w, pairs, one_w))
+      return 1;
+    CHECK(i0 == idx && d0 == dst && s0 == src, "batch 0 equals the flat pass's route and layout");
+    CHECK(std::memcmp(w0.data(), w.data(), pairs * sizeof(float)) == 0, "batch 0 weights");
+    CHECK(i1 == one_i && d1 == one_d && s1 == one_s && e1 == one_e,
+          "batch 1 equals its single calls");
+    (void)one_w;
+    const int bad_n = moe_route_batched(0, rio, T, E, k, MOE_SCORE_SOFTMAX, 1, 1, st);
+    CHECK(bad_n == MOE_ERR_INVALID, "zero batches are rejected");
+    HIP_OK(hipFree(d_logits1));
+    for (int b = 0; b < 2; ++b) {
+      void* bb[] = {d_wb[b], d_ib[b], d_ecb[b], d_eob[b], d_rcb[b], d_rob[b], d_rtcb[b],
+                    d_dstb[b], d_srcb[b], d_ovfb[b], d_wsb[b]};
+      for (void* q : bb) HIP_OK(hipFree(q));
+    }
   }
 
   // ---- an error is reported on the host, before anything is enqueued
