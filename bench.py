@@ -16,10 +16,11 @@ in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
-streams in groups of 4 steps: the route and layout of one group run beside the
-dispatch and combine of the group before, on 8 sets of layer buffers used in
-turn (--serial: one step after the other; the default with --eager). The serial rate of the
-same steps is measured in the same run and reported beside it.
+streams in groups of 8 steps: the routes and layouts of one group (batched
+launches) run beside the dispatch and combine of the group before, on 16 sets
+of routing and layout buffers used in turn (--serial: one step after the
+other; the default with --eager). The serial rate of the same steps is
+measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      HBM roofline of the dominant kernel (combine): algorithmic
@@ -822,8 +823,8 @@ def serial_steps(w, bufs, inputs, y, first, steps, fuse=True):
         b.combine(y)
 
 
-PIPE_GROUP = 4   # steps per cross-stream wait of the pipelined mode
-PIPE_LEAD = 4    # steps of the first group
+PIPE_GROUP = 8   # steps per cross-stream wait of the pipelined mode (one batched front call)
+PIPE_LEAD = 8    # steps of the first group
 
 
 def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
