@@ -16,11 +16,12 @@ in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
-streams in groups of 8 steps: the routes and layouts of one group (batched
-launches) run beside the dispatch and combine of the group before, on 16 sets
-of routing and layout buffers used in turn (--serial: one step after the
-other; the default with --eager). The serial rate of the same steps is
-measured in the same run and reported beside it.
+streams in groups of 16 steps after a first group of 8 (groups of 8 for
+decode-sized steps, pipe_shape): the routes and layouts of one group (batched
+launches) run beside the dispatch and combine of the group before, on 2 *
+group sets of routing and layout buffers used in turn (--serial: one step
+after the other; the default with --eager). The serial rate of the same steps
+is measured in the same run and reported beside it.
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      HBM roofline of the dominant kernel (combine): algorithmic
@@ -265,11 +266,12 @@ def hierarchical_fronts(w, sets, inputs, pairs):
     launch and their expert layouts in one launch per pass (the batched
     entry points), then each (token, rank) layout."""
     M = _moe()
-    lbs = [sets[s][0] for _, s in pairs]
-    ds = [inputs[i % len(inputs)] for i, _ in pairs]
-    M.route_batches(lbs, [d["logits"] for d in ds], [d["bias"] for d in ds], w.score_fn,
-                    w.groups, w.topk_groups)
-    M.layout_batches(lbs)
+    for c in range(0, len(pairs), M.MOE_MAX_BATCHES):
+        lbs = [sets[s][0] for _, s in pairs[c:c + M.MOE_MAX_BATCHES]]
+        ds = [inputs[i % len(inputs)] for i, _ in pairs[c:c + M.MOE_MAX_BATCHES]]
+        M.route_batches(lbs, [d["logits"] for d in ds], [d["bias"] for d in ds], w.score_fn,
+                        w.groups, w.topk_groups)
+        M.layout_batches(lbs)
     for _, s in pairs:
         lb, rb = sets[s]
         rb.rank_layout(lb.topk_idx)
@@ -307,9 +309,10 @@ def run_hierarchical(args, w, M, W, torch, np):
     lb = M.LayerBuffers.allocate(T, H, w.experts, k, w.ranks, w.capacity, device=dev,
                                  dtype=dtype)
     rb = M.RankBuffers.allocate(T, H, w.experts, k, w.ranks, dtype=dtype, device=dev)
-    # pipelined steps: 2 * PIPE_GROUP sets of layout buffers in turn, row
-    # buffers shared
-    nsets = 2 * PIPE_GROUP if overlap else 1
+    # pipelined steps: 2 * group sets of layout buffers in turn, row buffers
+    # shared
+    group, lead = pipe_shape(w)
+    nsets = 2 * group if overlap else 1
     sets = [(lb, rb)] + [(lb.sharing_rows(), rb.sharing_rows()) for _ in range(nsets - 1)]
 
     phases = ["route", "layout", "rank_layout", "dispatch", "expand", "combine_local",
@@ -336,7 +339,7 @@ def run_hierarchical(args, w, M, W, torch, np):
     def piped(first, n):
         pipelined(torch, lambda pairs: hierarchical_fronts(w, sets, inputs,
                                                            [(first + i, s) for i, s in pairs]),
-                  lambda i, s: back(first + i, s), nsets, n, side)
+                  lambda i, s: back(first + i, s), nsets, n, side, group, lead)
 
     side = torch.cuda.Stream() if overlap else None
 
@@ -396,7 +399,7 @@ def run_hierarchical(args, w, M, W, torch, np):
                    "route, expert layout and (token, rank) layout of one group run beside "
                    "the send, fan-out and combines of the group before (%d sets of layout "
                    "buffers in turn, row buffers shared)"
-                   % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP), 2 * PIPE_GROUP) if overlap
+                   % (group, min(lead, group), 2 * group) if overlap
                    else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 5),
         "cache_eviction": EVICTION,
@@ -533,7 +536,7 @@ def measure_lib():
     return _measure_lib
 
 
-def stamped_pipeline(torch, np, front, back, nsets, steps, side):
+def stamped_pipeline(torch, np, front, back, nsets, steps, side, group, lead):
     """Per-step latency and completion intervals of pipelined steps, from
     the GPU's wall clock: the pipelined steps are captured again with a
     one-wave stamp kernel before each step's front (on the side stream) and
@@ -561,7 +564,8 @@ def stamped_pipeline(torch, np, front, back, nsets, steps, side):
         back(i, s)
         stamp(steps + i)
 
-    wall = timed_run(torch, lambda: pipelined(torch, f, b, nsets, steps, side), True)
+    wall = timed_run(torch, lambda: pipelined(torch, f, b, nsets, steps, side, group, lead),
+                     True)
     t = st.cpu().numpy().astype(np.float64) * 1e6 / hz       # microseconds
     lat = t[1] - t[0]
     gap = np.diff(t[1])
@@ -823,8 +827,21 @@ def serial_steps(w, bufs, inputs, y, first, steps, fuse=True):
         b.combine(y)
 
 
-PIPE_GROUP = 8   # steps per cross-stream wait of the pipelined mode (one batched front call)
-PIPE_LEAD = 8    # steps of the first group
+PIPE_GROUP = 16         # steps per cross-stream wait of the pipelined mode
+PIPE_LEAD = 8           # steps of the first group
+PIPE_GROUP_ONE_TILE = 8  # the same for steps of one layout tile (decode)
+
+
+def pipe_shape(w):
+    """(group, first group) of the pipelined mode for workload w. Same
+    process, median of 10 replays, batched fronts: groups of 16 after a first
+    group of 8 ran the DeepSeek-V3-shaped steps at 147.2 / 146.5 us/step (20 /
+    50 steps) against 148.4 / 148.3 in groups of 8, mixtral ~1 us faster,
+    qwen3_skew within noise; decode steps ran slower in groups of 16 (16.3 /
+    14.3 against 14.2 / 13.5 us in groups of 8)."""
+    if w.tokens * w.top_k > 1024:
+        return PIPE_GROUP, PIPE_LEAD
+    return PIPE_GROUP_ONE_TILE, PIPE_LEAD
 
 
 def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
@@ -892,10 +909,12 @@ def step_halves(w, sets, inputs, y, first):
     def front(pairs):
         ds = [inputs[(first + i) % len(inputs)] for i, _ in pairs]
         if batch_all or pairs[0][0] == 0:
-            bufs = [sets[s] for _, s in pairs]
-            M.route_batches(bufs, [d["logits"] for d in ds], [d["bias"] for d in ds],
-                            w.score_fn, w.groups, w.topk_groups)
-            M.layout_batches(bufs)
+            for c in range(0, len(pairs), M.MOE_MAX_BATCHES):
+                bufs = [sets[s] for _, s in pairs[c:c + M.MOE_MAX_BATCHES]]
+                dc = ds[c:c + M.MOE_MAX_BATCHES]
+                M.route_batches(bufs, [d["logits"] for d in dc], [d["bias"] for d in dc],
+                                w.score_fn, w.groups, w.topk_groups)
+                M.layout_batches(bufs)
             return
         for (_, s), d in zip(pairs, ds):
             sets[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
@@ -909,14 +928,15 @@ def step_halves(w, sets, inputs, y, first):
     return front, back
 
 
-def overlapped_steps(torch, w, sets, inputs, y, first, steps, side, group=PIPE_GROUP):
+def overlapped_steps(torch, w, sets, inputs, y, first, steps, side, group=PIPE_GROUP,
+                     lead=PIPE_LEAD):
     """The steps of serial_steps pipelined on two streams (pipelined()): the
     route and layout of a group of steps run beside the dispatch and combine
     of the group before, on the 2 * group buffer sets in `sets` in turn
     (routing and layout buffers of their own, row buffers shared). Every step
     does all of its work; the results equal those of serial_steps."""
     front, back = step_halves(w, sets, inputs, y, first)
-    pipelined(torch, front, back, len(sets), steps, side, group)
+    pipelined(torch, front, back, len(sets), steps, side, group, lead)
 
 
 GRAPH_WARM_REPLAYS = 3   # untimed replays of a captured graph before the timed one
@@ -1025,9 +1045,10 @@ def main():
     # us/step eager, 18.3 against 20.1 replayed)
     if args.overlap is None:
         args.overlap = args.graph
-    # pipelined steps: 2 * PIPE_GROUP sets of routing and layout buffers in
+    # pipelined steps: 2 * group sets of routing and layout buffers in
     # turn, the row buffers of `buf` shared (the backs run one after the other)
-    bufs = [buf] + ([buf.sharing_rows() for _ in range(2 * PIPE_GROUP - 1)]
+    group, lead = pipe_shape(w)
+    bufs = [buf] + ([buf.sharing_rows() for _ in range(2 * group - 1)]
                     if args.overlap else [])
     side = torch.cuda.Stream() if args.overlap else None
 
@@ -1063,13 +1084,14 @@ def main():
     # ---- warmup
     serial_steps(w, bufs, inputs, y, 0, warm, fuse=not args.graph)
     if args.overlap:
-        overlapped_steps(torch, w, bufs, inputs, y, 0, warm, side)
+        overlapped_steps(torch, w, bufs, inputs, y, 0, warm, side, group, lead)
     torch.cuda.synchronize()
 
     # ---- timed steps: back to back, nothing but the path on the stream(s)
     serial_wall = timed_run(torch, lambda: serial_steps(w, bufs, inputs, y, warm, steps,
                                                         fuse=not args.graph), args.graph)
-    wall = (timed_run(torch, lambda: overlapped_steps(torch, w, bufs, inputs, y, warm, steps, side),
+    wall = (timed_run(torch, lambda: overlapped_steps(torch, w, bufs, inputs, y, warm, steps, side,
+                                                      group, lead),
                       args.graph) if args.overlap else serial_wall)
 
     # ---- the same steps again with HIP events between the phases (on the
@@ -1108,7 +1130,8 @@ def main():
     stamped = None
     if args.overlap and args.graph:
         front_h, back_h = step_halves(w, bufs, inputs, y, warm)
-        stamped = stamped_pipeline(torch, np, front_h, back_h, len(bufs), steps, side)
+        stamped = stamped_pipeline(torch, np, front_h, back_h, len(bufs), steps, side, group,
+                                   lead)
 
     # ---- cold steps: 1 GiB write between steps (untimed)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -1153,9 +1176,9 @@ def main():
                    "routes and layouts of one group (batched launches%s) run beside the "
                    "dispatch and combine of the group before (%d sets of routing and layout "
                    "buffers in turn, row buffers shared)"
-                   % (PIPE_GROUP, min(PIPE_LEAD, PIPE_GROUP),
+                   % (group, min(lead, group),
                       "" if w.tokens * w.top_k > 1024 else " for the first group",
-                      2 * PIPE_GROUP)
+                      2 * group)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "cache_eviction": EVICTION,
