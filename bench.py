@@ -16,8 +16,8 @@ in HBM when timing starts. The timed steps are captured once into a HIP graph
 and replayed (every kernel of every step still runs; the host only stops
 issuing the launches one by one); --eager launches them from the host instead.
 Steps are independent batches, so by default they are pipelined on two
-streams in groups of 16 steps after a first group of 8 (groups of 8 for
-decode-sized steps, pipe_shape): the routes and layouts of one group (batched
+streams in groups of 16 steps after a first group of 8 (pipe_shape): the
+routes and layouts of one group (batched
 launches) run beside the dispatch and combine of the group before, on 2 *
 group sets of routing and layout buffers used in turn (--serial: one step
 after the other; the default with --eager). The serial rate of the same steps
@@ -827,21 +827,18 @@ def serial_steps(w, bufs, inputs, y, first, steps, fuse=True):
         b.combine(y)
 
 
-PIPE_GROUP = 16         # steps per cross-stream wait of the pipelined mode
-PIPE_LEAD = 8           # steps of the first group
-PIPE_GROUP_ONE_TILE = 8  # the same for steps of one layout tile (decode)
+PIPE_GROUP = 16   # steps per cross-stream wait of the pipelined mode
+PIPE_LEAD = 8     # steps of the first group
 
 
 def pipe_shape(w):
-    """(group, first group) of the pipelined mode for workload w. Same
-    process, median of 10 replays, batched fronts: groups of 16 after a first
-    group of 8 ran the DeepSeek-V3-shaped steps at 147.2 / 146.5 us/step (20 /
-    50 steps) against 148.4 / 148.3 in groups of 8, mixtral ~1 us faster,
-    qwen3_skew within noise; decode steps ran slower in groups of 16 (16.3 /
-    14.3 against 14.2 / 13.5 us in groups of 8)."""
-    if w.tokens * w.top_k > 1024:
-        return PIPE_GROUP, PIPE_LEAD
-    return PIPE_GROUP_ONE_TILE, PIPE_LEAD
+    """(group, first group) of the pipelined mode. Same process, batched
+    fronts: groups of 16 after a first group of 8 ran the DeepSeek-V3-shaped
+    steps at 147.2 / 146.5 us/step (20 / 50 steps, median of 10) against 148.4
+    / 148.3 in groups of 8, mixtral ~1 us faster, qwen3_skew within noise, and
+    decode steps at 11.6 / 11.7 us (50 / 200 steps, median of 8) against 12.1 /
+    12.3 in groups of 8."""
+    return PIPE_GROUP, PIPE_LEAD
 
 
 def pipeline_groups(steps, group=PIPE_GROUP, lead=PIPE_LEAD):
@@ -893,32 +890,23 @@ def pipelined(torch, front, back, nsets, steps, side, group=PIPE_GROUP, lead=PIP
 def step_halves(w, sets, inputs, y, first):
     """front(pairs): route and layout of the steps (i, s) in `pairs`, step i
     on buffer set s; back(i, s): dispatch and combine of step i. The fronts
-    of a group run as batches, one routing launch and one launch per layout
-    pass (moe_route_batched, moe_layout_batched): a group's fronts then cost
-    about one step's launches, which shortens the pipeline's fill. For steps
-    of one layout tile (decode) only the first group is batched: later ones
-    ran 0.5 us/step faster one step at a time (12.3 against 12.8 us over 200
-    steps), while the DeepSeek-V3-shaped steps gain from batching every group
-    (148.9 against 149.5 us). Layout and dispatch are separate launches here
-    even where moe_layout_dispatch would fuse them (decode-sized capacity
-    mode): the layout is latency-bound, and on the side stream it is
-    hidden."""
+    of a group run as batches of up to MOE_MAX_BATCHES steps, one routing
+    launch and one launch per layout pass each (moe_route_batched,
+    moe_layout_batched): a group's fronts then cost about one step's
+    launches, which shortens the pipeline's fill and leaves fewer launches
+    beside the backs. Layout and dispatch are separate launches here even
+    where moe_layout_dispatch would fuse them (decode-sized capacity mode):
+    the layout is latency-bound, and on the side stream it is hidden."""
     M = _moe()
-    batch_all = w.tokens * w.top_k > 1024
 
     def front(pairs):
         ds = [inputs[(first + i) % len(inputs)] for i, _ in pairs]
-        if batch_all or pairs[0][0] == 0:
-            for c in range(0, len(pairs), M.MOE_MAX_BATCHES):
-                bufs = [sets[s] for _, s in pairs[c:c + M.MOE_MAX_BATCHES]]
-                dc = ds[c:c + M.MOE_MAX_BATCHES]
-                M.route_batches(bufs, [d["logits"] for d in dc], [d["bias"] for d in dc],
-                                w.score_fn, w.groups, w.topk_groups)
-                M.layout_batches(bufs)
-            return
-        for (_, s), d in zip(pairs, ds):
-            sets[s].route(d["logits"], d["bias"], w.score_fn, w.groups, w.topk_groups)
-            sets[s].layout()
+        for c in range(0, len(pairs), M.MOE_MAX_BATCHES):
+            bufs = [sets[s] for _, s in pairs[c:c + M.MOE_MAX_BATCHES]]
+            dc = ds[c:c + M.MOE_MAX_BATCHES]
+            M.route_batches(bufs, [d["logits"] for d in dc], [d["bias"] for d in dc],
+                            w.score_fn, w.groups, w.topk_groups)
+            M.layout_batches(bufs)
 
     def back(i, s):
         d = inputs[(first + i) % len(inputs)]
@@ -1173,12 +1161,10 @@ def main():
         "data": "synthetic",
         "launch": ("hip graph replay" if args.graph else "eager launches") +
                   ("; steps pipelined on two streams in groups of %d (the first of %d): the "
-                   "routes and layouts of one group (batched launches%s) run beside the "
+                   "routes and layouts of one group (batched launches) run beside the "
                    "dispatch and combine of the group before (%d sets of routing and layout "
                    "buffers in turn, row buffers shared)"
-                   % (group, min(lead, group),
-                      "" if w.tokens * w.top_k > 1024 else " for the first group",
-                      2 * group)
+                   % (group, min(lead, group), 2 * group)
                    if args.overlap else "; one step after the other on one stream"),
         "serial_ms_per_step": round(serial_wall * 1e3 / steps, 5),
         "cache_eviction": EVICTION,
