@@ -73,10 +73,13 @@ def _check(sets, want_small, want_rows, what):
         assert torch.equal(got, v), (what, "rows of the last step", n)
 
 
-@pytest.mark.parametrize("name,steps,group", [("dsv3", 10, 4), ("dsv3", 5, 1), ("decode", 11, 4)])
-def test_pipelined_steps_equal_serial_steps(name, steps, group):
+@pytest.mark.parametrize("name,steps,group,lead", [
+    ("dsv3", 10, 4, 4), ("dsv3", 5, 1, 1), ("decode", 11, 4, 4),
+    # the bench's shape: groups of 16 after a first group of 8, fronts in batched calls of 8
+    ("dsv3", 21, 16, 8), ("decode", 40, 16, 8)])
+def test_pipelined_steps_equal_serial_steps(name, steps, group, lead):
     w = W.WORKLOADS[name]
-    say("pipelined steps", name, "x", steps, "in groups of", group)
+    say("pipelined steps", name, "x", steps, "in groups of", group, "after a first of", lead)
     seeds = [w.step_seed0 + i for i in range(steps)] if w.steps > 1 else list(range(steps))
     inputs = []
     for s in seeds:
@@ -111,7 +114,7 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
 
     side = torch.cuda.Stream()
     _poison(sets)
-    bench.overlapped_steps(torch, w, sets, inputs, y, 0, steps, side, group)
+    bench.overlapped_steps(torch, w, sets, inputs, y, 0, steps, side, group, lead)
     torch.cuda.synchronize()
     _check(sets, want_small, want_rows, "eager")
     say("  eager pipelined steps equal the serial ones")
@@ -119,7 +122,7 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group):
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        bench.overlapped_steps(torch, w, sets, inputs, y, 0, steps, side, group)
+        bench.overlapped_steps(torch, w, sets, inputs, y, 0, steps, side, group, lead)
     for rep in range(2):
         _poison(sets)
         torch.cuda.synchronize()
