@@ -263,18 +263,18 @@ def _moe():
 
 def hierarchical_fronts(w, sets, inputs, pairs):
     """hierarchical_front of steps (i, s) in `pairs`: their routes in one
-    launch and their expert layouts in one launch per pass (the batched
-    entry points), then each (token, rank) layout."""
+    launch, their expert layouts and their (token, rank) layouts in one
+    launch per pass (the batched entry points), in calls of up to
+    MOE_MAX_BATCHES steps."""
     M = _moe()
     for c in range(0, len(pairs), M.MOE_MAX_BATCHES):
         lbs = [sets[s][0] for _, s in pairs[c:c + M.MOE_MAX_BATCHES]]
+        rbs = [sets[s][1] for _, s in pairs[c:c + M.MOE_MAX_BATCHES]]
         ds = [inputs[i % len(inputs)] for i, _ in pairs[c:c + M.MOE_MAX_BATCHES]]
         M.route_batches(lbs, [d["logits"] for d in ds], [d["bias"] for d in ds], w.score_fn,
                         w.groups, w.topk_groups)
         M.layout_batches(lbs)
-    for _, s in pairs:
-        lb, rb = sets[s]
-        rb.rank_layout(lb.topk_idx)
+        M.rank_layout_batches(rbs, [lb.topk_idx for lb in lbs])
 
 
 def hierarchical_back(sets, inputs, y, i, s):

@@ -43,7 +43,7 @@ EXPORTED = ("moe_status_string", "moe_last_error", "moe_route",
             "moe_rank_layout_workspace_bytes", "moe_rank_layout", "moe_expand",
             "moe_combine_local", "moe_combine_partials", "moe_layout_dispatch",
             "moe_layout_dispatch_is_fused", "moe_layout_no_alloc", "moe_route_batched",
-            "moe_layout_batched")
+            "moe_layout_batched", "moe_rank_layout_batched")
 
 _lib = None
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.moe_route_batched.restype = i32
     L.moe_layout_batched.argtypes = [i32, vp, i32, i32, i32, i32, i32, vp]
     L.moe_layout_batched.restype = i32
+    L.moe_rank_layout_batched.argtypes = [i32, vp, i32, i32, i32, i32, vp]
+    L.moe_rank_layout_batched.restype = i32
     _lib = L
     return L
 
@@ -239,6 +241,26 @@ def moe_layout_batched(num_tokens, num_experts, top_k, num_ranks, capacity, batc
                                     num_experts, top_k, num_ranks, capacity, _stream(stream)))
 
 
+class RankLayoutIO(ctypes.Structure):
+    """moe_rank_layout_io: one batch of moe_rank_layout_batched."""
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("rank_token_counts", ctypes.c_void_p),
+                ("rank_token_offsets", ctypes.c_void_p), ("rank_row", ctypes.c_void_p),
+                ("send_row", ctypes.c_void_p), ("row_token", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def moe_rank_layout_batched(num_tokens, num_experts, top_k, num_ranks, batches,
+                            stream=None) -> None:
+    """batches: sequence of dicts with the keys of RankLayoutIO (device
+    tensors; workspace_bytes an int)."""
+    arr = (RankLayoutIO * max(len(batches), 1))(
+        *[RankLayoutIO(*[_ptr(b.get(f)) for f, _ in RankLayoutIO._fields_[:-1]],
+                       int(b["workspace_bytes"])) for b in batches])
+    _check(lib().moe_rank_layout_batched(len(batches), ctypes.cast(arr, ctypes.c_void_p),
+                                         num_tokens, num_experts, top_k, num_ranks,
+                                         _stream(stream)))
+
+
 def moe_layout_dispatch_is_fused(num_tokens, top_k, capacity) -> bool:
     return bool(lib().moe_layout_dispatch_is_fused(num_tokens, top_k, capacity))
 
@@ -321,5 +343,5 @@ def moe_combine_partials(num_tokens, hidden, top_k, num_rank_rows, partial_bf16,
                                       _stream(stream)))
 
 
-from .buffers import (LayerBuffers, RankBuffers, layout_batches, route_batches,  # noqa: E402,F401
-                      run_layer)
+from .buffers import (LayerBuffers, RankBuffers, layout_batches,  # noqa: E402,F401
+                      rank_layout_batches, route_batches, run_layer)

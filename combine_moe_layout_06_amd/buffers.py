@@ -15,8 +15,8 @@ from . import (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP8_E4M3, MOE_FP8
                MOE_MX_BLOCK, moe_combine, moe_combine_local, moe_combine_partials,
                moe_dispatch, moe_expand, moe_layout, moe_layout_dispatch,
                moe_layout_workspace_bytes,
-               moe_layout_batched, moe_rank_layout, moe_rank_layout_workspace_bytes, moe_route,
-               moe_route_batched)
+               moe_layout_batched, moe_rank_layout, moe_rank_layout_batched,
+               moe_rank_layout_workspace_bytes, moe_route, moe_route_batched)
 
 
 @dataclasses.dataclass
@@ -247,6 +247,19 @@ def layout_batches(bufs, stream=None):
                              dst_row=b.dst_row, src_pair=b.src_pair, overflow=b.overflow,
                              workspace=b.workspace, workspace_bytes=b.workspace_bytes)
                         for b in bufs], stream)
+
+
+def rank_layout_batches(bufs, topk_idx, stream=None):
+    """rank_layout() of every RankBuffers in `bufs` (same sizes) on the
+    routing topk_idx[i] of each, one launch per pass for all of them
+    (moe_rank_layout_batched)."""
+    b0 = bufs[0]
+    moe_rank_layout_batched(b0.tokens, b0.experts, b0.top_k, b0.ranks,
+                            [dict(topk_idx=ix, rank_token_counts=b.rank_token_counts,
+                                  rank_token_offsets=b.rank_token_offsets, rank_row=b.rank_row,
+                                  send_row=b.send_row, row_token=b.row_token,
+                                  workspace=b.workspace, workspace_bytes=b.workspace_bytes)
+                             for b, ix in zip(bufs, topk_idx)], stream)
 
 
 def run_layer(buf: LayerBuffers, logits, bias, x, score_fn, num_groups=1, topk_groups=1,

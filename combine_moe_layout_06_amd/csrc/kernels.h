@@ -76,6 +76,22 @@ hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
                               int32_t* counts, int32_t* offsets, int32_t* rank_row,
                               int32_t* send_row, int32_t* row_token, void* workspace,
                               hipStream_t stream);
+// Several (token, rank) layouts of the same shape in one set of launches:
+// batch b on grid row b.
+struct RankLayoutBatch {
+  const int32_t* idx;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* rank_row;
+  int32_t* send_row;
+  int32_t* row_token;
+  void* workspace;
+};
+struct RankLayoutBatches {
+  RankLayoutBatch b[kMaxBatches];
+};
+hipError_t launch_rank_layout_batches(int nb, const RankLayoutBatches& rb, int T, int E, int k,
+                                      int R, hipStream_t stream);
 
 hipError_t launch_dispatch_bf16(int T, int H, int k, int num_rows, const void* x,
                                 const int32_t* dst_row, void* out, hipStream_t stream);

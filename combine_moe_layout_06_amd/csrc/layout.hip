@@ -787,8 +787,10 @@ __device__ __forceinline__ int first_slot_of_rank(const int* r, int j) {
 }
 
 __global__ __launch_bounds__(kThreads) void rank_count_kernel(
-    int T, int E, int k, int R, int epr, int epr_shift, int tt,
-    const int32_t* __restrict__ idx, int32_t* __restrict__ ws_rhist) {
+    int T, int E, int k, int R, int epr, int epr_shift, int tt, const RankLayoutBatches rb) {
+  const RankLayoutBatch& bt = rb.b[blockIdx.y];
+  const int32_t* __restrict__ idx = bt.idx;
+  int32_t* __restrict__ ws_rhist = static_cast<int32_t*>(bt.workspace);
   __shared__ int s_rhist[MOE_MAX_EXPERTS];
   __shared__ int s_rank[kTilePairs];
 
@@ -825,13 +827,21 @@ __global__ __launch_bounds__(kThreads) void rank_count_kernel(
 }
 
 // ntiles == 1 (all pairs in one tile, one block): the block counts its own
-// pairs and no count pass runs. Otherwise one block per tile.
+// pairs and no count pass runs. Otherwise one block per tile. scanned: the
+// scan pass has run; the workspace holds the base of every tile, then the
+// totals. Batch blockIdx.y.
 __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     int T, int E, int k, int R, int epr, int epr_shift, int tt, int ntiles, int max_rows,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ ws_rhist,
-    const int32_t* __restrict__ ws_tot, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ rank_row, int32_t* __restrict__ send_row,
-    int32_t* __restrict__ row_token) {
+    int scanned, const RankLayoutBatches rb) {
+  const RankLayoutBatch& bt = rb.b[blockIdx.y];
+  const int32_t* __restrict__ idx = bt.idx;
+  const int32_t* __restrict__ ws_rhist = static_cast<const int32_t*>(bt.workspace);
+  const int32_t* __restrict__ ws_tot = scanned ? ws_rhist + (size_t)ntiles * R : nullptr;
+  int32_t* __restrict__ counts = bt.counts;
+  int32_t* __restrict__ offsets = bt.offsets;
+  int32_t* __restrict__ rank_row = bt.rank_row;
+  int32_t* __restrict__ send_row = bt.send_row;
+  int32_t* __restrict__ row_token = bt.row_token;
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_pre[MOE_MAX_EXPERTS];
@@ -855,9 +865,7 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     const int p = (wave * kChunks + c) * MOE_WAVE + lane;
     v[c] = p < np ? idx[pair0 + p] : -1;
   }
-  // ws_tot != nullptr: the scan pass has run; ws_rhist holds the base of
-  // every tile, and the block reads its own row and the totals
-  const bool scanned = ws_tot != nullptr;
+  // after the scan pass the block reads its own base row and the totals
   const int hist_n = self_count || scanned ? 0 : ntiles * R;
   int h[kStage / kThreads];
   stage_load(h, ws_rhist, min(kStage, hist_n));
@@ -1084,37 +1092,44 @@ size_t rank_layout_workspace_bytes(int T, int k, int R) {
   return (tiles + (layout_scans((int)tiles, R) ? 1 : 0)) * (size_t)R * sizeof(int32_t);
 }
 
-hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
-                              int32_t* counts, int32_t* offsets, int32_t* rank_row,
-                              int32_t* send_row, int32_t* row_token, void* workspace,
-                              hipStream_t stream) {
+hipError_t launch_rank_layout_batches(int nb, const RankLayoutBatches& rb, int T, int E,
+                                      int k, int R, hipStream_t stream) {
+  if (nb == 0) return hipSuccess;
   const int tt = layout_tile_tokens(k);
   const int ntiles = layout_num_tiles(T, k);
   const int epr = E / R;
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
   const int max_rows = T * (k < R ? k : R);
-  int32_t* ws = static_cast<int32_t*>(workspace);
   const bool scan = ntiles > 1 && layout_scans(ntiles, R);
-  int32_t* ws_tot = scan ? ws + (size_t)ntiles * R : nullptr;
   if (ntiles > 1) {
-    hipLaunchKernelGGL(rank_count_kernel, dim3(ntiles), dim3(kThreads), 0, stream,
-                       T, E, k, R, epr, epr_shift, tt, idx, ws);
+    hipLaunchKernelGGL(rank_count_kernel, dim3(ntiles, nb), dim3(kThreads), 0, stream,
+                       T, E, k, R, epr, epr_shift, tt, rb);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (scan) {
+    // the scan pass is rare (hundreds of tiles): one launch per batch
+    for (int b = 0; scan && b < nb; ++b) {
+      int32_t* ws = static_cast<int32_t*>(rb.b[b].workspace);
       hipLaunchKernelGGL(layout_scan_kernel, dim3((R + kScanCols - 1) / kScanCols),
                          dim3(kScanThreads), 0, stream, ntiles, R,
-                         (R + kScanCols - 1) / kScanCols, ws, ws_tot, 0,
+                         (R + kScanCols - 1) / kScanCols, ws, ws + (size_t)ntiles * R, 0,
                          static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
       err = hipGetLastError();
       if (err != hipSuccess) return err;
     }
   }
   const int blocks = ntiles > 1 ? ntiles : 1;
-  hipLaunchKernelGGL(rank_place_kernel, dim3(blocks), dim3(kThreads), 0, stream, T, E, k, R,
-                     epr, epr_shift, tt, ntiles, max_rows, idx, ws, ws_tot, counts, offsets,
-                     rank_row, send_row, row_token);
+  hipLaunchKernelGGL(rank_place_kernel, dim3(blocks, nb), dim3(kThreads), 0, stream, T, E, k,
+                     R, epr, epr_shift, tt, ntiles, max_rows, scan ? 1 : 0, rb);
   return hipGetLastError();
+}
+
+hipError_t launch_rank_layout(int T, int E, int k, int R, const int32_t* idx,
+                              int32_t* counts, int32_t* offsets, int32_t* rank_row,
+                              int32_t* send_row, int32_t* row_token, void* workspace,
+                              hipStream_t stream) {
+  RankLayoutBatches rb{};
+  rb.b[0] = RankLayoutBatch{idx, counts, offsets, rank_row, send_row, row_token, workspace};
+  return launch_rank_layout_batches(1, rb, T, E, k, R, stream);
 }
 
 bool layout_dispatch_fused(int T, int k, int cap) {

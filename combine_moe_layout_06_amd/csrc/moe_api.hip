@@ -452,12 +452,16 @@ size_t moe_rank_layout_workspace_bytes(int num_tokens, int top_k, int num_ranks)
   return moe::rank_layout_workspace_bytes(num_tokens, top_k, num_ranks);
 }
 
-int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
-                    const int32_t* topk_idx, int32_t* rank_token_counts,
-                    int32_t* rank_token_offsets, int32_t* rank_row, int32_t* send_row,
-                    int32_t* row_token, void* workspace, size_t workspace_bytes,
-                    void* stream) {
-  const char* fn = "moe_rank_layout";
+}  // extern "C"
+
+namespace {
+
+// Arguments of one (token, rank) layout.
+int check_rank_layout(const char* fn, int num_tokens, int num_experts, int top_k,
+                      int num_ranks, const int32_t* topk_idx, const int32_t* rank_token_counts,
+                      const int32_t* rank_token_offsets, const int32_t* rank_row,
+                      const int32_t* send_row, const int32_t* row_token, const void* workspace,
+                      size_t workspace_bytes) {
   int st = check_topk(fn, num_tokens, num_experts, top_k);
   if (st != MOE_OK) return st;
   if (num_ranks < 1 || num_ranks > num_experts || num_experts % num_ranks != 0)
@@ -476,10 +480,50 @@ int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace_bytes);
   if (!aligned(workspace, 4)) return fail(MOE_ERR_INVALID, "%s: workspace not aligned", fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
+                    const int32_t* topk_idx, int32_t* rank_token_counts,
+                    int32_t* rank_token_offsets, int32_t* rank_row, int32_t* send_row,
+                    int32_t* row_token, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "moe_rank_layout";
+  const int st = check_rank_layout(fn, num_tokens, num_experts, top_k, num_ranks, topk_idx,
+                                   rank_token_counts, rank_token_offsets, rank_row, send_row,
+                                   row_token, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
   return from_hip(moe::launch_rank_layout(num_tokens, num_experts, top_k, num_ranks, topk_idx,
                                           rank_token_counts, rank_token_offsets, rank_row,
                                           send_row, row_token, workspace,
                                           static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int moe_rank_layout_batched(int num_batches, const moe_rank_layout_io* batches, int num_tokens,
+                            int num_experts, int top_k, int num_ranks, void* stream) {
+  const char* fn = "moe_rank_layout_batched";
+  if (num_batches < 1 || num_batches > MOE_MAX_BATCHES || !batches)
+    return fail(MOE_ERR_INVALID, "%s: num_batches=%d not in [1, %d] (or NULL batches)", fn,
+                num_batches, MOE_MAX_BATCHES);
+  moe::RankLayoutBatches rb{};
+  for (int b = 0; b < num_batches; ++b) {
+    const moe_rank_layout_io& io = batches[b];
+    const int st = check_rank_layout(fn, num_tokens, num_experts, top_k, num_ranks, io.topk_idx,
+                                     io.rank_token_counts, io.rank_token_offsets, io.rank_row,
+                                     io.send_row, io.row_token, io.workspace,
+                                     io.workspace_bytes);
+    if (st != MOE_OK) return st;
+    rb.b[b] = moe::RankLayoutBatch{io.topk_idx, io.rank_token_counts, io.rank_token_offsets,
+                                   io.rank_row, io.send_row, io.row_token, io.workspace};
+  }
+  return from_hip(moe::launch_rank_layout_batches(num_batches, rb, num_tokens, num_experts,
+                                                  top_k, num_ranks,
+                                                  static_cast<hipStream_t>(stream)),
                   fn);
 }
 

@@ -430,6 +430,35 @@ int moe_rank_layout(int num_tokens, int num_experts, int top_k, int num_ranks,
                     void* stream);
 
 /*
+ * moe_rank_layout_batched -- moe_rank_layout on num_batches independent
+ * batches of the same sizes (each with its own routing, outputs and
+ * workspace), with one launch per pass for all of them. Each batch's results
+ * equal those of moe_rank_layout on it alone (hyper.ai story on Hybrid-EP,
+ * preallocated buffers). Sizes that need the scan pass (hundreds of tiles)
+ * run one scan launch per batch.
+ *
+ *   batches   HOST array of num_batches moe_rank_layout_io, read during the
+ *             call only; 1 <= num_batches <= MOE_MAX_BATCHES
+ * Every batch is validated as moe_rank_layout validates its arguments
+ * before anything is enqueued. Batches must not share outputs or
+ * workspaces.
+ */
+typedef struct {
+  const int32_t* topk_idx;      /* the arrays of moe_rank_layout, per batch */
+  int32_t* rank_token_counts;
+  int32_t* rank_token_offsets;
+  int32_t* rank_row;
+  int32_t* send_row;
+  int32_t* row_token;
+  void* workspace;
+  size_t workspace_bytes;
+} moe_rank_layout_io;
+
+int moe_rank_layout_batched(int num_batches, const moe_rank_layout_io* batches,
+                            int num_tokens, int num_experts, int top_k,
+                            int num_ranks, void* stream);
+
+/*
  * moe_expand -- on the receiving rank, copy each (token, rank) row to the
  * expert rows of that token on the rank:
  *

@@ -12,8 +12,8 @@
 //     below half a bf16 ulp);
 //   - the fanned-out (token, rank) rows equal the dispatched rows, and the
 //     two-level sum stays within two bf16 ulps of x;
-//   - the batched routing and layout give, per batch, what the single calls
-//     give;
+//   - the batched routing, layout and (token, rank) layout give, per batch,
+//     what the single calls give;
 //   - a call with bad arguments returns MOE_ERR_INVALID and names itself.
 // Prints "c-abi check ok" and exits 0 on success.
 
@@ -239,6 +239,38 @@ int main() {
     CHECK(i1 == one_i && d1 == one_d && s1 == one_s && e1 == one_e,
           "batch 1 equals its single calls");
     (void)one_w;
+    // batched (token, rank) layouts of both routings; batch 0 against the flat
+    // pass's rank_row, batch 1 against a single call on its routing (d_idx)
+    int32_t *d_rcntb[2], *d_roffb[2], *d_rrowb[2], *d_srowb[2], *d_rtokb[2];
+    void* d_rwsb[2];
+    for (int b = 0; b < 2; ++b) {
+      if (alloc(R, &d_rcntb[b]) || alloc(R + 1, &d_roffb[b]) || alloc(pairs, &d_rrowb[b]) ||
+          alloc(pairs, &d_srowb[b]) || alloc(nrr, &d_rtokb[b]))
+        return 1;
+      HIP_OK(hipMalloc(&d_rwsb[b], rws_bytes + 16));
+    }
+    moe_rank_layout_io rlio[2];
+    for (int b = 0; b < 2; ++b)
+      rlio[b] = moe_rank_layout_io{d_ib[b], d_rcntb[b], d_roffb[b], d_rrowb[b], d_srowb[b],
+                                   d_rtokb[b], d_rwsb[b], rws_bytes};
+    MOE_CALL(moe_rank_layout_batched(2, rlio, T, E, k, R, st));
+    MOE_CALL(moe_rank_layout(T, E, k, R, d_idx, d_rtc2, d_rto, d_rrow, d_srow, d_rtok, d_rws,
+                             rws_bytes, st));
+    HIP_OK(hipStreamSynchronize(st));
+    std::vector<int32_t> rr0, rr1, sr1, rt1, ro1, one_rr, one_sr, one_rt, one_ro;
+    if (to_host(d_rrowb[0], pairs, rr0) || to_host(d_rrowb[1], pairs, rr1) ||
+        to_host(d_srowb[1], pairs, sr1) || to_host(d_rtokb[1], nrr, rt1) ||
+        to_host(d_roffb[1], R + 1, ro1) || to_host(d_rrow, pairs, one_rr) ||
+        to_host(d_srow, pairs, one_sr) || to_host(d_rtok, nrr, one_rt) ||
+        to_host(d_rto, R + 1, one_ro))
+      return 1;
+    CHECK(rr0 == rrow, "batched rank layout 0 equals the flat pass's");
+    CHECK(rr1 == one_rr && sr1 == one_sr && rt1 == one_rt && ro1 == one_ro,
+          "batched rank layout 1 equals its single call");
+    for (int b = 0; b < 2; ++b) {
+      void* bb[] = {d_rcntb[b], d_roffb[b], d_rrowb[b], d_srowb[b], d_rtokb[b], d_rwsb[b]};
+      for (void* q : bb) HIP_OK(hipFree(q));
+    }
     const int bad_n = moe_route_batched(0, rio, T, E, k, MOE_SCORE_SOFTMAX, 1, 1, st);
     CHECK(bad_n == MOE_ERR_INVALID, "zero batches are rejected");
     HIP_OK(hipFree(d_logits1));

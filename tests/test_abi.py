@@ -425,6 +425,32 @@ def test_batched_calls_reject():
     assert L.moe_layout_batched(2, None, *largs) == M.MOE_ERR_INVALID
     assert M.moe_last_error().startswith("moe_layout_batched")
 
+    def rio(**kw):
+        d = dict(topk_idx=A16, rank_token_counts=A16, rank_token_offsets=A16, rank_row=A16,
+                 send_row=A16, row_token=A16, workspace=A16b, workspace_bytes=1 << 20)
+        d.update(kw)
+        return M.RankLayoutIO(*[d[f] for f, _ in M.RankLayoutIO._fields_])
+
+    ra = (M.RankLayoutIO * 3)(rio(), rio(), rio(send_row=None))
+    rargs = (16, 64, 4, 8, None)
+    assert L.moe_rank_layout_batched(3, ctypes.cast(ra, ctypes.c_void_p),
+                                     *rargs) == M.MOE_ERR_INVALID
+    assert M.moe_last_error().startswith("moe_rank_layout_batched")
+    ra[2] = rio(row_token=A16 + 2)                      # misaligned
+    assert L.moe_rank_layout_batched(3, ctypes.cast(ra, ctypes.c_void_p),
+                                     *rargs) == M.MOE_ERR_INVALID
+    ra[2] = rio(workspace_bytes=0)
+    assert L.moe_rank_layout_batched(3, ctypes.cast(ra, ctypes.c_void_p),
+                                     5000, 64, 4, 8, None) == M.MOE_ERR_WORKSPACE
+    ra[2] = rio()
+    assert L.moe_rank_layout_batched(3, ctypes.cast(ra, ctypes.c_void_p),
+                                     16, 64, 4, 6, None) == M.MOE_ERR_INVALID   # 6 ∤ 64
+    assert L.moe_rank_layout_batched(0, ctypes.cast(ra, ctypes.c_void_p),
+                                     *rargs) == M.MOE_ERR_INVALID
+    assert L.moe_rank_layout_batched(M.MOE_MAX_BATCHES + 1, ctypes.cast(ra, ctypes.c_void_p),
+                                     *rargs) == M.MOE_ERR_INVALID
+    assert L.moe_rank_layout_batched(2, None, *rargs) == M.MOE_ERR_INVALID
+
 
 def test_batch_limit_matches_the_header():
     with open(os.path.join(ROOT, "include", "moe.h")) as f:

@@ -1,8 +1,9 @@
-"""GPU parity of the batched entry points: moe_route_batched and
-moe_layout_batched give, for every batch, the bits that moe_route and
-moe_layout give on that batch alone (and hence the oracle's, which the
-single-call parity tests pin). Outputs are poisoned with a value the calls
-never write, and followed by guard entries."""
+"""GPU parity of the batched entry points: moe_route_batched,
+moe_layout_batched and moe_rank_layout_batched give, for every batch, the
+bits that moe_route, moe_layout and moe_rank_layout give on that batch alone
+(and hence the oracle's, which the single-call parity tests pin). Outputs
+are poisoned with a value the calls never write, and followed by guard
+entries."""
 
 import sys
 
@@ -138,6 +139,68 @@ def test_layout_batched_equals_single_calls(case):
                 assert np.array_equal(got[name], L[name].reshape(got[name].shape)), (case, b, name)
 
 
+class RankOut:
+    def __init__(self, t, e, k, r):
+        self.n = dict(rank_token_counts=r, rank_token_offsets=r + 1, rank_row=t * k,
+                      send_row=t * k, row_token=t * min(k, r))
+        self.bufs = {name: _ints(max(n, 1)) for name, n in self.n.items()}
+        self.wsb = M.moe_rank_layout_workspace_bytes(t, k, r)
+        self.ws = torch.empty(max(self.wsb, 4), dtype=torch.uint8, device="cuda")
+
+    def io(self, idx):
+        return dict(self.bufs, topk_idx=idx, workspace=self.ws, workspace_bytes=self.wsb)
+
+    def single(self, t, e, k, r, idx):
+        b = self.bufs
+        M.moe_rank_layout(t, e, k, r, idx, b["rank_token_counts"], b["rank_token_offsets"],
+                          b["rank_row"], b["send_row"], b["row_token"], self.ws, self.wsb)
+
+    def result(self):
+        out = {}
+        for name, n in self.n.items():
+            a = host(self.bufs[name])
+            assert (a[max(n, 1):] == POISON).all(), ("write past", name)
+            out[name] = a[:n]
+        return out
+
+
+RANK_CASES = [
+    # batches, T, E, k, R, mask fraction
+    (8, 4096, 256, 8, 8, 0.0),        # DeepSeek-V3 (token, rank) layout: count + place
+    (8, 128, 256, 8, 8, 0.0),         # decode steps: one tile each
+    (3, 16384, 8, 2, 8, 0.05),        # mixtral shape, masked slots
+    (2, 8192, 128, 8, 16, 0.1),       # qwen3 shape
+    (2, 70000, 64, 4, 64, 0.1),       # scan pass: one scan launch per batch
+    (1, 100, 6, 4, 3, 0.2),           # one batch, one tile
+    (3, 0, 8, 2, 4, 0.0),             # no tokens
+]
+
+
+@pytest.mark.parametrize("case", RANK_CASES, ids=lambda c: "nb%d_T%d_E%d_k%d_R%d" % c[:5])
+def test_rank_layout_batched_equals_single_calls(case):
+    nb, t, e, k, r, mf = case
+    say("batched rank layout", case)
+    g = W.rng(sum(case[:5]) + 11)
+    idx_h = [W.random_topk_idx(g, t, e, k, distinct=True, mask_frac=mf) for _ in range(nb)]
+    idx = [dev(a) if t > 0 else torch.empty(0, dtype=torch.int32, device="cuda")
+           for a in idx_h]
+    outs = [RankOut(t, e, k, r) for _ in range(nb)]
+    M.moe_rank_layout_batched(t, e, k, r, [outs[b].io(idx[b]) for b in range(nb)])
+    for b in range(nb):
+        got = outs[b].result()
+        one = RankOut(t, e, k, r)
+        one.single(t, e, k, r, idx[b])
+        want = one.result()
+        for name in want:
+            assert np.array_equal(got[name], want[name]), (case, b, name)
+    if 0 < t * k <= 40000:                     # and the oracle, on the first and last batch
+        for b in (0, nb - 1):
+            L = O.rank_layout(idx_h[b], e, r)
+            got = outs[b].result()
+            for name in got:
+                assert np.array_equal(got[name], L[name].reshape(got[name].shape)), (case, b, name)
+
+
 N_RANDOM = 40
 
 
@@ -161,8 +224,8 @@ def _draw(seed):
 
 @pytest.mark.parametrize("seed", range(N_RANDOM))
 def test_batched_random_shapes(seed):
-    """Seeded random shapes through both batched calls, each batch against
-    the single calls on the same inputs, bit for bit."""
+    """Seeded random shapes through the three batched calls, each batch
+    against the single calls on the same inputs, bit for bit."""
     c = _draw(seed)
     say("batched random case", c)
     nb, t, e, k, r, cap = c["nb"], c["T"], c["E"], c["k"], c["R"], c["cap"]
@@ -191,3 +254,11 @@ def test_batched_random_shapes(seed):
         want = one.result()
         for name in want:
             assert np.array_equal(got[name], want[name]), (c, b, name)
+    rk = [RankOut(t, e, k, r) for _ in range(nb)]
+    M.moe_rank_layout_batched(t, e, k, r, [rk[b].io(idx[b]) for b in range(nb)])
+    for b in range(nb):
+        one = RankOut(t, e, k, r)
+        one.single(t, e, k, r, idx[b])
+        got, want = rk[b].result(), one.result()
+        for name in want:
+            assert np.array_equal(got[name], want[name]), (c, b, "rank", name)
