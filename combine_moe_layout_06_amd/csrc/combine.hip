@@ -410,12 +410,13 @@ hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void
 
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
-                          hipStream_t stream, bool allow_held) {
+                          hipStream_t stream, bool allow_held, bool fine_items) {
   if (T == 0) return hipSuccess;
   const int nch = H / 8;
   if (allow_held && try_launch_held(T, nch, k, num_rows, y, dst_row, w, out, stream))
     return hipGetLastError();
-  int parts = T > 0 ? (kTargetWaves + T - 1) / T : 1;
+  const bool fine = fine_items && k == 8;
+  int parts = fine ? nch / MOE_WAVE : (kTargetWaves + T - 1) / T;
   parts = max(1, min(parts, nch / MOE_WAVE));
   int cpp = (nch + parts - 1) / parts;
   cpp = (cpp + MOE_WAVE - 1) / MOE_WAVE * MOE_WAVE;
@@ -426,7 +427,12 @@ hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
     case 2: launch_fixed<2, 4>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
     case 4: launch_fixed<4, 2>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
     case 6: launch_fixed<6, 1>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
-    case 8: launch_fixed<8, MOE_COMBINE_U8>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out); break;
+    case 8:
+      if (fine)
+        launch_fixed<8, 1>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out);
+      else
+        launch_fixed<8, MOE_COMBINE_U8>(grid, stream, T, nch, parts, cpp, num_rows, y, dst_row, w, out);
+      break;
     default:
       hipLaunchKernelGGL(combine_kernel_any_k, grid, dim3(256), 0, stream, T, k, nch, parts,
                          cpp, num_rows, static_cast<const u32x4*>(y), dst_row, w,

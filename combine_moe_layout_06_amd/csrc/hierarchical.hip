@@ -23,7 +23,8 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 constexpr int kExpandChunks = 8;   // 16-byte chunks in flight per lane
 // Workgroups per CU (occupancy caps, see lds_cap_bytes), measured on dsv3:
-// expand about 2% faster at 3, the partial combine about 2.5% at 2.
+// expand about 2% faster at 3; the partial combine (1 KiB items) 2% faster
+// at 2 than at 3, 28% faster than at 1.
 constexpr int kExpandBlocksPerCu = 3;
 constexpr int kCombineLocalBlocksPerCu = 2;
 
@@ -278,7 +279,11 @@ hipError_t launch_combine_local(int T, int H, int k, int num_rows, int num_rank_
                                 const float* w, void* partial, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int nch = H / 8;
-  int parts = (kTargetWaves + T - 1) / T;
+  // k = 8: items of 1 KiB (one 16-byte chunk per lane), as many parts as a
+  // row has. On the DeepSeek-V3 shape (rows of 14 KiB, about 7 partial rows
+  // per token) that took 160.1-160.6 us against 165-169 us with 2 KiB items
+  // (3 KiB: 168-170, 4 KiB: 166-170; same box, 20 back-to-back launches).
+  int parts = k == 8 ? nch / MOE_WAVE : (kTargetWaves + T - 1) / T;
   parts = max(1, min(parts, nch / MOE_WAVE));
   int cpp = (nch + parts - 1) / parts;
   cpp = (cpp + MOE_WAVE - 1) / MOE_WAVE * MOE_WAVE;
@@ -288,7 +293,7 @@ hipError_t launch_combine_local(int T, int H, int k, int num_rows, int num_rank_
     case 1: launch_local_fixed<1, 4>(grid, stream, T, nch, parts, cpp, num_rows, num_rank_rows, y, dst_row, rank_row, w, partial); break;
     case 2: launch_local_fixed<2, 4>(grid, stream, T, nch, parts, cpp, num_rows, num_rank_rows, y, dst_row, rank_row, w, partial); break;
     case 4: launch_local_fixed<4, 2>(grid, stream, T, nch, parts, cpp, num_rows, num_rank_rows, y, dst_row, rank_row, w, partial); break;
-    case 8: launch_local_fixed<8, 2>(grid, stream, T, nch, parts, cpp, num_rows, num_rank_rows, y, dst_row, rank_row, w, partial); break;
+    case 8: launch_local_fixed<8, 1>(grid, stream, T, nch, parts, cpp, num_rows, num_rank_rows, y, dst_row, rank_row, w, partial); break;
     default:
       hipLaunchKernelGGL(combine_local_kernel_any_k, grid, dim3(256), 0, stream, T, k, nch,
                          parts, cpp, num_rows, num_rank_rows, static_cast<const u32x4*>(y),

@@ -105,10 +105,13 @@ hipError_t launch_dispatch_mxfp8(int T, int H, int k, int num_rows, const void* 
                                  hipStream_t stream);
 
 // w == nullptr means unit weights (the gradient of dispatch). allow_held:
-// the held-output kernel may serve the shapes it is chosen for.
+// the held-output kernel may serve the shapes it is chosen for. fine_items:
+// the per-item kernel at k = 8 takes items of 1 KiB (one 16-byte chunk per
+// lane), as many parts as a row has.
 hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
                           const int32_t* dst_row, const float* w, void* out,
-                          hipStream_t stream, bool allow_held = true);
+                          hipStream_t stream, bool allow_held = true,
+                          bool fine_items = false);
 
 // Fan-out of the (token, rank) rows to the expert rows, and the per-rank
 // partial combine.

@@ -207,6 +207,9 @@ LOCAL_CASES = [
     (90, 18, 6, 3, 2, 64),         # k = 6 with drops
     (40, 8, 1, 2, 0, 72),          # k = 1, hidden not a multiple of 512
     (128, 256, 8, 32, 128, 7168),  # decode shape
+    (200, 64, 8, 8, 0, 2880),      # k = 8 items of 1 KiB: 3 parts, the last one ragged
+    (77, 64, 8, 16, 5, 1000),      # k = 8, one part shorter than a wave's chunk step
+    (33, 16, 8, 4, 0, 8),          # k = 8, one 16-byte chunk per row
     (0, 8, 2, 4, 0, 64),           # empty
 ]
 
@@ -234,10 +237,22 @@ def test_hierarchical_combine_parity(case):
     say("  partials and outputs equal the oracle's bits")
 
 
-def test_combine_partials_parity():
+PARTIAL_CASES = [
+    # T, E, k, R, H
+    (500, 64, 8, 16, 384),
+    (1000, 256, 8, 32, 7168),      # k = 8 items of 1 KiB: 14 parts
+    (300, 64, 8, 8, 2880),         # 3 parts, the last one ragged
+    (77, 32, 8, 4, 1000),          # one part shorter than a wave's chunk step
+    (33, 16, 8, 4, 8),             # one 16-byte chunk per row
+    (200, 24, 6, 6, 512),          # k = 6
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=lambda c: "T%d_E%d_k%d_R%d_H%d" % c)
+def test_combine_partials_parity(case):
     """Second level alone on synthetic partial rows."""
-    g = W.rng(77)
-    t, e, k, r, h = 500, 64, 8, 16, 384
+    t, e, k, r, h = case
+    g = W.rng(77 + sum(case))
     idx = W.random_topk_idx(g, t, e, k, mask_frac=0.1)
     rl = O.rank_layout(idx, e, r)
     nrr = rl["num_rank_rows"]
