@@ -9,25 +9,27 @@
 // sections "Megatron-LM (NVIDIA)" and "Défis et optimisations" (capacity
 // and token dropping).
 //
-// Two launches (one when all pairs fit in one tile: layout_one_tile_kernel,
-// three for many tiles), no global atomics, deterministic:
-//   1. count: one block per tile of whole tokens builds the tile's expert
-//      histogram (and per-rank distinct-token counts) in LDS and writes it
-//      to the workspace.
-//   2. place: every block sums the histogram columns of the tiles before it
-//      (its per-expert base) and of all tiles (totals), scans the totals
-//      into offsets, and gives each pair its stable row. Inside a wave, the
-//      pairs of one expert are found with one ballot per expert-id bit and
-//      ranked by their lane order; waves of a tile are chained through LDS.
-// Every place block reads the whole [tiles, E] histogram (8192 ints per
-// staging pass), so the pass grows with tiles^2 * E over the grid: one
-// staging pass up to 8192 / E tiles (32 for E = 256, 1024 for E = 8). For
-// many tiles a scan pass between the two (layout_scan_kernel) rewrites the
-// histogram as per-tile bases plus totals, and each place block reads only
-// its own row: linear in tiles * E.
+// Two launches (one when all pairs fit in one tile of 1024 pairs, three for
+// hundreds of tiles), no global atomics, deterministic:
+//   1. count (layout_count_kernel): one block per tile of whole tokens
+//      builds the tile's expert histogram (and per-rank distinct-token
+//      counts) in LDS and writes it to the workspace.
+//   2. place (layout_wide_kernel): one 1024-thread block per tile, one pair
+//      per thread. Every block adds the histogram rows of the tiles before it
+//      (its per-expert base) and of all tiles (totals), scans the totals into
+//      offsets, and gives each pair its stable row. Inside a wave, the pairs
+//      of one expert are found with one ballot per expert-id bit and ranked
+//      by their lane order; the waves of a tile are chained through LDS. With
+//      one tile the block counts the pairs itself and no count pass runs.
+// Every place block reads the whole [tiles, E] histogram, so that pass grows
+// with tiles^2 * E over the grid. From 256 tiles, or past 16384 histogram
+// entries, a scan pass between the two (layout_scan_kernel) rewrites the
+// histogram as per-tile bases plus totals, and 256-thread place blocks
+// (layout_place_kernel) read only their own row: linear in tiles * E.
 //
-// Also here: the (token, rank) rows of the deduplicated dispatch
-// (rank_count_kernel, rank_place_kernel), and the fused layout + dispatch
+// Also here: the (token, rank) rows of the deduplicated dispatch, placed the
+// same way with the rank as the key (rank_count_kernel, rank_wide_kernel;
+// rank_place_kernel after the scan pass), and the fused layout + dispatch
 // launch for decode-sized inputs in capacity mode (layout_dispatch_kernel).
 
 #include "dispatch_body.h"
@@ -161,38 +163,6 @@ __device__ int block_exclusive_scan(int* s, int n, int* s_wave) {
   }
   __syncthreads();
   return total;
-}
-
-// Load n ints of `src` (n <= kStage) into registers, all in flight at once.
-__device__ __forceinline__ void stage_load(int (&h)[kStage / kThreads], const int32_t* src, int n) {
-#pragma unroll
-  for (int q = 0; q < kStage / kThreads; ++q) {
-    const int i = q * kThreads + threadIdx.x;
-    h[q] = i < n ? src[i] : 0;
-  }
-}
-__device__ __forceinline__ void stage_store(const int (&h)[kStage / kThreads], int* s_stage) {
-#pragma unroll
-  for (int q = 0; q < kStage / kThreads; ++q) s_stage[q * kThreads + threadIdx.x] = h[q];
-}
-
-// Sum column c of a row-major [rows, W] matrix whose flat elements
-// [c0, c0 + n) are staged in s_stage; rows below `limit` also go to *pre.
-__device__ __forceinline__ void column_sums(const int* s_stage, int c0, int n, int W, int c,
-                                            int limit, int* tot, int* pre) {
-  int t = 0, p = 0;
-  // rows b with c0 <= b*W + c < c0 + n; eight LDS reads in flight at a time
-  const int b0 = (c0 + W - 1 - c) / W;
-  const int nb = c0 + n - c > 0 ? (c0 + n - c + W - 1) / W - b0 : 0;
-#pragma unroll 8
-  for (int i = 0; i < nb; ++i) {
-    const int b = b0 + i;
-    const int x = s_stage[b * W + c - c0];
-    t += x;
-    p += b < limit ? x : 0;
-  }
-  *tot += t;
-  *pre += p;
 }
 
 // Column scan of the per-tile histograms, for many tiles. Matrix `a`
@@ -826,17 +796,26 @@ __global__ __launch_bounds__(kThreads) void rank_count_kernel(
   for (int r = tid; r < R; r += kThreads) ws_rhist[(size_t)tile * R + r] = s_rhist[r];
 }
 
-// ntiles == 1 (all pairs in one tile, one block): the block counts its own
-// pairs and no count pass runs. Otherwise one block per tile. scanned: the
-// scan pass has run; the workspace holds the base of every tile, then the
-// totals. Batch blockIdx.y.
+// The rank at the token's first slot on it for pair p of a tile (the key
+// of the (token, rank) row the pair stands for), else -1; *first = that
+// first slot (-1 for a masked slot). s_rank holds the ranks of the tile's
+// pairs.
+__device__ __forceinline__ int rank_key(const int* s_rank, int p, int k, int* first) {
+  const int tl = p / k, j = p - tl * k;
+  *first = first_slot_of_rank(s_rank + tl * k, j);
+  return *first == j ? s_rank[p] : -1;
+}
+
+// Place pass for many tiles (after the scan pass): one 256-thread block per
+// tile reads its tile's base row and the totals from the workspace. Batch
+// blockIdx.y.
 __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     int T, int E, int k, int R, int epr, int epr_shift, int tt, int ntiles, int max_rows,
-    int scanned, const RankLayoutBatches rb) {
+    const RankLayoutBatches rb) {
   const RankLayoutBatch& bt = rb.b[blockIdx.y];
   const int32_t* __restrict__ idx = bt.idx;
-  const int32_t* __restrict__ ws_rhist = static_cast<const int32_t*>(bt.workspace);
-  const int32_t* __restrict__ ws_tot = scanned ? ws_rhist + (size_t)ntiles * R : nullptr;
+  const int32_t* __restrict__ ws_base = static_cast<const int32_t*>(bt.workspace);
+  const int32_t* __restrict__ ws_tot = ws_base + (size_t)ntiles * R;
   int32_t* __restrict__ counts = bt.counts;
   int32_t* __restrict__ offsets = bt.offsets;
   int32_t* __restrict__ rank_row = bt.rank_row;
@@ -844,20 +823,17 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
   int32_t* __restrict__ row_token = bt.row_token;
   __shared__ int s_tot[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
-  __shared__ int s_pre[MOE_MAX_EXPERTS];
   __shared__ int s_cnt[kWaves][MOE_MAX_EXPERTS];
   __shared__ int s_base[kWaves][MOE_MAX_EXPERTS];
   __shared__ int s_wave[kWaves];
   __shared__ int s_rank[kTilePairs];
   __shared__ int s_row[kTilePairs];
-  __shared__ int s_stage[kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
   const int tok0 = tile * tt;
   const int np = tile < ntiles ? min(tt, T - tok0) * k : 0;
   const size_t pair0 = (size_t)tok0 * k;
-  const bool self_count = ntiles <= 1;
 
   int v[kChunks];
 #pragma unroll
@@ -865,27 +841,10 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
     const int p = (wave * kChunks + c) * MOE_WAVE + lane;
     v[c] = p < np ? idx[pair0 + p] : -1;
   }
-  // after the scan pass the block reads its own base row and the totals
-  const int hist_n = self_count || scanned ? 0 : ntiles * R;
-  int h[kStage / kThreads];
-  stage_load(h, ws_rhist, min(kStage, hist_n));
-  constexpr int kPerThread = MOE_MAX_EXPERTS / kThreads;
-  int pre0[kPerThread], tot0[kPerThread];
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const int r = q * kThreads + tid;
-    pre0[q] = scanned && r < R ? ws_rhist[(size_t)tile * R + r] : 0;
-    tot0[q] = scanned && r < R ? ws_tot[r] : 0;
-  }
-
-#pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
-    const int r = q * kThreads + tid;
-    if (r < R) {
-      s_tot[r] = tot0[q];
-      s_pre[r] = pre0[q];
-      for (int w = 0; w < kWaves; ++w) s_cnt[w][r] = 0;
-    }
+  for (int r = tid; r < R; r += kThreads) {
+    s_tot[r] = ws_tot[r];
+    s_off[r] = ws_tot[r];
+    for (int w = 0; w < kWaves; ++w) s_cnt[w][r] = 0;
   }
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
@@ -895,41 +854,18 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
   }
   __syncthreads();
 
-  // key: the rank at the token's first slot on it, else -1
   int key[kChunks], first[kChunks];
+  uint64_t peers[kChunks];
+  const int nbits = ceil_log2(R);
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int p = (wave * kChunks + c) * MOE_WAVE + lane;
     key[c] = -1;
     first[c] = -1;
-    if (p < np) {
-      const int tl = p / k, j = p - tl * k;
-      first[c] = first_slot_of_rank(s_rank + tl * k, j);
-      if (first[c] == j) key[c] = s_rank[p];
-    }
-    if (self_count && key[c] >= 0) atomicAdd(&s_tot[key[c]], 1);
-  }
-  // per-wave ranking of the keys needs no histogram: it runs while the
-  // histogram loads are in flight
-  const int nbits = ceil_log2(R);
-  uint64_t peers[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
+    if (p < np) key[c] = rank_key(s_rank, p, k, &first[c]);
     peers[c] = peer_mask((uint32_t)key[c], key[c] >= 0, nbits);
     if (key[c] >= 0 && count_below(peers[c]) == 0) atomicAdd(&s_cnt[wave][key[c]], __popcll(peers[c]));
   }
-
-  for (int c0 = 0; c0 < hist_n; c0 += kStage) {
-    const int n = min(kStage, hist_n - c0);
-    if (c0 > 0) stage_load(h, ws_rhist + c0, n);
-    __syncthreads();
-    stage_store(h, s_stage);
-    __syncthreads();
-    for (int r = tid; r < R; r += kThreads) column_sums(s_stage, c0, n, R, r, tile, &s_tot[r], &s_pre[r]);
-  }
-  __syncthreads();
-  for (int r = tid; r < R; r += kThreads) s_off[r] = s_tot[r];
-  __syncthreads();
   const int total = block_exclusive_scan(s_off, R, s_wave);
   if (tid == 0) s_off[R] = total;
   __syncthreads();
@@ -938,11 +874,10 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
       counts[r] = s_tot[r];
       offsets[r] = s_off[r];
     }
-    if (tid == 0) offsets[R] = s_off[R];
+    if (tid == 0) offsets[R] = total;
   }
-
   for (int r = tid; r < R; r += kThreads) {
-    int run = s_pre[r];
+    int run = ws_base[(size_t)tile * R + r];
     for (int w = 0; w < kWaves; ++w) {
       s_base[w][r] = run;
       run += s_cnt[w][r];
@@ -972,8 +907,119 @@ __global__ __launch_bounds__(kThreads) void rank_place_kernel(
 
   // rows past the last (token, rank) row are marked -1
   const int gwave = tile * kWaves + wave, nwaves = gridDim.x * kWaves;
-  for (int row = s_off[R] + gwave * MOE_WAVE + lane; row < max_rows; row += nwaves * MOE_WAVE)
+  for (int row = total + gwave * MOE_WAVE + lane; row < max_rows; row += nwaves * MOE_WAVE)
     row_token[row] = -1;
+}
+
+// Place pass in 1024-thread blocks, one pair per thread, one block per tile:
+// the expert layout's wide place pass with the (token, rank) key.
+//   - SELF (all pairs in one tile, no count pass ran): the block counts its
+//     keys from the per-wave counts; the layout is a single launch.
+//   - otherwise rank_count_kernel has written the per-tile counts [ntiles, R]
+//     and every block adds all rows (its totals) and the rows before its tile
+//     (its base), one LDS atomic per nonzero entry, all loads in flight at
+//     once. Used while ntiles * R fits kWideHistLoads loads per thread.
+// Block 0 writes the counts and offsets; the waves of the grid mark the rows
+// past the last one. Batch blockIdx.y.
+template <bool SELF>
+__global__ __launch_bounds__(kWideThreads) void rank_wide_kernel(
+    int T, int E, int k, int R, int epr, int epr_shift, int tt, int ntiles, int max_rows,
+    int r_shift, const RankLayoutBatches rb) {
+  const RankLayoutBatch& bt = rb.b[blockIdx.y];
+  const int32_t* __restrict__ idx = bt.idx;
+  const int32_t* __restrict__ ws_rhist = static_cast<const int32_t*>(bt.workspace);
+  int32_t* __restrict__ row_token = bt.row_token;
+  __shared__ int s_cnt[kWideWaves][MOE_MAX_EXPERTS];
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_pre[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_rank[kTilePairs];
+  __shared__ int s_row[kTilePairs];
+  __shared__ int s_wave[kWideWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x;
+  const int tok0 = tile * tt;
+  const int np = tile < ntiles ? min(tt, T - tok0) * k : 0;
+  const size_t pair0 = (size_t)tok0 * k;
+  const int raw = tid < np ? idx[pair0 + tid] : -1;
+  const int hist_n = SELF ? 0 : ntiles * R;
+  int h[kWideHistLoads];
+#pragma unroll
+  for (int j = 0; j < kWideHistLoads; ++j) {
+    const int i = j * kWideThreads + tid;
+    h[j] = i < hist_n ? ws_rhist[i] : 0;
+  }
+  if (tid < R) {
+    for (int w = 0; w < kWideWaves; ++w) s_cnt[w][tid] = 0;
+    s_tot[tid] = 0;
+    s_pre[tid] = 0;
+  }
+  const int e = clean_expert(raw, E);
+  if (tid < np) s_rank[tid] = e >= 0 ? rank_of(e, epr, epr_shift) : -1;
+  __syncthreads();
+
+#pragma unroll
+  for (int j = 0; j < kWideHistLoads; ++j) {
+    const int i = j * kWideThreads + tid;
+    if (h[j] != 0) {
+      const int row = row_of(i, R, r_shift), col = i - row * R;
+      atomicAdd(&s_tot[col], h[j]);
+      if (row < tile) atomicAdd(&s_pre[col], h[j]);
+    }
+  }
+  // the wave's keys of one rank (one ballot per rank-id bit); the lowest
+  // lane of each stores their number
+  int first = -1;
+  const int key = tid < np ? rank_key(s_rank, tid, k, &first) : -1;
+  const uint64_t peers = peer_mask((uint32_t)key, key >= 0, ceil_log2(R));
+  const int below = count_below(peers);
+  if (key >= 0 && below == 0) s_cnt[wave][key] = __popcll(peers);
+  __syncthreads();
+
+  // chain the waves: s_cnt[w][r] becomes the first row of wave w's keys of
+  // rank r inside the rank's region (after the tiles before)
+  if (tid < R) {
+    int c[kWideWaves];
+#pragma unroll
+    for (int w = 0; w < kWideWaves; ++w) c[w] = s_cnt[w][tid];
+    int run = s_pre[tid];
+#pragma unroll
+    for (int w = 0; w < kWideWaves; ++w) {
+      s_cnt[w][tid] = run;
+      run += c[w];
+    }
+    if (SELF) s_tot[tid] = run;
+    s_off[tid] = SELF ? run : s_tot[tid];
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan_wide(s_off, R, s_wave);
+  if (tid == 0) s_off[R] = total;
+  __syncthreads();
+  if (tile == 0) {
+    if (tid < R) {
+      bt.counts[tid] = s_tot[tid];
+      bt.offsets[tid] = s_off[tid];
+    }
+    if (tid == 0) bt.offsets[R] = total;
+  }
+
+  int row = -1;
+  if (key >= 0) {
+    row = s_off[key] + s_cnt[wave][key] + below;
+    if (row < max_rows) row_token[row] = tok0 + tid / k;
+  }
+  if (tid < np) {
+    s_row[tid] = row;
+    bt.send_row[pair0 + tid] = row;
+  }
+  __syncthreads();
+  if (tid < np) bt.rank_row[pair0 + tid] = first >= 0 ? s_row[(tid / k) * k + first] : -1;
+
+  // rows past the last (token, rank) row are marked -1
+  const int gwave = tile * kWideWaves + wave, nwaves = gridDim.x * kWideWaves;
+  for (int r = total + gwave * MOE_WAVE + lane; r < max_rows; r += nwaves * MOE_WAVE)
+    row_token[r] = -1;
 }
 
 }  // namespace
@@ -1099,27 +1145,34 @@ hipError_t launch_rank_layout_batches(int nb, const RankLayoutBatches& rb, int T
   const int ntiles = layout_num_tiles(T, k);
   const int epr = E / R;
   const int epr_shift = (epr & (epr - 1)) == 0 ? __builtin_ctz(epr) : -1;
+  const int r_shift = (R & (R - 1)) == 0 ? __builtin_ctz(R) : -1;
   const int max_rows = T * (k < R ? k : R);
-  const bool scan = ntiles > 1 && layout_scans(ntiles, R);
-  if (ntiles > 1) {
-    hipLaunchKernelGGL(rank_count_kernel, dim3(ntiles, nb), dim3(kThreads), 0, stream,
-                       T, E, k, R, epr, epr_shift, tt, rb);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // the scan pass is rare (hundreds of tiles): one launch per batch
-    for (int b = 0; scan && b < nb; ++b) {
-      int32_t* ws = static_cast<int32_t*>(rb.b[b].workspace);
-      hipLaunchKernelGGL(layout_scan_kernel, dim3((R + kScanCols - 1) / kScanCols),
-                         dim3(kScanThreads), 0, stream, ntiles, R,
-                         (R + kScanCols - 1) / kScanCols, ws, ws + (size_t)ntiles * R, 0,
-                         static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
-    }
+  if (ntiles <= 1) {
+    hipLaunchKernelGGL(rank_wide_kernel<true>, dim3(1, nb), dim3(kWideThreads), 0, stream, T, E,
+                       k, R, epr, epr_shift, tt, ntiles, max_rows, r_shift, rb);
+    return hipGetLastError();
   }
-  const int blocks = ntiles > 1 ? ntiles : 1;
-  hipLaunchKernelGGL(rank_place_kernel, dim3(blocks, nb), dim3(kThreads), 0, stream, T, E, k,
-                     R, epr, epr_shift, tt, ntiles, max_rows, scan ? 1 : 0, rb);
+  hipLaunchKernelGGL(rank_count_kernel, dim3(ntiles, nb), dim3(kThreads), 0, stream,
+                     T, E, k, R, epr, epr_shift, tt, rb);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (!layout_scans(ntiles, R)) {
+    hipLaunchKernelGGL(rank_wide_kernel<false>, dim3(ntiles, nb), dim3(kWideThreads), 0, stream,
+                       T, E, k, R, epr, epr_shift, tt, ntiles, max_rows, r_shift, rb);
+    return hipGetLastError();
+  }
+  // hundreds of tiles: a scan pass per batch, then the 256-thread place pass
+  for (int b = 0; b < nb; ++b) {
+    int32_t* ws = static_cast<int32_t*>(rb.b[b].workspace);
+    hipLaunchKernelGGL(layout_scan_kernel, dim3((R + kScanCols - 1) / kScanCols),
+                       dim3(kScanThreads), 0, stream, ntiles, R,
+                       (R + kScanCols - 1) / kScanCols, ws, ws + (size_t)ntiles * R, 0,
+                       static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(rank_place_kernel, dim3(ntiles, nb), dim3(kThreads), 0, stream, T, E, k, R,
+                     epr, epr_shift, tt, ntiles, max_rows, rb);
   return hipGetLastError();
 }
 
