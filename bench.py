@@ -680,7 +680,7 @@ def ceilings(torch, np):
 
 CPU_REPS = 5              # repeats of each CPU-baseline leg (median reported)
 CPU_SINGLE_TOKENS = 256   # tokens of the single-thread leg's sample
-CPU_MAX_WORKERS = 16      # the GPU machine's CPU share per GPU
+CPU_MAX_WORKERS = 16      # worker processes at most: the host's CPU share per GPU
 
 
 def cpu_baseline_phases(w, seed, lo, hi, dtype, reps, barrier=None):

@@ -3,7 +3,7 @@
 // in the path calls them).
 //
 // The path moves rows between HBM buffers in three patterns, and each kernel
-// is judged against the best a plain kernel reaches with the same pattern on
+// is measured against the best a plain kernel reaches with the same pattern on
 // the same chip:
 //   copy     sequential 16-byte reads and writes of one buffer into another
 //            (the plain device-to-device copy);

@@ -13,12 +13,13 @@ def pytest_configure(config):
 
 def pytest_sessionfinish(session, exitstatus):
     """Write the combine cases checked bit for bit in this session (name and
-    element count) to gpurun_out/combine_exactness.txt when that folder
-    exists."""
+    element count) to combine_exactness.txt in the folder that the
+    MOE_TEST_LOG_DIR environment variable names, when it is set and the
+    folder exists."""
     helpers = sys.modules.get("gpu_helpers")
     log = getattr(helpers, "EXACT_LOG", None)
-    out_dir = os.path.join(ROOT, "gpurun_out")
-    if not log or not os.path.isdir(out_dir):
+    out_dir = os.environ.get("MOE_TEST_LOG_DIR", "")
+    if not log or not out_dir or not os.path.isdir(out_dir):
         return
     total = sum(n for _, n in log)
     with open(os.path.join(out_dir, "combine_exactness.txt"), "w") as f:

@@ -12,8 +12,8 @@ Acceptance rules (derived from the arithmetic of each step):
     bf16, so the GPU's bits must equal the oracle's. (The contract's bound is
     one bf16 ulp; the failure message reports the largest distance in ulps.)
     Every checked case is recorded with its element count, and the session
-    writes the list to gpurun_out/combine_exactness.txt when that folder
-    exists.
+    writes the list to combine_exactness.txt in the folder MOE_TEST_LOG_DIR
+    names (when set).
 """
 
 from __future__ import annotations

@@ -127,6 +127,6 @@ extern "C" int convert_sweep(void* res, void* stream) {
 }
 
 // The two references on the host, so that CPU tests can check them against
-// the oracle's codecs before they judge the device.
+// the oracle's codecs before they check the device.
 extern "C" uint32_t convert_ref_bf16(uint32_t u) { return ref_bf16(u); }
 extern "C" uint32_t convert_ref_e4m3(uint32_t u) { return ref_e4m3(u); }

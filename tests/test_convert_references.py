@@ -1,5 +1,5 @@
 """The integer rounding references of tests/hip/convert_sweep.hip (which
-judge the hardware converts on the device) checked on the host against the
+check the hardware converts on the device) checked on the host against the
 oracle's codecs: every finite bf16 pattern times a range of multipliers for
 e4m3, e4m3 midpoints, saturation, subnormals and zeros, and random fp32
 patterns over the whole exponent range for both formats (CPU only)."""
