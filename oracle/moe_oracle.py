@@ -476,11 +476,11 @@ def fma_f32(a, b, c) -> np.ndarray:
     a64 = np.asarray(a, dtype=F32).astype(F64)
     b64 = np.asarray(b, dtype=F32).astype(F64)
     c64 = np.asarray(c, dtype=F32).astype(F64)
-    p = a64 * b64
-    s = p + c64
-    bv = s - p
-    e = (p - (s - bv)) + (c64 - bv)
-    with np.errstate(over="ignore", invalid="ignore"):
+    with np.errstate(over="ignore", invalid="ignore"):   # inf and nan inputs propagate
+        p = a64 * b64
+        s = p + c64
+        bv = s - p
+        e = (p - (s - bv)) + (c64 - bv)
         r = s.astype(F32)
         r64 = r.astype(F64)
         side = np.where(s > r64, np.float32(np.inf), np.float32(-np.inf))
