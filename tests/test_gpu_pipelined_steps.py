@@ -132,14 +132,16 @@ def test_pipelined_steps_equal_serial_steps(name, steps, group, lead):
     say("  graph replays equal the serial steps")
 
 
-def test_pipelined_hierarchical_steps_equal_serial_steps():
+@pytest.mark.parametrize("group,lead,steps", [(2, 2, 5), (16, 8, 21)])
+def test_pipelined_hierarchical_steps_equal_serial_steps(group, lead, steps):
     """The hierarchical pass pipelined the same way (route, expert layout and
     (token, rank) layout of a group beside the send, fan-out and combines of
-    the group before), replayed from a graph, against the same steps run one
-    after the other: each set's (token, rank) layout of the last step that
-    used it, and the last step's partials and output."""
+    the group before; the bench's shape is groups of 16 after a first group
+    of 8, fronts in batched calls of 8), replayed from a graph, against the
+    same steps run one after the other: each set's (token, rank) layout of
+    the last step that used it, and the last step's partials and output."""
     w = W.WORKLOADS["dsv3"]
-    group, steps = 2, 5
+    say("pipelined hierarchical steps x", steps, "in groups of", group, "after a first of", lead)
     inputs = []
     for s in range(steps):
         inp = W.make_inputs(w, 10 + s)
@@ -168,7 +170,7 @@ def test_pipelined_hierarchical_steps_equal_serial_steps():
     with torch.cuda.graph(graph):
         bench.pipelined(torch, lambda pairs: bench.hierarchical_fronts(w, sets, inputs, pairs),
                         lambda i, s: bench.hierarchical_back(sets, inputs, y, i, s),
-                        2 * group, steps, side, group)
+                        2 * group, steps, side, group, lead)
     for rep in range(2):
         for lb, rb in sets:
             rb.send_row.fill_(-7)
@@ -177,7 +179,7 @@ def test_pipelined_hierarchical_steps_equal_serial_steps():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for i in range(steps - 2 * group, steps):              # the last user of each set
+        for i in range(max(0, steps - 2 * group), steps):      # the last user of each set
             assert torch.equal(sets[i % (2 * group)][1].send_row, want_send[i]), (rep, i)
         assert torch.equal(lb0.combined, want[0]), rep
         assert torch.equal(rb0.partial[:n_sent], want[1]), rep
