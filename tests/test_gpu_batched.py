@@ -173,6 +173,9 @@ RANK_CASES = [
     (2, 70000, 64, 4, 64, 0.1),       # scan pass: one scan launch per batch
     (1, 100, 6, 4, 3, 0.2),           # one batch, one tile
     (3, 0, 8, 2, 4, 0.0),             # no tokens
+    (3, 300, 512, 32, 512, 0.05),     # maximum sizes: one expert per rank, k = 32
+    (8, 2000, 512, 32, 16, 0.0),      # k = 32, 63 tiles, every batch slot used
+    (4, 1001, 12, 3, 3, 0.1),         # R not a power of two, ragged last tile
 ]
 
 
