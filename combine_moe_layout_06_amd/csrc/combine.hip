@@ -28,9 +28,6 @@ constexpr int kWavesPerBlock = 4;
 // Workgroups per CU for the fixed-k combine (measured on dsv3, qwen3_skew
 // and mixtral shapes: 3 is 1-3% faster than the 5-8 the registers allow).
 constexpr int kCombineBlocksPerCu = 3;
-// Workgroups per CU for the combine backward (one block per token): 4 is
-// about 1.5% faster on dsv3 than uncapped.
-constexpr int kCombineBackwardBlocksPerCu = 4;
 
 #ifndef MOE_COMBINE_U8
 #define MOE_COMBINE_U8 2   // 16-byte chunks per lane per step when k = 8
@@ -285,7 +282,11 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
 // of the row (kBwdChunks 16-byte chunks per lane per group). Its dout chunks
 // stay in registers while it walks the k rows; each pair's dot product is
 // reduced in the wave and the four waves' partial sums are added in wave
-// order, so the result is deterministic.
+// order, so the result is deterministic. Two launches of the same kernel:
+// DW reads the expert rows and writes dw, DY writes the dy rows. Apart, each
+// runs at its own access pattern's ceiling (reads only: 77.7 us on the
+// DeepSeek-V3 shape; fan-out: 106 us); fused, the mix of random-row reads and
+// writes took 193-194 us against 183-184 us for the two.
 // ---------------------------------------------------------------------------
 constexpr int kBwdChunks = 4;
 
@@ -306,6 +307,7 @@ __device__ __forceinline__ u32x4 scale_row(const u32x4& g, float w) {
   return r;
 }
 
+template <bool DY, bool DW>
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     int T, int k, int nch, int num_rows, const u32x4* __restrict__ dout,
     const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
@@ -338,21 +340,23 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
       for (int u = 0; u < kBwdChunks; ++u) {
         const int c = c0 + u * MOE_WAVE + lane;
         v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (c < nch) v[u] = stream_load(y_row + c);
+        if (DW && c < nch) v[u] = stream_load(y_row + c);
       }
       float part = 0.0f;
 #pragma unroll
       for (int u = 0; u < kBwdChunks; ++u) {
         const int c = c0 + u * MOE_WAVE + lane;
-        part = dot8(g[u], v[u], part);
-        if (c < nch) stream_store(scale_row(g[u], wj), dy_row + c);
+        if (DW) part = dot8(g[u], v[u], part);
+        if (DY && c < nch) stream_store(scale_row(g[u], wj), dy_row + c);
       }
-      const float sum = wave_sum_f32(part);
-      if (lane == 0) s_part[wave][j] += sum;
+      if (DW) {
+        const float sum = wave_sum_f32(part);
+        if (lane == 0) s_part[wave][j] += sum;
+      }
     }
   }
   __syncthreads();
-  if (wave == 0 && lane < k) {
+  if (DW && wave == 0 && lane < k) {
     float acc = 0.0f;
 #pragma unroll
     for (int v = 0; v < kWavesPerBlock; ++v) acc += s_part[v][lane];
@@ -413,9 +417,14 @@ hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void
                                    const void* y, const int32_t* dst_row, const float* w,
                                    void* dy, float* dw, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(T), dim3(256),
-                     lds_cap_bytes(kCombineBackwardBlocksPerCu), stream, T, k, H / 8, num_rows, static_cast<const u32x4*>(dout), static_cast<const u32x4*>(y),
-                     dst_row, w, static_cast<u32x4*>(dy), dw);
+  const auto* g = static_cast<const u32x4*>(dout);
+  const auto* yr = static_cast<const u32x4*>(y);
+  hipLaunchKernelGGL((combine_backward_kernel<false, true>), dim3(T), dim3(256), 0, stream, T, k,
+                     H / 8, num_rows, g, yr, dst_row, w, static_cast<u32x4*>(dy), dw);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((combine_backward_kernel<true, false>), dim3(T), dim3(256), 0, stream, T, k,
+                     H / 8, num_rows, g, yr, dst_row, w, static_cast<u32x4*>(dy), dw);
   return hipGetLastError();
 }
 
