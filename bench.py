@@ -68,6 +68,10 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_traffic.json")
 COMBINE_SOURCES = [os.path.join(ROOT, "combine_moe_layout_06_amd", "csrc", f)
                    for f in ("combine.hip", "wave.h", "kernels.h")]
+HIER_SOURCES = [os.path.join(ROOT, "combine_moe_layout_06_amd", "csrc", f)
+                for f in ("hierarchical.hip", "wave.h", "kernels.h")]
+# counter records of the other passes' roofline kernels (combine_local, combine_backward)
+KERNEL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "roofline_traffic.json")
 ROOF_REPS = 20   # back-to-back launches timed for the roofline kernel
 
 
@@ -218,7 +222,9 @@ def run_backward(args, w, M, W, torch, np):
         "cache_eviction": EVICTION,
         "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_kernel_traffic("combine_backward", COMBINE_SOURCES,
+                                                    nb["combine_backward"]),
                      "algorithmic_bytes_per_launch": nb["combine_backward"],
                      "launch_us": round(cb_us, 2), "timing": roofline_timing()},
         "cpu_baseline": None}), flush=True)
@@ -416,7 +422,8 @@ def run_hierarchical(args, w, M, W, torch, np):
                             "hierarchical": n_sent * row + n_sent * H * 2},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_kernel_traffic(dom, HIER_SOURCES, nb[dom]),
                      "algorithmic_bytes_per_launch": nb[dom],
                      "launch_us": round(dom_us, 2), "timing": roofline_timing()},
         "cpu_baseline": None}
@@ -485,6 +492,23 @@ def load_traffic(algorithmic_bytes):
     if d.get("algorithmic_bytes_per_launch") != algorithmic_bytes:
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def load_kernel_traffic(kernel, sources, algorithmic_bytes):
+    """HBM bytes per call of `kernel` from the committed counter records, or
+    None when there is no record of it taken on the current source of
+    `sources` for a workload with these algorithmic bytes."""
+    try:
+        with open(KERNEL_TRAFFIC_FILE) as f:
+            recs = json.load(f)
+    except (OSError, ValueError):
+        return None
+    sha = sha_of(sources)
+    for d in recs if isinstance(recs, list) else []:
+        if (d.get("kernel") == kernel and d.get("kernel_source_sha256") == sha
+                and d.get("algorithmic_bytes_per_launch") == algorithmic_bytes):
+            return d.get("traffic_bytes_per_launch")
+    return None
 
 
 def calibrate_copy():

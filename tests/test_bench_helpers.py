@@ -87,6 +87,43 @@ def test_committed_traffic_record_describes_the_dsv3_combine():
     assert rec["algorithmic_bytes_per_launch"] == bench.step_bytes(w, w.tokens * w.top_k)["combine"]
 
 
+def test_kernel_traffic_records_follow_kernel_source_and_workload(tmp_path, monkeypatch):
+    src = _write(tmp_path, "h.hip", "__global__ void k() { y += 1; }\n")
+    recs = [{"kernel": "combine_local", "kernel_source_sha256": bench.sha_of([src]),
+             "algorithmic_bytes_per_launch": 500, "traffic_bytes_per_launch": 510},
+            {"kernel": "combine_backward", "kernel_source_sha256": bench.sha_of([src]),
+             "algorithmic_bytes_per_launch": 900, "traffic_bytes_per_launch": 950}]
+    monkeypatch.setattr(bench, "KERNEL_TRAFFIC_FILE", _write(tmp_path, "r.json", json.dumps(recs)))
+    assert bench.load_kernel_traffic("combine_local", [src], 500) == 510
+    assert bench.load_kernel_traffic("combine_backward", [src], 900) == 950
+    assert bench.load_kernel_traffic("combine_local", [src], 900) is None     # other workload
+    assert bench.load_kernel_traffic("expand", [src], 500) is None            # no record
+    _write(tmp_path, "h.hip", "__global__ void k() { y += 2; }\n")            # code edit
+    assert bench.load_kernel_traffic("combine_local", [src], 500) is None
+    monkeypatch.setattr(bench, "KERNEL_TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.load_kernel_traffic("combine_backward", [src], 900) is None
+
+
+def test_committed_kernel_traffic_records_describe_the_dsv3_passes():
+    """The records of the hierarchical and backward passes' roofline kernels
+    carry the bench's own algorithmic bytes for the DeepSeek-V3 shape, and
+    their traffic stays within a few percent of them."""
+    with open(bench.KERNEL_TRAFFIC_FILE) as f:
+        recs = {d["kernel"]: d for d in json.load(f)}
+    w = W.WORKLOADS["dsv3"]
+    rows = w.tokens * w.top_k
+    want = {"combine_local": (bench.HIER_SOURCES, None),
+            "combine_backward": (bench.COMBINE_SOURCES,
+                                 bench.backward_bytes(w, rows)["combine_backward"])}
+    for kernel, (sources, alg) in want.items():
+        d = recs[kernel]
+        if d["kernel_source_sha256"] != bench.sha_of(sources):
+            pytest.skip("the %s code changed since its HBM counters were taken" % kernel)
+        if alg is not None:
+            assert d["algorithmic_bytes_per_launch"] == alg
+        assert 1.0 <= d["traffic_bytes_per_launch"] / d["algorithmic_bytes_per_launch"] < 1.08
+
+
 def test_launch_flags(monkeypatch):
     """Default: graph replay, pipelining decided later (None: it follows the
     launch mode); --eager, --serial and --overlap override."""
