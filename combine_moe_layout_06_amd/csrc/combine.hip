@@ -278,17 +278,17 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
 // Backward of combine: for each live pair (t, j) with row d = dst_row[t, j]
 //   dy[d, :] = bf16( w[t, j] * dout[t, :] )
 //   dw[t, j] = sum_h dout[t, h] * y[d, h]        (fp32)
-// One 256-thread block per token; wave v covers chunk groups v, v + 4, ...
-// of the row (kBwdChunks 16-byte chunks per lane per group). Its dout chunks
-// stay in registers while it walks the k rows; each pair's dot product is
-// reduced in the wave and the four waves' partial sums are added in wave
-// order, so the result is deterministic. Two launches of the same kernel:
-// DW reads the expert rows and writes dw, DY writes the dy rows. Apart, each
-// runs at its own access pattern's ceiling (reads only: 77.7 us on the
-// DeepSeek-V3 shape; fan-out: 106 us); fused, the mix of random-row reads and
-// writes took 193-194 us against 183-184 us for the two.
+// Two launches, each at its own access pattern's ceiling: the dw launch only
+// reads (the expert rows and dout), the dy launch only fans dout out. In one
+// kernel the random-row reads and writes mixed at 5.0 TB/s (193-194 us on
+// the DeepSeek-V3 shape); apart they take 77.7 us (6.8 TB/s) and 99 us.
 // ---------------------------------------------------------------------------
 constexpr int kBwdChunks = 4;
+// dy launch: 1 KiB pieces, workgroups per CU (measured on the DeepSeek-V3
+// shape, dy launch with the dw launch: 177.0-177.7 us at 5, 177.4-179.4 at 6,
+// 182.6-182.8 at 4, 184.6-185.2 at 8, 183.9-185.3 uncapped; one 256-thread
+// block per token with 4 KiB pieces: 183.0-184.5)
+constexpr int kBwdDyBlocksPerCu = 5;
 
 __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
 #pragma unroll
@@ -307,16 +307,18 @@ __device__ __forceinline__ u32x4 scale_row(const u32x4& g, float w) {
   return r;
 }
 
-template <bool DY, bool DW>
-__global__ __launch_bounds__(256) void combine_backward_kernel(
+// dw: one 256-thread block per token; wave v covers chunk groups v, v + 4,
+// ... of the row (kBwdChunks 16-byte chunks per lane per group). Its dout
+// chunks stay in registers while it walks the k rows; each pair's dot
+// product is reduced in the wave and the four waves' partial sums are added
+// in wave order, so the result is deterministic.
+__global__ __launch_bounds__(256) void combine_backward_dw_kernel(
     int T, int k, int nch, int num_rows, const u32x4* __restrict__ dout,
-    const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
-    const float* __restrict__ w, u32x4* __restrict__ dy, float* __restrict__ dw) {
+    const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row, float* __restrict__ dw) {
   __shared__ float s_part[kWavesPerBlock][MOE_MAX_TOPK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x;
   const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
   if (lane < k) s_part[wave][lane] = 0.0f;
   const u32x4* g_row = dout + (size_t)t * nch;
   constexpr int kGroup = MOE_WAVE * kBwdChunks;
@@ -332,35 +334,49 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     for (int j = 0; j < k; ++j) {
       const int d = read_lane(my_dst, j);
       if (d < 0 || d >= num_rows) continue;
-      const float wj = read_lane(my_w, j);
       const u32x4* y_row = y + (size_t)d * nch;
-      u32x4* dy_row = dy + (size_t)d * nch;
       u32x4 v[kBwdChunks];
 #pragma unroll
       for (int u = 0; u < kBwdChunks; ++u) {
         const int c = c0 + u * MOE_WAVE + lane;
         v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (DW && c < nch) v[u] = stream_load(y_row + c);
+        if (c < nch) v[u] = stream_load(y_row + c);
       }
       float part = 0.0f;
 #pragma unroll
-      for (int u = 0; u < kBwdChunks; ++u) {
-        const int c = c0 + u * MOE_WAVE + lane;
-        if (DW) part = dot8(g[u], v[u], part);
-        if (DY && c < nch) stream_store(scale_row(g[u], wj), dy_row + c);
-      }
-      if (DW) {
-        const float sum = wave_sum_f32(part);
-        if (lane == 0) s_part[wave][j] += sum;
-      }
+      for (int u = 0; u < kBwdChunks; ++u) part = dot8(g[u], v[u], part);
+      const float sum = wave_sum_f32(part);
+      if (lane == 0) s_part[wave][j] += sum;
     }
   }
   __syncthreads();
-  if (DW && wave == 0 && lane < k) {
+  if (wave == 0 && lane < k) {
     float acc = 0.0f;
 #pragma unroll
     for (int v = 0; v < kWavesPerBlock; ++v) acc += s_part[v][lane];
     dw[(size_t)t * k + lane] = (my_dst >= 0 && my_dst < num_rows) ? acc : 0.0f;
+  }
+}
+
+// dy: one wave per (token, 1 KiB piece of the row): the piece of dout in
+// one 16-byte chunk per lane, scaled and written to each of the token's rows.
+__global__ __launch_bounds__(256) void combine_backward_dy_kernel(
+    int T, int k, int nch, int parts, int num_rows, const u32x4* __restrict__ dout,
+    const int32_t* __restrict__ dst_row, const float* __restrict__ w, u32x4* __restrict__ dy) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= T * parts) return;
+  const int t = gw / parts;
+  const int c = (gw - t * parts) * MOE_WAVE + lane;
+  const int my_dst = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
+  u32x4 g = u32x4{0u, 0u, 0u, 0u};
+  if (c < nch) g = stream_load(dout + (size_t)t * nch + c);
+  for (int j = 0; j < k; ++j) {
+    const int d = read_lane(my_dst, j);
+    if (d < 0 || d >= num_rows) continue;
+    const float wj = read_lane(my_w, j);
+    if (c < nch) stream_store(scale_row(g, wj), dy + (size_t)d * nch + c);
   }
 }
 
@@ -417,14 +433,18 @@ hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void
                                    const void* y, const int32_t* dst_row, const float* w,
                                    void* dy, float* dw, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  const int nch = H / 8;
   const auto* g = static_cast<const u32x4*>(dout);
-  const auto* yr = static_cast<const u32x4*>(y);
-  hipLaunchKernelGGL((combine_backward_kernel<false, true>), dim3(T), dim3(256), 0, stream, T, k,
-                     H / 8, num_rows, g, yr, dst_row, w, static_cast<u32x4*>(dy), dw);
+  hipLaunchKernelGGL(combine_backward_dw_kernel, dim3(T), dim3(256), 0, stream, T, k, nch,
+                     num_rows, g, static_cast<const u32x4*>(y), dst_row, dw);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((combine_backward_kernel<true, false>), dim3(T), dim3(256), 0, stream, T, k,
-                     H / 8, num_rows, g, yr, dst_row, w, static_cast<u32x4*>(dy), dw);
+  const int parts = (nch + MOE_WAVE - 1) / MOE_WAVE;
+  const long long waves = (long long)T * parts;
+  hipLaunchKernelGGL(combine_backward_dy_kernel,
+                     dim3((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(256),
+                     lds_cap_bytes(kBwdDyBlocksPerCu), stream, T, k, nch, parts, num_rows, g,
+                     dst_row, w, static_cast<u32x4*>(dy));
   return hipGetLastError();
 }
 
