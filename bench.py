@@ -671,7 +671,7 @@ def ceilings(torch, np):
                                             ("shuffle", 2, 14336, (128, 256, 896))):
         rows = n // row_bytes
         perm = torch.from_numpy(gen.permutation(rows).astype(np.int32)).cuda()
-        cfgs = [(p, pc) for p in pieces for pc in (0, 1, 2, 3, 4)]
+        cfgs = [(p, pc) for p in pieces for pc in (0, 1, 2, 3, 4, 5, 6)]
         g, c = best(2 * rows * row_bytes, cfgs,
                     lambda p, pc: L.ceil_rows(gather, a.data_ptr(), b.data_ptr(),
                                               perm.data_ptr(), rows, row_bytes, p, pc, stream))
@@ -681,7 +681,7 @@ def ceilings(torch, np):
                                           ("rwrite", 1, 7168, (64, 448))):
         rows = n // row_bytes
         perm = torch.from_numpy(gen.permutation(rows).astype(np.int32)).cuda()
-        cfgs = [(p, pc) for p in pieces for pc in (0, 2, 3, 4)]
+        cfgs = [(p, pc) for p in pieces for pc in (0, 2, 3, 4, 5, 6)]
         g, c = best(rows * row_bytes, cfgs,
                     lambda p, pc: L.ceil_rows_one_way(mode, a.data_ptr(), b.data_ptr(),
                                                       perm.data_ptr(), rows, row_bytes, p, pc,
@@ -691,7 +691,7 @@ def ceilings(torch, np):
     row_bytes, k = 7168, 8
     rows = n // (row_bytes * k)
     perm = torch.from_numpy(gen.permutation(rows * k).astype(np.int32)).cuda()
-    cfgs = [(p, pc) for p in (64, 128, 256, 448) for pc in (0, 1, 2, 3, 4)]
+    cfgs = [(p, pc) for p in (64, 128, 256, 448) for pc in (0, 1, 2, 3, 4, 5, 6)]
     g, c = best(rows * row_bytes * (1 + k), cfgs,
                 lambda p, pc: L.ceil_fanout(a.data_ptr(), b.data_ptr(), perm.data_ptr(), rows, k,
                                             row_bytes, p, pc, stream))
