@@ -13,16 +13,17 @@ namespace moe {
 namespace {
 
 // Workgroups per CU (occupancy caps, see lds_cap_bytes), measured on the
-// dsv3, mixtral and qwen3_skew shapes: bf16 with k <= 2 runs about 3% faster
-// at 4, and MXFP8 best uncapped. The row-held FP8 kernel: 4 or 5 (53.4, 53.2
-// us on dsv3), 3: 57.0, 2: 61.0, uncapped: 53.7. bf16 with k > 2 takes 1 KiB
-// pieces (below) at 5: on qwen3_skew (k = 8, 8 KiB rows) 111.2-111.9 us
-// against 120.6-121.5 with 2 KiB pieces uncapped; caps 4 and 6: 113-114, 2
-// and 3: 131-134, 8: 120-121. For k = 2 the same pieces needed cap 8 and
-// gained 1% on mixtral, so k <= 2 keeps its larger pieces.
+// dsv3, mixtral and qwen3_skew shapes: MXFP8 runs best uncapped; the row-held
+// FP8 kernel at 4 or 5 (53.4, 53.2 us on dsv3), 3: 57.0, 2: 61.0, uncapped:
+// 53.7. The bf16 dispatch takes 1 KiB pieces (below); with few rows per
+// token each wave writes less, so it needs more waves: on qwen3_skew (k = 8,
+// 8 KiB rows) 111.2-111.9 us at 5 against 120.6-121.5 with 2 KiB pieces
+// uncapped (caps 4 and 6: 113-114, 2 and 3: 131-134, 8: 120-121); on
+// mixtral (k = 2) 67.0-68.2 us at 8 against 68.5-69.0 with 4 KiB pieces at 4
+// (1 KiB pieces at 6: 70.2-71.7, at 4: 88.0-88.7).
 constexpr int kFp8RowsBlocksPerCu = 4;
-constexpr int kBf16FewBlocksPerCu = 4;
-constexpr int kBf16ManyBlocksPerCu = 5;
+constexpr int kBf16FewBlocksPerCu = 8;    // k <= 2
+constexpr int kBf16ManyBlocksPerCu = 5;   // k > 2
 // Steps (8 blocks of 128 columns) per row-held FP8 wave at most.
 constexpr int kFp8RowMaxSteps = 8;
 // Row-held kernels split a row into more parts while T * parts stays below
@@ -128,10 +129,9 @@ hipError_t launch_dispatch_bf16(int T, int H, int k, int num_rows, const void* x
   if (T == 0) return hipSuccess;
   const int nch = H / 8;
   int parts, cpp;
-  // k > 2: pieces of one 16-byte chunk per lane (1 KiB), as many parts as a
-  // row has; each wave then writes k short pieces, and the cap keeps about
-  // 20 waves per CU in flight
-  split_row(T, nch, MOE_WAVE, k > 2 ? MOE_WAVE : 1 << 30, &parts, &cpp);
+  // pieces of one 16-byte chunk per lane (1 KiB), as many parts as a row
+  // has; each wave writes k short pieces
+  split_row(T, nch, MOE_WAVE, MOE_WAVE, &parts, &cpp);
   const int waves = T * parts;
   hipLaunchKernelGGL(dispatch_bf16_kernel, dim3((waves + kWavesPerBlock - 1) / kWavesPerBlock),
                      dim3(256), lds_cap_bytes(k <= 2 ? kBf16FewBlocksPerCu : kBf16ManyBlocksPerCu),
