@@ -1165,7 +1165,8 @@ def main():
     achieved = nbytes["combine"] / (comb_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "kernel": "combine", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(nbytes["combine"]),
+            "traffic": (load_traffic(nbytes["combine"])
+                        or load_kernel_traffic("combine", COMBINE_SOURCES, nbytes["combine"])),
             "algorithmic_bytes_per_launch": nbytes["combine"],
             "launch_us": round(comb_us, 2), "timing": roofline_timing()}
 

@@ -109,7 +109,7 @@ def test_committed_kernel_traffic_records_describe_the_dsv3_passes():
     carry the bench's own algorithmic bytes for the DeepSeek-V3 shape, and
     their traffic stays within a few percent of them."""
     with open(bench.KERNEL_TRAFFIC_FILE) as f:
-        recs = {d["kernel"]: d for d in json.load(f)}
+        recs = {d["kernel"]: d for d in json.load(f) if d["workload_key"] == "dsv3"}
     w = W.WORKLOADS["dsv3"]
     rows = w.tokens * w.top_k
     want = {"combine_local": (bench.HIER_SOURCES, None),
@@ -122,6 +122,24 @@ def test_committed_kernel_traffic_records_describe_the_dsv3_passes():
         if alg is not None:
             assert d["algorithmic_bytes_per_launch"] == alg
         assert 1.0 <= d["traffic_bytes_per_launch"] / d["algorithmic_bytes_per_launch"] < 1.08
+
+
+def test_committed_combine_records_of_other_workloads():
+    """The mixtral and qwen3_skew combine records carry the bench's own
+    algorithmic combine bytes of their workload, so the forward bench line
+    of each finds its record, and their traffic is within a few percent."""
+    with open(bench.KERNEL_TRAFFIC_FILE) as f:
+        recs = {d["workload_key"]: d for d in json.load(f) if d["kernel"] == "combine"}
+    assert set(recs) == {"mixtral", "qwen3_skew"}
+    for name, d in recs.items():
+        if d["kernel_source_sha256"] != bench.sha_of(bench.COMBINE_SOURCES):
+            pytest.skip("the combine code changed since its HBM counters were taken")
+        w = W.WORKLOADS[name]
+        alg = bench.step_bytes(w, w.tokens * w.top_k)["combine"]
+        assert d["algorithmic_bytes_per_launch"] == alg
+        assert bench.load_kernel_traffic("combine", bench.COMBINE_SOURCES, alg) \
+            == d["traffic_bytes_per_launch"]
+        assert 1.0 <= d["traffic_bytes_per_launch"] / alg < 1.02
 
 
 def test_launch_flags(monkeypatch):
