@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
     L.moe_rank_layout.restype = i32
     L.moe_expand.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp]
     L.moe_expand.restype = i32
-    L.moe_combine_local.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.moe_combine_local.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp]
     L.moe_combine_local.restype = i32
     L.moe_combine_partials.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
     L.moe_combine_partials.restype = i32
@@ -330,10 +330,11 @@ def moe_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, rank_rows, rank_
 
 
 def moe_combine_local(num_tokens, hidden, top_k, num_rows, expert_out_bf16, dst_row, rank_row,
-                      topk_weights, num_rank_rows, partial_bf16, stream=None) -> None:
+                      row_token, topk_weights, num_rank_rows, partial_bf16, stream=None) -> None:
     _check(lib().moe_combine_local(num_tokens, hidden, top_k, num_rows, _ptr(expert_out_bf16),
-                                   _ptr(dst_row), _ptr(rank_row), _ptr(topk_weights),
-                                   num_rank_rows, _ptr(partial_bf16), _stream(stream)))
+                                   _ptr(dst_row), _ptr(rank_row), _ptr(row_token),
+                                   _ptr(topk_weights), num_rank_rows, _ptr(partial_bf16),
+                                   _stream(stream)))
 
 
 def moe_combine_partials(num_tokens, hidden, top_k, num_rank_rows, partial_bf16, send_row,

@@ -218,8 +218,8 @@ class RankBuffers:
 
     def combine_local(self, layer: LayerBuffers, expert_out, stream=None):
         moe_combine_local(self.tokens, self.hidden, self.top_k, layer.num_rows, expert_out,
-                          layer.dst_row, self.rank_row, layer.topk_weights, self.num_rank_rows,
-                          self.partial, stream)
+                          layer.dst_row, self.rank_row, self.row_token, layer.topk_weights,
+                          self.num_rank_rows, self.partial, stream)
 
     def combine_partials(self, out, stream=None):
         moe_combine_partials(self.tokens, self.hidden, self.top_k, self.num_rank_rows,

@@ -121,7 +121,8 @@ hipError_t launch_expand(int T, int H, int k, int dtype, int num_rank_rows, cons
                          hipStream_t stream);
 hipError_t launch_combine_local(int T, int H, int k, int num_rows, int num_rank_rows,
                                 const void* y, const int32_t* dst_row, const int32_t* rank_row,
-                                const float* w, void* partial, hipStream_t stream);
+                                const int32_t* row_token, const float* w, void* partial,
+                                hipStream_t stream);
 
 hipError_t launch_combine_backward(int T, int H, int k, int num_rows, const void* dout,
                                    const void* y, const int32_t* dst_row, const float* w,

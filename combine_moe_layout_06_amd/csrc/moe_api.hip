@@ -569,23 +569,27 @@ int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_ro
 
 int moe_combine_local(int num_tokens, int hidden, int top_k, int num_rows,
                       const void* expert_out_bf16, const int32_t* dst_row,
-                      const int32_t* rank_row, const float* topk_weights, int num_rank_rows,
-                      void* partial_bf16, void* stream) {
+                      const int32_t* rank_row, const int32_t* row_token,
+                      const float* topk_weights, int num_rank_rows, void* partial_bf16,
+                      void* stream) {
   const char* fn = "moe_combine_local";
   int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
   if (st != MOE_OK) return st;
   if (num_rank_rows < 0) return fail(MOE_ERR_INVALID, "%s: num_rank_rows=%d < 0", fn, num_rank_rows);
   if (num_tokens > 0 && (!dst_row || !rank_row || !topk_weights))
     return fail(MOE_ERR_INVALID, "%s: NULL dst_row/rank_row/topk_weights", fn);
+  if (num_rank_rows > 0 && !row_token) return fail(MOE_ERR_INVALID, "%s: NULL row_token", fn);
   if (num_rows > 0 && !expert_out_bf16) return fail(MOE_ERR_INVALID, "%s: NULL expert_out", fn);
   if (num_rank_rows > 0 && !partial_bf16) return fail(MOE_ERR_INVALID, "%s: NULL partial", fn);
   if (!aligned(expert_out_bf16, 16) || !aligned(partial_bf16, 16))
     return fail(MOE_ERR_INVALID, "%s: expert_out and partial must be 16-byte aligned", fn);
-  if (!aligned(dst_row, 4) || !aligned(rank_row, 4) || !aligned(topk_weights, 4))
+  if (!aligned(dst_row, 4) || !aligned(rank_row, 4) || !aligned(row_token, 4) ||
+      !aligned(topk_weights, 4))
     return fail(MOE_ERR_INVALID, "%s: index/weight buffers must be 4-byte aligned", fn);
   return from_hip(moe::launch_combine_local(num_tokens, hidden, top_k, num_rows, num_rank_rows,
-                                            expert_out_bf16, dst_row, rank_row, topk_weights,
-                                            partial_bf16, static_cast<hipStream_t>(stream)),
+                                            expert_out_bf16, dst_row, rank_row, row_token,
+                                            topk_weights, partial_bf16,
+                                            static_cast<hipStream_t>(stream)),
                   fn);
 }
 

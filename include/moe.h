@@ -488,17 +488,22 @@ int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_ro
  *                         and a kept expert row of w[t,j] * y[dst_row[t,j], :] )
  *
  * in fp32 fused multiply-adds, slot order inside the row, one rounding to
- * bf16 (nearest even). A row whose pairs were all dropped by capacity is
- * written as +0. Rows of `partial` that no token owns are left untouched.
+ * bf16 (nearest even), where t = row_token[s]. A row whose pairs were all
+ * dropped by capacity is written as +0. Rows whose row_token is -1 (past
+ * the last row) are left untouched. The rows are visited in their own
+ * order, each rank's rows one after the other, as the receiving rank would
+ * reduce them.
  *   expert_out [num_rows, hidden] bf16;  dst_row [T, k] from moe_layout
- *   rank_row   [T, k] from moe_rank_layout;  topk_weights [T, k] fp32
+ *   rank_row   [T, k] and row_token [num_rank_rows], both from the same
+ *              moe_rank_layout call;  topk_weights [T, k] fp32
  *   partial    [num_rank_rows, hidden] bf16
  * Requires hidden % 8 == 0.
  */
 int moe_combine_local(int num_tokens, int hidden, int top_k, int num_rows,
                       const void* expert_out_bf16, const int32_t* dst_row,
-                      const int32_t* rank_row, const float* topk_weights, int num_rank_rows,
-                      void* partial_bf16, void* stream);
+                      const int32_t* rank_row, const int32_t* row_token,
+                      const float* topk_weights, int num_rank_rows, void* partial_bf16,
+                      void* stream);
 
 /*
  * moe_combine_partials -- second level: each token sums its partial rows,

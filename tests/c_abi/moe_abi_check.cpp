@@ -172,7 +172,7 @@ int main() {
   HIP_OK(hipMemsetAsync(d_rows, 0xFF, (size_t)rows * H * 2, st));
   MOE_CALL(moe_expand(T, H, k, MOE_DTYPE_BF16, nrr, d_sent, nullptr, d_rrow, rows, d_src, d_rows,
                       nullptr, st));
-  MOE_CALL(moe_combine_local(T, H, k, rows, d_rows, d_dst, d_rrow, d_w, nrr, d_part, st));
+  MOE_CALL(moe_combine_local(T, H, k, rows, d_rows, d_dst, d_rrow, d_rtok, d_w, nrr, d_part, st));
   MOE_CALL(moe_combine_partials(T, H, k, nrr, d_part, d_srow, d_out, st));
   HIP_OK(hipStreamSynchronize(st));
   std::vector<int32_t> rtc, rtc2, rrow;

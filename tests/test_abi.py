@@ -322,6 +322,8 @@ def test_expand_rejects(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(H=12), M.MOE_ERR_INVALID),
     (dict(rr=None), M.MOE_ERR_INVALID),
+    (dict(rt=None), M.MOE_ERR_INVALID),
+    (dict(rt=A16 + 2), M.MOE_ERR_INVALID),
     (dict(w=None), M.MOE_ERR_INVALID),
     (dict(part=None), M.MOE_ERR_INVALID),
     (dict(nrr=-3), M.MOE_ERR_INVALID),
@@ -329,10 +331,11 @@ def test_expand_rejects(kw, status):
 ])
 def test_combine_local_rejects(kw, status):
     _no_gpu()
-    a = dict(T=4, H=256, k=2, rows=8, y=A16, dst=A16, rr=A16, w=A16, nrr=8, part=A16b)
+    a = dict(T=4, H=256, k=2, rows=8, y=A16, dst=A16, rr=A16, rt=A16, w=A16, nrr=8, part=A16b)
     a.update(kw)
     assert M.lib().moe_combine_local(a["T"], a["H"], a["k"], a["rows"], a["y"], a["dst"],
-                                     a["rr"], a["w"], a["nrr"], a["part"], None) == status
+                                     a["rr"], a["rt"], a["w"], a["nrr"], a["part"],
+                                     None) == status
     assert M.moe_last_error().startswith("moe_combine_local")
 
 
