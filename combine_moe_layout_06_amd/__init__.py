@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
     L.moe_rank_layout_workspace_bytes.restype = sz
     L.moe_rank_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_rank_layout.restype = i32
-    L.moe_expand.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp]
+    L.moe_expand.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     L.moe_expand.restype = i32
     L.moe_combine_local.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp]
     L.moe_combine_local.restype = i32
@@ -323,10 +323,10 @@ def moe_rank_layout(num_tokens, num_experts, top_k, num_ranks, topk_idx, rank_to
 
 
 def moe_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, rank_rows, rank_scales,
-               rank_row, num_rows, src_pair, out, out_scales, stream=None) -> None:
+               rank_row, row_token, num_rows, dst_row, out, out_scales, stream=None) -> None:
     _check(lib().moe_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, _ptr(rank_rows),
-                            _ptr(rank_scales), _ptr(rank_row), num_rows, _ptr(src_pair),
-                            _ptr(out), _ptr(out_scales), _stream(stream)))
+                            _ptr(rank_scales), _ptr(rank_row), _ptr(row_token), num_rows,
+                            _ptr(dst_row), _ptr(out), _ptr(out_scales), _stream(stream)))
 
 
 def moe_combine_local(num_tokens, hidden, top_k, num_rows, expert_out_bf16, dst_row, rank_row,

@@ -213,8 +213,8 @@ class RankBuffers:
     def expand(self, layer: LayerBuffers, stream=None):
         """Fan the sent rows out to the expert rows of `layer`."""
         moe_expand(self.tokens, self.hidden, self.top_k, self.dtype, self.num_rank_rows,
-                   self.sent, self.sent_scales, self.rank_row, layer.num_rows, layer.src_pair,
-                   layer.dispatched, layer.scales, stream)
+                   self.sent, self.sent_scales, self.rank_row, self.row_token, layer.num_rows,
+                   layer.dst_row, layer.dispatched, layer.scales, stream)
 
     def combine_local(self, layer: LayerBuffers, expert_out, stream=None):
         moe_combine_local(self.tokens, self.hidden, self.top_k, layer.num_rows, expert_out,

@@ -116,9 +116,9 @@ hipError_t launch_combine(int T, int H, int k, int num_rows, const void* y,
 // Fan-out of the (token, rank) rows to the expert rows, and the per-rank
 // partial combine.
 hipError_t launch_expand(int T, int H, int k, int dtype, int num_rank_rows, const void* src,
-                         const void* src_scales, const int32_t* rank_row, int num_rows,
-                         const int32_t* src_pair, void* out, void* out_scales,
-                         hipStream_t stream);
+                         const void* src_scales, const int32_t* rank_row,
+                         const int32_t* row_token, int num_rows, const int32_t* dst_row,
+                         void* out, void* out_scales, hipStream_t stream);
 hipError_t launch_combine_local(int T, int H, int k, int num_rows, int num_rank_rows,
                                 const void* y, const int32_t* dst_row, const int32_t* rank_row,
                                 const int32_t* row_token, const float* w, void* partial,

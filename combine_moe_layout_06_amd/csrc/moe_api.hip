@@ -529,8 +529,8 @@ int moe_rank_layout_batched(int num_batches, const moe_rank_layout_io* batches, 
 
 int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_rows,
                const void* rank_rows, const void* rank_scales, const int32_t* rank_row,
-               int num_rows, const int32_t* src_pair, void* out, void* out_scales,
-               void* stream) {
+               const int32_t* row_token, int num_rows, const int32_t* dst_row, void* out,
+               void* out_scales, void* stream) {
   const char* fn = "moe_expand";
   int st = check_rows(fn, num_tokens, hidden, top_k, num_rows);
   if (st != MOE_OK) return st;
@@ -545,10 +545,11 @@ int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_ro
   if (mx && hidden % MOE_MX_BLOCK != 0)
     return fail(MOE_ERR_INVALID, "%s: MXFP8 needs hidden %% %d == 0 (hidden=%d)", fn,
                 MOE_MX_BLOCK, hidden);
-  if (num_rows > 0 && (!src_pair || !out))
-    return fail(MOE_ERR_INVALID, "%s: NULL src_pair/out", fn);
-  if (num_rows > 0 && num_tokens > 0 && !rank_row)
-    return fail(MOE_ERR_INVALID, "%s: NULL rank_row", fn);
+  if (num_rows > 0 && !out) return fail(MOE_ERR_INVALID, "%s: NULL out", fn);
+  if (num_rows > 0 && num_tokens > 0 && (!rank_row || !dst_row))
+    return fail(MOE_ERR_INVALID, "%s: NULL rank_row/dst_row", fn);
+  if (num_rank_rows > 0 && num_rows > 0 && !row_token)
+    return fail(MOE_ERR_INVALID, "%s: NULL row_token", fn);
   if (num_rank_rows > 0 && num_rows > 0 && !rank_rows)
     return fail(MOE_ERR_INVALID, "%s: NULL rank_rows", fn);
   if ((fp8 || mx) && num_rows > 0 && (!out_scales || (num_rank_rows > 0 && !rank_scales)))
@@ -558,12 +559,12 @@ int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_ro
   if (!aligned(rank_rows, 16) || !aligned(out, 16))
     return fail(MOE_ERR_INVALID, "%s: rank_rows and out must be 16-byte aligned", fn);
   const bool words = fp8 || (mx && (hidden / MOE_MX_BLOCK) % 4 == 0);
-  if (!aligned(rank_row, 4) || !aligned(src_pair, 4) ||
+  if (!aligned(rank_row, 4) || !aligned(row_token, 4) || !aligned(dst_row, 4) ||
       (words && (!aligned(rank_scales, 4) || !aligned(out_scales, 4))))
     return fail(MOE_ERR_INVALID, "%s: index and scale buffers must be 4-byte aligned", fn);
   return from_hip(moe::launch_expand(num_tokens, hidden, top_k, dtype, num_rank_rows, rank_rows,
-                                     rank_scales, rank_row, num_rows, src_pair, out, out_scales,
-                                     static_cast<hipStream_t>(stream)),
+                                     rank_scales, rank_row, row_token, num_rows, dst_row, out,
+                                     out_scales, static_cast<hipStream_t>(stream)),
                   fn);
 }
 

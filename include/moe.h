@@ -460,25 +460,29 @@ int moe_rank_layout_batched(int num_batches, const moe_rank_layout_io* batches,
 
 /*
  * moe_expand -- on the receiving rank, copy each (token, rank) row to the
- * expert rows of that token on the rank:
+ * expert rows of that token on the rank: for every row s with
+ * t = row_token[s] >= 0 and every slot j of t with rank_row[t,j] = s,
  *
- *   out[q] = rank_rows[rank_row[src_pair[q]]]     for rows q with a pair
+ *   out[dst_row[t,j]] = rank_rows[s]          when 0 <= dst_row[t,j] < num_rows
  *
  * (payload and, for FP8 / MXFP8, the scales; a byte copy). After the
  * deduplicated dispatch this gives exactly the rows moe_dispatch writes with
- * dst_row. Rows whose src_pair is -1 are left untouched.
+ * dst_row. Expert rows that no slot reaches are left untouched. The rows are
+ * visited in their own order, each read once, as the receiving rank would
+ * walk what it received.
  *   dtype         MOE_DTYPE_* of the rows
  *   rank_rows     [num_rank_rows, hidden] bf16 or e4m3 codes
  *   rank_scales   FP8: fp32 [num_rank_rows, hidden/128]; MXFP8: uint8
  *                 [num_rank_rows, hidden/32]; bf16: NULL
- *   rank_row      [T, k] from moe_rank_layout
- *   src_pair      [num_rows] from moe_layout (row -> t*k + j, -1 = none)
+ *   rank_row      [T, k] and row_token [num_rank_rows], both from the same
+ *                 moe_rank_layout call
+ *   dst_row       [T, k] from moe_layout (-1 = dropped)
  *   out, out_scales  [num_rows, ...] in the same formats
  */
 int moe_expand(int num_tokens, int hidden, int top_k, int dtype, int num_rank_rows,
                const void* rank_rows, const void* rank_scales, const int32_t* rank_row,
-               int num_rows, const int32_t* src_pair, void* out, void* out_scales,
-               void* stream);
+               const int32_t* row_token, int num_rows, const int32_t* dst_row, void* out,
+               void* out_scales, void* stream);
 
 /*
  * moe_combine_local -- first level of the hierarchical combine: for each

@@ -170,7 +170,7 @@ int main() {
                            rws_bytes, st));
   MOE_CALL(moe_dispatch(T, H, k, nrr, d_x, d_srow, MOE_DTYPE_BF16, d_sent, nullptr, st));
   HIP_OK(hipMemsetAsync(d_rows, 0xFF, (size_t)rows * H * 2, st));
-  MOE_CALL(moe_expand(T, H, k, MOE_DTYPE_BF16, nrr, d_sent, nullptr, d_rrow, rows, d_src, d_rows,
+  MOE_CALL(moe_expand(T, H, k, MOE_DTYPE_BF16, nrr, d_sent, nullptr, d_rrow, d_rtok, rows, d_dst, d_rows,
                       nullptr, st));
   MOE_CALL(moe_combine_local(T, H, k, rows, d_rows, d_dst, d_rrow, d_rtok, d_w, nrr, d_part, st));
   MOE_CALL(moe_combine_partials(T, H, k, nrr, d_part, d_srow, d_out, st));

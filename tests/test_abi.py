@@ -294,11 +294,11 @@ def test_rank_layout_workspace_bytes():
 
 def _expand(**kw):
     _no_gpu()
-    a = dict(T=4, H=256, k=2, dt=0, nrr=8, src=A16, ssc=None, rr=A16, rows=8, sp=A16,
+    a = dict(T=4, H=256, k=2, dt=0, nrr=8, src=A16, ssc=None, rr=A16, rt=A16, rows=8, dst=A16,
              out=A16b, osc=None)
     a.update(kw)
     return M.lib().moe_expand(a["T"], a["H"], a["k"], a["dt"], a["nrr"], a["src"], a["ssc"],
-                              a["rr"], a["rows"], a["sp"], a["out"], a["osc"], None)
+                              a["rr"], a["rt"], a["rows"], a["dst"], a["out"], a["osc"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -310,7 +310,10 @@ def _expand(**kw):
     (dict(dt=2, ssc=A16, osc=None), M.MOE_ERR_INVALID),
     (dict(dt=0, ssc=A16), M.MOE_ERR_INVALID),
     (dict(dt=1, ssc=A16 + 2, osc=A16b), M.MOE_ERR_INVALID),
-    (dict(sp=None), M.MOE_ERR_INVALID),
+    (dict(dst=None), M.MOE_ERR_INVALID),
+    (dict(rr=None), M.MOE_ERR_INVALID),
+    (dict(rt=None), M.MOE_ERR_INVALID),
+    (dict(rt=A16 + 2), M.MOE_ERR_INVALID),
     (dict(src=None), M.MOE_ERR_INVALID),
     (dict(out=A16b + 8), M.MOE_ERR_INVALID),
 ])
