@@ -125,12 +125,13 @@ def test_committed_kernel_traffic_records_describe_the_dsv3_passes():
 
 
 def test_committed_combine_records_of_other_workloads():
-    """The mixtral and qwen3_skew combine records carry the bench's own
-    algorithmic combine bytes of their workload, so the forward bench line
-    of each finds its record, and their traffic is within a few percent."""
+    """The mixtral, qwen3_skew and decode combine records carry the bench's
+    own algorithmic combine bytes of their workload, so the forward bench
+    line of each finds its record, and their traffic is within a few
+    percent."""
     with open(bench.KERNEL_TRAFFIC_FILE) as f:
         recs = {d["workload_key"]: d for d in json.load(f) if d["kernel"] == "combine"}
-    assert set(recs) == {"mixtral", "qwen3_skew"}
+    assert set(recs) == {"mixtral", "qwen3_skew", "decode"}
     for name, d in recs.items():
         if d["kernel_source_sha256"] != bench.sha_of(bench.COMBINE_SOURCES):
             pytest.skip("the combine code changed since its HBM counters were taken")
